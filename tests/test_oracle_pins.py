@@ -1,0 +1,535 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a library routine (numpy / torch CPU),
+brute force on tiny inputs, exact rational arithmetic, a closed form, an
+invariant, or a hand-worked fixture under tests/golden/.  None of these calls
+the GPU library.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads
+from tests.helpers import (bf16_bits_to_f32, exact_round_bf16, floats, ints, read_golden,
+                           rel_err)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def _torch_bf16_bits(vals: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(vals, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_encoder_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(1)
+    # random magnitudes across the whole exponent range, plus exact ties
+    vals = (rng.standard_normal(20000) * np.exp2(rng.integers(-120, 120, 20000))).astype(np.float32)
+    base = rng.integers(0, 1 << 16, 5000).astype(np.uint32)
+    ties = ((base << 16) | 0x8000).view(np.float32)           # exactly halfway
+    near = ((base << 16) | 0x7FFF).view(np.float32)
+    vals = np.concatenate([vals, ties, near, np.float32([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38])])
+    vals = vals[np.isfinite(vals)]
+    want = _torch_bf16_bits(vals)
+    got = np.array([oracle.bf16_from_double(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_encoder_on_values_between_fp32_points():
+    # double inputs that fp32 cannot hold: a hair above / below a bf16 midpoint
+    rng = np.random.default_rng(2)
+    for _ in range(300):
+        hi = int(rng.integers(0x0080, 0x7F00))              # a normal bf16 pattern
+        lo_val = float(bf16_bits_to_f32(np.uint16(hi)))
+        nxt = float(bf16_bits_to_f32(np.uint16(hi + 1)))
+        mid = Fraction(lo_val) + (Fraction(nxt) - Fraction(lo_val)) / 2
+        for delta in (Fraction(1, 1 << 40), -Fraction(1, 1 << 40), Fraction(0)):
+            q = mid + delta * Fraction(lo_val)
+            v = float(q)
+            assert oracle.bf16_from_double(v) == exact_round_bf16(Fraction(v))
+
+
+def test_bf16_encoder_special_values():
+    assert oracle.bf16_from_double(float("inf")) == 0x7F80
+    assert oracle.bf16_from_double(-float("inf")) == 0xFF80
+    assert oracle.bf16_from_double(1e39) == 0x7F80            # past the largest finite
+    assert (oracle.bf16_from_double(float("nan")) & 0x7F80) == 0x7F80
+    assert oracle.bf16_from_double(-0.0) == 0x8000
+
+
+def test_e4m3_encoder_matches_torch():
+    rng = np.random.default_rng(3)
+    # every E4M3 value, every midpoint between neighbours, a hair around them, random values
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    pos = np.unique(np.abs(vals))
+    mids = (pos[:-1].astype(np.float64) + pos[1:]) / 2
+    eps = np.concatenate([mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20)])
+    rnd = rng.uniform(-448, 448, 20000)
+    small = rng.uniform(-0.03, 0.03, 5000)
+    allv = np.concatenate([vals, mids, -mids, eps, -eps, rnd, small]).astype(np.float32)
+    allv = np.clip(allv, -448, 448)
+    want = torch.from_numpy(allv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_from_float(float(v)) for v in allv], np.uint8)
+    # torch keeps the sign of zero results; so does the oracle
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_decoder_roundtrip():
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            assert np.isnan(oracle.e4m3_to_double(c))
+            continue
+        v = oracle.e4m3_to_double(c)
+        tv = torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).item()
+        assert v == tv
+        assert oracle.e4m3_from_float(v) == c
+
+
+# ---------------------------------------------------------------------------
+# layout: counts, offsets, stable positions, HT and LL destinations
+# ---------------------------------------------------------------------------
+
+def test_layout_golden():
+    g = read_golden("layout_small.txt")[""]
+    idx = ints(g["idx"]).reshape(int(g["T"][0]), int(g["k"][0])).astype(np.int32)
+    E = int(g["E"][0])
+    L = oracle.layout(idx, E, "ht")
+    assert L.counts.tolist() == ints(g["counts"]).tolist()
+    assert L.offsets.tolist() == ints(g["offsets"]).tolist()
+    assert L.pos.ravel().tolist() == ints(g["pos"]).tolist()
+    assert L.dst.ravel().tolist() == ints(g["dst_ht"]).tolist()
+    assert L.flags == 0
+    LL = oracle.layout(idx, E, "ll", cap=int(g["cap"][0]))
+    assert LL.dst.ravel().tolist() == ints(g["dst_ll"]).tolist()
+    assert LL.flags == int(g["flags_ll"][0])
+
+
+def _brute_positions(idx_flat: np.ndarray, E: int) -> np.ndarray:
+    """HT row of every valid entry by sorting (expert, flat index) pairs."""
+    valid = [f for f in range(idx_flat.size) if 0 <= idx_flat[f] < E]
+    order = sorted(valid, key=lambda f: (int(idx_flat[f]), f))
+    dst = np.full(idx_flat.size, -1, np.int64)
+    for row, f in enumerate(order):
+        dst[f] = row
+    return dst
+
+
+@pytest.mark.parametrize("seed,T,E,k", [(0, 64, 8, 2), (1, 37, 5, 3), (2, 1, 4, 4), (3, 100, 64, 8)])
+def test_layout_brute_force(seed, T, E, k):
+    idx, _, _ = workloads.random_case(seed, T, 8, E, k, mask_frac=0.1, dup_frac=0.2)
+    L = oracle.layout(idx, E, "ht")
+    assert L.dst.ravel().tolist() == _brute_positions(idx.ravel(), E).tolist()
+
+
+@pytest.mark.parametrize("name", ["prefill", "training"])
+def test_layout_matches_numpy_at_workload_size(name):
+    inp = workloads.make_inputs(name)
+    E = inp.cfg.E
+    idx = inp.topk_idx
+    L = oracle.layout(idx, E, "ht")
+    flat = idx.ravel()
+    assert np.array_equal(L.counts, np.bincount(flat, minlength=E))
+    assert np.array_equal(L.offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert L.offsets[-1] == flat.size
+    # inverse of a stable argsort by expert id
+    order = np.argsort(flat, kind="stable")
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    assert np.array_equal(L.dst.ravel(), inv)
+
+
+def test_layout_masked_and_out_of_range():
+    idx, _, _ = workloads.random_case(7, 200, 8, 16, 4, mask_frac=0.1, bad_frac=0.05)
+    L = oracle.layout(idx, 16, "ht")
+    flat = idx.ravel()
+    valid = (flat >= 0) & (flat < 16)
+    assert L.flags == oracle.FLAG_INDEX_RANGE
+    assert np.all(L.dst.ravel()[~valid] == -1)
+    assert np.array_equal(L.counts, np.bincount(flat[valid], minlength=16))
+    # only -1 masking: no flag
+    idx2 = np.where(valid.reshape(idx.shape), idx, -1).astype(np.int32)
+    assert oracle.layout(idx2, 16, "ht").flags == 0
+
+
+@pytest.mark.parametrize("cap", [1, 3, 64])
+def test_layout_ll_capacity(cap):
+    idx, _, _ = workloads.random_case(11, 64, 8, 8, 2, skew=1.5)
+    E = 8
+    L = oracle.layout(idx, E, "ll", cap=cap)
+    ht = _brute_positions(idx.ravel(), E)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    pos = ht - off[idx.ravel()]
+    want = np.where(pos < cap, idx.ravel() * cap + pos, -1)
+    assert L.dst.ravel().tolist() == want.tolist()
+    assert L.flags == (oracle.FLAG_CAPACITY if counts.max() > cap else 0)
+
+
+# ---------------------------------------------------------------------------
+# planner
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["A", "B", "C"])
+def test_planner_golden(case):
+    g = read_golden("planner_small.txt")[case]
+    E, R, S, T, k = (int(g[x][0]) for x in ("E", "R", "S", "T", "k"))
+    idx = ints(g["idx"]).reshape(T, k).astype(np.int32)
+    L = oracle.layout(idx, E, "static", R=R, S=S)
+    p = L.plan
+    assert L.counts.tolist() == ints(g["counts"]).tolist()
+    assert p.C == int(g["C"][0])
+    assert p.keep.tolist() == ints(g["keep"]).tolist()
+    assert p.native_row.tolist() == ints(g["native_row"]).tolist()
+    assert p.segments.ravel().tolist() == ints(g["segments"]).tolist()
+    assert p.load.tolist() == ints(g["load"]).tolist()
+    assert p.replica.ravel().tolist() == ints(g["replica"]).tolist()
+    assert L.flags == int(g["flags"][0])
+    assert L.dst.ravel().tolist() == ints(g["dst"]).tolist()
+
+
+def check_plan_invariants(counts: np.ndarray, R: int, S: int, C: int, p: "oracle.Plan"):
+    E = counts.size
+    m = E // R
+    N = int(counts.sum())
+    tgt = np.array([N // R + (1 if r < N % R else 0) for r in range(R)])
+    home = counts.reshape(R, m).sum(axis=1)
+    # static shape: every rank gets exactly its target
+    assert np.array_equal(p.load, tgt)
+    assert p.load.sum() == N and p.load.max(initial=0) <= C
+    seg = p.segments
+    # rows of every expert conserved; shed positions are the tail, covered once, in order
+    for e in range(E):
+        mine = seg[seg[:, 0] == e] if seg.size else np.zeros((0, 5), np.int64)
+        assert p.seg_count[e] == len(mine)
+        cur = p.keep[e]
+        for s in mine:
+            assert s[2] == cur and s[3] > 0
+            cur += s[3]
+        assert cur == counts[e]
+    # native rows kept per rank = min(home, target); only donors shed, only receivers receive
+    keep_rank = p.keep.reshape(R, m).sum(axis=1)
+    assert np.array_equal(keep_rank, np.minimum(home, tgt))
+    for s in seg:
+        e, r = s[0], s[1]
+        assert home[e // m] > tgt[e // m]          # donor's expert
+        assert home[r] < tgt[r]                    # onto a receiver
+    # rows of a rank: own kept rows, then received segments packed behind them
+    for r in range(R):
+        mine = seg[seg[:, 1] == r] if seg.size else np.zeros((0, 5), np.int64)
+        cur = home[r] if home[r] < tgt[r] else keep_rank[r]
+        for s in mine:
+            assert s[4] == cur
+            cur += s[3]
+        assert cur == tgt[r]
+        # slots: distinct experts received, numbered in order
+        exps = list(mine[:, 0]) if len(mine) else []
+        assert len(set(exps)) == len(exps)
+        if len(exps) > S:
+            assert p.flags & oracle.FLAG_SLOT_BUDGET
+        row = p.replica[r]
+        assert list(row[: min(S, len(exps))]) == exps[:S]
+        assert np.all(row[min(S, len(exps)):] == -1)
+    if all(len(seg[seg[:, 1] == r]) <= S for r in range(R)) if seg.size else True:
+        assert not (p.flags & oracle.FLAG_SLOT_BUDGET)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(1, 8), st.integers(1, 6), st.integers(0, 4), st.data())
+def test_planner_invariants_random(R, m, S, data):
+    E = R * m
+    counts = np.array(data.draw(st.lists(st.integers(0, 40), min_size=E, max_size=E)), np.int32)
+    N = int(counts.sum())
+    C = -(-N // R) + data.draw(st.integers(0, 3))
+    p = oracle.plan(counts, R, S, C)
+    check_plan_invariants(counts, R, S, C, p)
+
+
+def test_planner_uniform_reduces_to_ht():
+    # every rank's own load equals its target: no replicas, rows = HT layout
+    R, m = 4, 2
+    idx = np.array([[e, (e + 1) % 8] for e in range(8)] * 2, np.int32)  # counts all 4
+    L = oracle.layout(idx, 8, "static", R=R, S=2)
+    assert L.plan.segments.shape[0] == 0
+    assert np.all(L.plan.replica == -1)
+    H = oracle.layout(idx, 8, "ht")
+    assert np.array_equal(L.dst, H.dst)
+
+
+@pytest.mark.parametrize("rho", workloads.SWEEP_RHOS)
+def test_planner_sweep_workload(rho):
+    inp = workloads.make_inputs("sweep", rho=rho)
+    c = inp.cfg
+    L = oracle.layout(inp.topk_idx, c.E, "static", R=c.R, S=c.S)
+    check_plan_invariants(L.counts, c.R, c.S, L.plan.C, L.plan)
+    assert L.flags == 0
+    # dst is a bijection onto the used rows [r*C, r*C + load_r)
+    used = np.sort(L.dst.ravel())
+    want = np.sort(np.concatenate([r * L.plan.C + np.arange(L.plan.load[r]) for r in range(c.R)]))
+    assert np.array_equal(used, want)
+
+
+def test_planner_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.plan(np.array([1, 2, 3], np.int32), 2, 1, 4)      # E % R != 0
+    with pytest.raises(ValueError):
+        oracle.plan(np.array([5, 5], np.int32), 2, 1, 4)         # C < ceil(N/R)
+
+
+# ---------------------------------------------------------------------------
+# dispatch and FP8
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["ht", "ll", "static"])
+def test_dispatch_is_a_row_permutation(kind):
+    idx, w, x = workloads.random_case(5, 300, 24, 16, 4, mask_frac=0.05)
+    L = oracle.layout(idx, 16, kind, cap=300, R=4, S=4)
+    recv = oracle.dispatch(x, L.dst, L.rows, fill=0xFFFF)
+    d = L.dst.ravel()
+    f = np.nonzero(d >= 0)[0]
+    assert np.array_equal(recv[d[f]], x[f // 4])
+    untouched = np.setdiff1d(np.arange(L.rows), d[f])
+    assert np.all(recv[untouched] == 0xFFFF)
+    src, ridx, rw = oracle.recv_meta(idx, w, L.dst, L.rows)
+    assert np.array_equal(src[d[f]], f)
+    assert np.all(src[untouched] == -1) and np.all(ridx[untouched] == -1)
+    assert np.array_equal(ridx[d[f]], idx.ravel()[f])
+    assert np.array_equal(rw[d[f]], w.ravel()[f])
+
+
+def test_fp8_golden_block():
+    g = read_golden("fp8_small.txt")[""]
+    vals = np.zeros(128, np.float32)
+    xs = floats(g["x"]).astype(np.float32)
+    vals[: xs.size] = xs
+    bits = workloads.f32_to_bf16_bits(vals)
+    assert np.array_equal(bf16_bits_to_f32(bits), vals)        # exactly representable
+    q, s = oracle.quantize_row_fp8(bits)
+    want = np.zeros(128, np.uint8)
+    want[: xs.size] = ints(g["codes"])
+    assert np.array_equal(q, want)
+    assert s.tolist() == [float(g["scale"][0])]
+
+
+def test_fp8_matches_torch_pipeline():
+    inp = workloads.make_inputs("decode")
+    x = inp.x[:64]
+    H = x.shape[1]
+    xf = torch.from_numpy(bf16_bits_to_f32(x).copy()).view(64, H // 128, 128)
+    amax = xf.abs().amax(dim=2, keepdim=True)
+    s = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
+    qt = torch.clamp(xf / s, -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    for t in range(64):
+        q, sc = oracle.quantize_row_fp8(x[t])
+        assert np.array_equal(q, qt[t].reshape(-1).numpy())
+        assert np.array_equal(sc, s[t].reshape(-1).numpy())
+
+
+def test_fp8_zero_block_and_dequant_error():
+    x = np.zeros(256, np.uint16)
+    q, s = oracle.quantize_row_fp8(x)
+    assert np.all(q == 0) and s.tolist() == [1.0, 1.0]
+    inp = workloads.make_inputs("decode")
+    xs = inp.x[:32]
+    deq = []
+    for t in range(32):
+        q, s = oracle.quantize_row_fp8(xs[t])
+        v = np.array([oracle.e4m3_to_double(c) for c in q]).reshape(-1, 128) * s[:, None]
+        deq.append(v.ravel())
+    err = rel_err(np.array(deq), bf16_bits_to_f32(xs))
+    assert 0.005 < err < 0.05          # 3 mantissa bits: a few percent, never exact
+
+
+def test_dispatch_fp8_rows():
+    idx, _, x = workloads.random_case(9, 50, 256, 8, 2)
+    L = oracle.layout(idx, 8, "ll", cap=50)
+    q, s = oracle.dispatch_fp8(x, L.dst, L.rows)
+    d = L.dst.ravel()
+    for f in range(0, d.size, 7):
+        qq, ss = oracle.quantize_row_fp8(x[f // 2])
+        assert np.array_equal(q[d[f]], qq) and np.array_equal(s[d[f]], ss)
+
+
+# ---------------------------------------------------------------------------
+# combine, combine backward, dispatch backward
+# ---------------------------------------------------------------------------
+
+def test_combine_golden():
+    g = read_golden("combine_small.txt")
+    a = g["A"]
+    rows = workloads.f32_to_bf16_bits(floats(a["rows"]).astype(np.float32)).reshape(6, 2)
+    dst = ints(a["dst"]).reshape(3, 2).astype(np.int32)
+    w = floats(a["w"]).astype(np.float32).reshape(3, 2)
+    y = oracle.combine(rows, dst, w)
+    assert np.array_equal(bf16_bits_to_f32(y).ravel(), floats(a["y"]).astype(np.float32))
+    b = g["B"]
+    ones = workloads.f32_to_bf16_bits(np.ones((3, 1), np.float32))
+    d3 = np.array([[0, 1, 2]], np.int32)
+    for i in (1, 2, 3):
+        wi = floats(b[f"w{i}"]).astype(np.float32).reshape(1, 3)
+        y = oracle.combine(ones, d3, wi)
+        assert int(y[0, 0]) == int(b[f"bits{i}"][0], 0)
+
+
+def test_combine_exact_rationals_tiny():
+    idx, w, x = workloads.random_case(21, 5, 6, 4, 3, mask_frac=0.2)
+    L = oracle.layout(idx, 4, "ht")
+    rng = np.random.default_rng(4)
+    rows = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, 6)).astype(np.float32))
+    y = oracle.combine(rows, L.dst, w)
+    rf = bf16_bits_to_f32(rows)
+    for t in range(5):
+        for h in range(6):
+            q = Fraction(0)
+            for j in range(3):
+                d = L.dst[t, j]
+                if d >= 0:
+                    q += Fraction(float(w[t, j])) * Fraction(float(rf[d, h]))
+            assert int(y[t, h]) == exact_round_bf16(q)
+
+
+@pytest.mark.parametrize("out_fp32", [False, True])
+def test_combine_matches_numpy_matmul(out_fp32):
+    idx, w, x = workloads.random_case(22, 400, 40, 16, 8, mask_frac=0.05)
+    L = oracle.layout(idx, 16, "ht")
+    rng = np.random.default_rng(5)
+    rows = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, 40)).astype(np.float32))
+    y = oracle.combine(rows, L.dst, w, out_fp32=out_fp32)
+    rf = bf16_bits_to_f32(rows).astype(np.float64)
+    gathered = np.where((L.dst >= 0)[:, :, None], rf[np.maximum(L.dst, 0)], 0.0)  # [T,k,H]
+    ref = np.matmul(w.astype(np.float64)[:, None, :], gathered)[:, 0, :]
+    if out_fp32:
+        assert np.max(np.abs(y - ref.astype(np.float32)) / np.maximum(np.abs(ref), 1e-30)) < 2e-7
+    else:
+        yf = bf16_bits_to_f32(y)
+        # one rounding to bf16: within half a bf16 ulp of the exact value
+        assert np.all(np.abs(yf - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+def test_combine_roundtrip_identity_experts_is_exact():
+    # identity experts + weights summing to 1: combine(dispatch(x)) == x bitwise
+    inp = workloads.make_inputs("prefill", T=512)
+    L = oracle.layout(inp.topk_idx, inp.cfg.E, "ht")
+    recv = oracle.dispatch(inp.x, L.dst, L.rows)
+    y = oracle.combine(recv, L.dst, inp.topk_w)
+    assert np.array_equal(y, inp.x)
+
+
+def test_combine_one_hot_weights_copy_rows():
+    idx, w, x = workloads.random_case(23, 64, 32, 8, 4)
+    L = oracle.layout(idx, 8, "ht")
+    rng = np.random.default_rng(6)
+    rows = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, 32)).astype(np.float32))
+    for j in range(4):
+        oh = np.zeros_like(w)
+        oh[:, j] = 1.0
+        y = oracle.combine(rows, L.dst, oh)
+        assert np.array_equal(y, rows[L.dst[:, j]])
+
+
+def test_dispatch_backward_sums_copies():
+    idx, _, _ = workloads.random_case(24, 128, 16, 8, 4)
+    L = oracle.layout(idx, 8, "ht")
+    rng = np.random.default_rng(7)
+    # small integers: sums are exact, so the unit-weight combine is a plain sum
+    gr = workloads.f32_to_bf16_bits(rng.integers(-8, 8, (L.rows, 16)).astype(np.float32))
+    y = oracle.combine(gr, L.dst, None)
+    ref = bf16_bits_to_f32(gr)[L.dst].sum(axis=1)
+    assert np.array_equal(bf16_bits_to_f32(y), ref.astype(np.float32))
+
+
+def test_combine_bwd_grad_rows_exact_rounding():
+    idx, w, _ = workloads.random_case(25, 6, 5, 4, 2)
+    L = oracle.layout(idx, 4, "ht")
+    rng = np.random.default_rng(8)
+    gy = workloads.f32_to_bf16_bits(rng.standard_normal((6, 5)).astype(np.float32))
+    out = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, 5)).astype(np.float32))
+    gout, gw = oracle.combine_bwd(gy, out, L.dst, w)
+    gyf = bf16_bits_to_f32(gy)
+    for t in range(6):
+        for j in range(2):
+            d = L.dst[t, j]
+            for h in range(5):
+                q = Fraction(float(w[t, j])) * Fraction(float(gyf[t, h]))
+                assert int(gout[d, h]) == exact_round_bf16(q)
+
+
+def test_combine_bwd_grad_w_matches_numpy():
+    idx, w, _ = workloads.random_case(26, 300, 64, 16, 8, mask_frac=0.05)
+    L = oracle.layout(idx, 16, "ht")
+    rng = np.random.default_rng(9)
+    gy = workloads.f32_to_bf16_bits(rng.standard_normal((300, 64)).astype(np.float32))
+    out = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, 64)).astype(np.float32))
+    _, gw = oracle.combine_bwd(gy, out, L.dst, w)
+    of = bf16_bits_to_f32(out).astype(np.float64)
+    gath = np.where((L.dst >= 0)[:, :, None], of[np.maximum(L.dst, 0)], 0.0)
+    ref = np.einsum("th,tjh->tj", bf16_bits_to_f32(gy).astype(np.float64), gath)
+    assert np.max(np.abs(gw - ref) / np.maximum(np.abs(ref), 1e-3)) < 1e-6
+    assert np.all(gw[L.dst < 0] == 0)
+
+
+def test_combine_bwd_identity_experts_same_dot_for_every_copy():
+    inp = workloads.make_inputs("training", T=256)
+    c = inp.cfg
+    L = oracle.layout(inp.topk_idx, c.E, "static", R=c.R, S=c.S)
+    recv = oracle.dispatch(inp.x, L.dst, L.rows)
+    gy = workloads.make_grad(c, 0, (256, c.H), 1)
+    _, gw = oracle.combine_bwd(gy, recv, L.dst, inp.topk_w)
+    assert np.all(gw == gw[:, :1])
+    ref = np.einsum("th,th->t", bf16_bits_to_f32(gy).astype(np.float64),
+                    bf16_bits_to_f32(inp.x).astype(np.float64))
+    assert np.max(np.abs(gw[:, 0] - ref) / np.maximum(np.abs(ref), 1.0)) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# duplicated-expert gradient reduce
+# ---------------------------------------------------------------------------
+
+def test_dup_reduce_integer_sums_exact():
+    rng = np.random.default_rng(10)
+    E, P, n = 5, 300, 4
+    owner = rng.integers(-1000, 1000, (E, P)).astype(np.float32)
+    rep_f = rng.integers(-100, 100, (n, P)).astype(np.float32)
+    rep = workloads.f32_to_bf16_bits(rep_f)
+    rep_e = np.array([3, 1, 3, -1], np.int32)
+    got = oracle.dup_reduce(rep, rep_e, owner)
+    want = owner.copy()
+    want[3] += rep_f[0] + rep_f[2]
+    want[1] += rep_f[1]
+    assert np.array_equal(got, want)
+
+
+def test_dup_reduce_zero_replicas_and_cancellation():
+    rng = np.random.default_rng(11)
+    owner = rng.standard_normal((3, 64)).astype(np.float32)
+    zeros = np.zeros((2, 64), np.uint16)
+    assert np.array_equal(oracle.dup_reduce(zeros, np.array([0, 2], np.int32), owner), owner)
+    # replica = -owner rounded to bf16, owner itself bf16-representable -> exact zero
+    ob = workloads.f32_to_bf16_bits(owner)
+    owner_b = bf16_bits_to_f32(ob).reshape(3, 64)
+    neg = (ob ^ 0x8000).astype(np.uint16)
+    got = oracle.dup_reduce(neg[1:2], np.array([1], np.int32), owner_b)
+    assert np.all(got[1] == 0) and np.array_equal(got[[0, 2]], owner_b[[0, 2]])
+
+
+def test_dup_reduce_rounds_once():
+    # owner 1.0, replicas 2^-24 and 2^-24: two fp32 adds would give 1.0 each
+    # time; the one rounding of the double sum 1 + 2^-23 gives the next float
+    owner = np.ones((1, 8), np.float32)
+    r = workloads.f32_to_bf16_bits(np.full((2, 8), 2.0 ** -24, np.float32))
+    got = oracle.dup_reduce(r, np.array([0, 0], np.int32), owner)
+    assert np.all(got == np.float32(1 + 2.0 ** -23))
