@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-parallel dispatch -> combine path on one MI355X.
+
+One step = one pass of the whole path over one batch already resident in
+HBM: ep_plan (layout, and the static plan where the workload uses it) ->
+ep_dispatch -> ep_combine with identity experts; the training workload adds
+ep_combine_bwd -> dispatch backward -> duplicated-expert gradient reduce.
+
+Default workload: prefill, T=4096 tokens, H=7168 bf16, E=256 experts, top-8,
+Zipf(1.1)-skewed routing, HT (2D concatenated) layout.
+
+Prints ONE JSON line: tokens/s of the whole step (value), HBM GB/s of the
+step's algorithmic bytes, the roofline of the dominant kernel timed with HIP
+events on the stream it is launched on, and the CPU oracle's throughput on a
+bounded sample of the same workload (a reported baseline, not a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak), T=4096 H=7168 top-8"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="prefill",
+                   choices=["prefill", "decode", "tiny", "sweep", "training"])
+    p.add_argument("--rho", type=float, default=8.0, help="sweep: max/mean expert load")
+    p.add_argument("--fp8", action="store_true", help="decode: FP8 e4m3 dispatch")
+    p.add_argument("--cold", action="store_true",
+                   help="write a 512 MB buffer before every step (Infinity Cache flushed); "
+                        "steps are then timed one by one")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                   help="only run a plain device copy of MB megabytes K times (counter scaling)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(c, fp8=False):
+    """Bytes each kernel must move by definition: x read once, every routed row
+    written once and read once, outputs written once, int32/fp32 metadata."""
+    N = c.T * c.k
+    row = c.H * 2
+    b = {
+        "plan": N * 4 + N * 4,                                   # topk_idx read, dst written
+        "dispatch": c.T * row + N * (c.H + c.H // 128 * 4 if fp8 else row) + N * 4,
+        "combine": N * row + N * 4 + N * 4 + c.T * row,          # rows, dst, w read; y written
+    }
+    if c.name == "training":
+        b["combine_bwd"] = c.T * row + N * row + N * row + N * 4 * 3 + N * 4   # gy, out rows, grad rows, dst/w, grad_w
+        b["dispatch_bwd"] = N * row + N * 4 + c.T * row
+        P = 4096 * 1536
+        b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
+    return b
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "combine_ep_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"dispatch": ["dispatch.hip", "device.h"], "combine": ["combine.hip", "device.h"],
+                  "combine_bwd": ["combine.hip", "device.h"], "dispatch_bwd": ["combine.hip", "device.h"],
+                  "plan": ["plan.hip"], "dup_reduce": ["dup_reduce.hip", "device.h"]}
+
+
+def traffic_for(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    k = d.get("kernels", {}).get(kernel)
+    if not k or k.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(name, rho, fp8, budget_s):
+    """The oracle, as it stands, on the first tokens of the same workload: the
+    full layout -> dispatch -> combine chain, repeated for about budget_s."""
+    import numpy as np
+    import oracle
+    import workloads
+    oracle.build(force=False)
+    c = workloads.get_config(name, rho)
+    Ts = min(c.T, 512)
+    inp = workloads.make_inputs(name, 0, rho) if name == "sweep" else workloads.make_inputs(name)
+    idx, w, x = inp.topk_idx[:Ts], inp.topk_w[:Ts], inp.x[:Ts]
+
+    def chain():
+        L = oracle.layout(idx, c.E, c.layout, cap=c.cap, R=c.R, S=c.S)
+        if fp8:
+            oracle.dispatch_fp8(x, L.dst, L.rows)
+        recv = oracle.dispatch(x, L.dst, L.rows)
+        oracle.combine(recv, L.dst, w, out_fp32=c.out_fp32)
+
+    chain()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        chain()
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    return {"value": Ts * runs / el, "unit": "tokens/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"first {Ts} of {c.T} tokens of the {name} workload, full "
+                      f"layout{'+plan' if c.layout == 'static' else ''}+dispatch+combine chain, "
+                      f"{runs} runs in {el:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); logical "
+              "expert-parallel ranks are regions of that GPU's HBM.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import combine_ep_plan_amd as ep
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20)
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(a.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": a.steps + a.warmup}))
+        return
+
+    name = a.workload
+    inp = workloads.make_inputs(name, 0, a.rho) if name == "sweep" else workloads.make_inputs(name)
+    c = inp.cfg
+    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S)
+    h = ep.Handle(g, c.T)
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(inp.topk_idx).to(dev)
+    w = torch.from_numpy(inp.topk_w).to(dev)
+    shape = g.recv_shape(c.T)
+    recv = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    rq = rs = None
+    if a.fp8:
+        rq = torch.empty(shape, dtype=torch.float8_e4m3fn, device=dev)
+        rs = torch.empty((h.recv_rows, c.H // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((c.T, c.H), dtype=torch.float32 if c.out_fp32 else torch.bfloat16, device=dev)
+    train = name == "training"
+    if train:
+        gy = torch.from_numpy(workloads.make_grad(c, 0, (c.T, c.H), 1).view(np.int16)).to(dev).view(torch.bfloat16)
+        gout = torch.empty_like(recv)
+        gw = torch.empty_like(w)
+        gx = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+        rep = torch.from_numpy(workloads.make_grad(c, 0, (2, 4096, 1536), 2).view(np.int16)).to(dev).view(torch.bfloat16)
+        owner = torch.zeros((c.E, 4096, 1536), dtype=torch.float32, device=dev)
+        rep_e = torch.zeros(2, dtype=torch.int32, device=dev)   # replicas of expert 0, same owner
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if a.cold else None
+
+    ops = []
+    ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, stream)))
+    if a.fp8:
+        # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
+        ep.ep_plan(h.ptr, idx, stream)
+        ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)
+        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, stream)))
+    else:
+        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)))
+    ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, stream)))
+    if train:
+        ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, stream)))
+        ops.append(("dispatch_bwd", lambda: ep.ep_combine(h.ptr, gout, None, gx, stream)))
+        ops.append(("dup_reduce", lambda: ep.ep_dup_grad_reduce(h.ptr, rep, rep_e, owner, stream)))
+
+    def step():
+        for _, f in ops:
+            f()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert h.status() == 0, "device flags raised on the benchmark input"
+
+    # timed region 1: the whole step, back to back (or one by one when --cold)
+    K = a.steps
+    if not a.cold:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t_host
+        step_ms = e0.elapsed_time(e1) / K
+    else:
+        tot = 0.0
+        t_host = time.perf_counter()
+        for _ in range(K):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        t_host = time.perf_counter() - t_host
+        step_ms = tot / K
+
+    # timed region 2: the same steps with an event pair around every launch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in ops] for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        if a.cold:
+            flush.fill_(1)
+        for (nm, f), (b, e) in zip(ops, evs[s]):
+            b.record(stream)
+            f()
+            e.record(stream)
+    torch.cuda.synchronize()
+    per_us = {nm: 1000.0 * sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(K)) / K
+              for i, (nm, _) in enumerate(ops)}
+
+    ab = algorithmic_bytes(c, a.fp8)
+    chain_bytes = sum(ab[nm] for nm, _ in ops)
+    step_s = step_ms / 1000.0
+    dom = max((nm for nm in ("dispatch", "combine", "combine_bwd") if nm in per_us),
+              key=lambda nm: per_us[nm])
+    dom_gbps = ab[dom] / (per_us[dom] * 1e-6) / 1e9
+    traffic = traffic_for(f"{name}{'_fp8' if a.fp8 else ''}", dom)
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic, "bytes_per_launch": ab[dom], "avg_us": round(per_us[dom], 2)}
+
+    wl = {"prefill": f"prefill HT T={c.T} H={c.H} E={c.E} top-{c.k} zipf(1.1) bf16",
+          "decode": f"decode LL T={c.T} H={c.H} E={c.E} top-{c.k} cap={c.cap}{' fp8' if a.fp8 else ' bf16'}",
+          "tiny": f"tiny LL T={c.T} H={c.H} E={c.E} top-{c.k} cap={c.cap} fp32 combine",
+          "sweep": f"imbalance sweep STATIC T={c.T} H={c.H} E={c.E} top-{c.k} R={c.R} S={c.S} rho={c.rho:g}",
+          "training": f"training fwd+bwd STATIC T={c.T} H={c.H} E={c.E} top-{c.k} R={c.R} S={c.S}"}[name]
+    out = {
+        "metric": METRIC,
+        "value": round(c.T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
+                   "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
+                   "step": " -> ".join(nm for nm, _ in ops)},
+        "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
+        "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": chain_bytes,
+        "kernels_us": {k: round(v, 2) for k, v in per_us.items()},
+        "kernels_gbps": {k: round(ab[k] / (per_us[k] * 1e-6) / 1e9, 1) for k in per_us if k in ab},
+        "host_wall_s": round(t_host, 3),
+        "roofline": roof,
+    }
+    if name == "sweep":
+        out["config"]["rho"] = c.rho
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(name, a.rho, a.fp8, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

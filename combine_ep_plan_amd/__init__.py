@@ -1,0 +1,413 @@
+"""MoE expert-parallel token dispatch / combine / static-shape planner for
+MI355X (gfx950).
+
+A thin binding over ``libep_mi355x.so`` (C ABI in ``include/ep.h``).  It only
+marshals arguments: torch tensors provide device memory and the stream, and
+every step of the path runs in the library's HIP kernels.  There is no CPU
+or PyTorch fallback: if the library is missing the calls raise.
+
+The functions ``ep_group_create`` ... ``ep_dup_grad_reduce`` mirror the C
+entry points one to one.  ``Group`` / ``Handle`` / ``Buffer`` wrap them in
+the group -> handle -> dispatch -> expert -> combine flow of the NCCL EP
+paper (listing, Table II and Figure 2), and ``Buffer.dispatch`` returns
+``recv_x, recv_i, recv_w, handle, event`` like that paper's Table V.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+import torch
+
+__all__ = [
+    "EpError", "LAYOUT_LL", "LAYOUT_HT", "LAYOUT_STATIC", "FLAG_INDEX_RANGE", "FLAG_CAPACITY",
+    "FLAG_SLOT_BUDGET", "Group", "Handle", "Buffer", "library_path", "load_library",
+    "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
+    "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
+    "ep_handle_status", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
+    "ep_dup_grad_reduce",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libep_mi355x.so"
+
+LAYOUT_LL, LAYOUT_HT, LAYOUT_STATIC = 0, 1, 2
+_LAYOUTS = {"ll": LAYOUT_LL, "ht": LAYOUT_HT, "static": LAYOUT_STATIC}
+FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET = 1, 2, 4
+TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0, 1, 2, 3, 4
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
+_STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
+           "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",
+           "EP_ERR_UNSUPPORTED", "EP_ERR_HIP"]
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        name = _STATUS[code] if 0 <= code < len(_STATUS) else str(code)
+        super().__init__(f"{what} failed: {name}")
+
+
+class ep_tensor_t(ctypes.Structure):
+    _fields_ = [("data", c_void_p), ("dtype", c_int32), ("tag", c_int32), ("ndim", c_int32),
+                ("reserved", c_int32), ("sizes", c_int64 * 4)]
+
+
+class ep_group_config_t(ctypes.Structure):
+    _fields_ = [("num_experts", c_int32), ("num_ranks", c_int32), ("hidden", c_int32),
+                ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
+                ("capacity", c_int32), ("slots_per_rank", c_int32)]
+
+
+class ep_handle_view_t(ctypes.Structure):
+    _fields_ = [("num_tokens", c_int32), ("top_k", c_int32), ("num_experts", c_int32),
+                ("num_ranks", c_int32), ("recv_rows", c_int64), ("rank_rows", c_int32),
+                ("max_segments", c_int32)] + [
+        (n, c_void_p) for n in ("counts", "offsets", "dst", "recv_src", "status", "keep",
+                                "native_row", "seg_first", "seg_count", "segments",
+                                "n_segments", "load", "replica")]
+
+
+_lib = None
+_T = POINTER(ep_tensor_t)
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libep_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m combine_ep_plan_amd.build`"
+                           " (there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    S = c_int32
+    sig = {
+        "ep_status_string": (ctypes.c_char_p, [S]),
+        "ep_group_create": (S, [POINTER(ep_group_config_t), POINTER(c_void_p)]),
+        "ep_group_destroy": (S, [c_void_p]),
+        "ep_group_recv_rows": (S, [c_void_p, c_int32, POINTER(c_int64)]),
+        "ep_handle_workspace_bytes": (S, [c_void_p, c_int32, POINTER(c_size_t)]),
+        "ep_handle_create": (S, [c_void_p, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
+        "ep_handle_destroy": (S, [c_void_p]),
+        "ep_handle_query": (S, [c_void_p, POINTER(ep_handle_view_t)]),
+        "ep_handle_status": (S, [c_void_p, c_void_p, POINTER(c_uint32)]),
+        "ep_plan": (S, [c_void_p, _T, c_void_p]),
+        "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
+        "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise EpError(code, what)
+
+
+def _tensor(t: torch.Tensor | None, tag: int):
+    """ep_tensor_t view of a contiguous device tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() < 1 or t.dim() > 4:
+        raise ValueError("tensors must have 1..4 dimensions")
+    v = ep_tensor_t()
+    v.data = t.data_ptr() if t.numel() > 0 else None
+    v.dtype = _DTYPES[t.dtype]
+    v.tag = tag
+    v.ndim = t.dim()
+    v.reserved = 0
+    for i, s in enumerate(t.shape):
+        v.sizes[i] = int(s)
+    return ctypes.pointer(v)
+
+
+def _stream(stream) -> c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return c_void_p(stream.cuda_stream)
+    return c_void_p(int(stream))
+
+
+# ---------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points
+# ---------------------------------------------------------------------------
+
+def ep_status_string(code: int) -> str:
+    return load_library().ep_status_string(int(code)).decode()
+
+
+def ep_group_create(cfg: ep_group_config_t) -> int:
+    out = c_void_p()
+    _check(load_library().ep_group_create(ctypes.byref(cfg), ctypes.byref(out)), "ep_group_create")
+    return out.value
+
+
+def ep_group_destroy(g: int) -> None:
+    _check(load_library().ep_group_destroy(c_void_p(g)), "ep_group_destroy")
+
+
+def ep_group_recv_rows(g: int, num_tokens: int) -> int:
+    out = c_int64()
+    _check(load_library().ep_group_recv_rows(c_void_p(g), num_tokens, ctypes.byref(out)),
+           "ep_group_recv_rows")
+    return out.value
+
+
+def ep_handle_workspace_bytes(g: int, num_tokens: int) -> int:
+    out = c_size_t()
+    _check(load_library().ep_handle_workspace_bytes(c_void_p(g), num_tokens, ctypes.byref(out)),
+           "ep_handle_workspace_bytes")
+    return out.value
+
+
+def ep_handle_create(g: int, num_tokens: int, workspace_ptr: int, workspace_bytes: int) -> int:
+    out = c_void_p()
+    _check(load_library().ep_handle_create(c_void_p(g), num_tokens, c_void_p(workspace_ptr),
+                                           workspace_bytes, ctypes.byref(out)), "ep_handle_create")
+    return out.value
+
+
+def ep_handle_destroy(h: int) -> None:
+    _check(load_library().ep_handle_destroy(c_void_p(h)), "ep_handle_destroy")
+
+
+def ep_handle_query(h: int) -> ep_handle_view_t:
+    v = ep_handle_view_t()
+    _check(load_library().ep_handle_query(c_void_p(h), ctypes.byref(v)), "ep_handle_query")
+    return v
+
+
+def ep_handle_status(h: int, stream=None) -> int:
+    out = c_uint32()
+    _check(load_library().ep_handle_status(c_void_p(h), _stream(stream), ctypes.byref(out)),
+           "ep_handle_status")
+    return out.value
+
+
+def ep_plan(h: int, topk_idx: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_plan(c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _stream(stream)),
+           "ep_plan")
+
+
+def ep_dispatch(h: int, tokens: torch.Tensor, topk_weights: torch.Tensor | None,
+                recv_tokens: torch.Tensor, recv_scales: torch.Tensor | None = None,
+                recv_topk_idx: torch.Tensor | None = None,
+                recv_topk_weights: torch.Tensor | None = None, stream=None) -> None:
+    _check(load_library().ep_dispatch(
+        c_void_p(h), _tensor(tokens, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+        _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
+        _tensor(recv_topk_idx, TAG_TOPK_IDX), _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS),
+        _stream(stream)), "ep_dispatch")
+
+
+def ep_combine(h: int, expert_out: torch.Tensor, topk_weights: torch.Tensor | None,
+               out_tokens: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_combine(
+        c_void_p(h), _tensor(expert_out, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+        _tensor(out_tokens, TAG_TOKENS), _stream(stream)), "ep_combine")
+
+
+def ep_combine_bwd(h: int, grad_tokens: torch.Tensor, expert_out: torch.Tensor,
+                   topk_weights: torch.Tensor, grad_expert_out: torch.Tensor,
+                   grad_topk_weights: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_combine_bwd(
+        c_void_p(h), _tensor(grad_tokens, TAG_TOKENS), _tensor(expert_out, TAG_TOKENS),
+        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(grad_expert_out, TAG_TOKENS),
+        _tensor(grad_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)), "ep_combine_bwd")
+
+
+def ep_dup_grad_reduce(h: int, replica_grads: torch.Tensor, replica_expert: torch.Tensor | None,
+                       owner_grads: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_dup_grad_reduce(
+        c_void_p(h), _tensor(replica_grads, TAG_EXPERT_GRADS), _tensor(replica_expert, TAG_TOPK_IDX),
+        _tensor(owner_grads, TAG_EXPERT_GRADS), _stream(stream)), "ep_dup_grad_reduce")
+
+
+# ---------------------------------------------------------------------------
+# group / handle / buffer objects
+# ---------------------------------------------------------------------------
+
+class Group:
+    """Long-lived configuration (experts, ranks, hidden size, top-k, layout)."""
+
+    def __init__(self, num_experts: int, num_ranks: int, hidden: int, top_k: int,
+                 max_tokens: int, layout: str | int = "ht", capacity: int = 0,
+                 slots_per_rank: int = 0):
+        self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+        self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
+                                     self.layout, capacity, slots_per_rank)
+        self.ptr = ep_group_create(self.cfg)
+
+    @property
+    def num_experts(self):
+        return self.cfg.num_experts
+
+    @property
+    def hidden(self):
+        return self.cfg.hidden
+
+    @property
+    def top_k(self):
+        return self.cfg.top_k
+
+    def recv_rows(self, num_tokens: int) -> int:
+        return ep_group_recv_rows(self.ptr, num_tokens)
+
+    def recv_shape(self, num_tokens: int) -> tuple[int, ...]:
+        c = self.cfg
+        rows = self.recv_rows(num_tokens)
+        if self.layout == LAYOUT_LL:
+            return (c.num_experts, c.capacity, c.hidden)
+        if self.layout == LAYOUT_STATIC:
+            return (c.num_ranks, rows // c.num_ranks, c.hidden)
+        return (rows, c.hidden)
+
+    def workspace_bytes(self, num_tokens: int) -> int:
+        return ep_handle_workspace_bytes(self.ptr, num_tokens)
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and _lib is not None:
+            _lib.ep_group_destroy(c_void_p(self.ptr))
+            self.ptr = None
+
+
+class Handle:
+    """Per-pass routing state over a device workspace owned by this object."""
+
+    def __init__(self, group: Group, num_tokens: int, device: torch.device | str | None = None):
+        self.group = group
+        self.num_tokens = num_tokens
+        nbytes = group.workspace_bytes(num_tokens)
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.ptr = ep_handle_create(group.ptr, num_tokens, self.workspace.data_ptr(), nbytes)
+        self._view = ep_handle_query(self.ptr)
+
+    def plan(self, topk_idx: torch.Tensor, stream=None) -> "Handle":
+        ep_plan(self.ptr, topk_idx, stream)
+        return self
+
+    def status(self, stream=None) -> int:
+        return ep_handle_status(self.ptr, stream)
+
+    @property
+    def recv_rows(self) -> int:
+        return self._view.recv_rows
+
+    @property
+    def rank_rows(self) -> int:
+        return self._view.rank_rows
+
+    def _ws(self, ptr: int | None, count: int) -> torch.Tensor | None:
+        if not ptr:
+            return None
+        off = ptr - self.workspace.data_ptr()
+        return self.workspace[off: off + 4 * count].view(torch.int32)
+
+    def tables(self) -> dict[str, torch.Tensor]:
+        """Views (no copies) of the layout and plan tables in the workspace."""
+        v = self._view
+        E, R, T, k = v.num_experts, v.num_ranks, v.num_tokens, v.top_k
+        out = {
+            "counts": self._ws(v.counts, E),
+            "offsets": self._ws(v.offsets, E + 1),
+            "dst": self._ws(v.dst, T * k).view(T, k) if T * k else self._ws(v.dst, 0),
+            "recv_src": self._ws(v.recv_src, v.recv_rows),
+            "status": self._ws(v.status, 1),
+        }
+        if v.keep:
+            S = self.group.cfg.slots_per_rank
+            out.update({
+                "keep": self._ws(v.keep, E), "native_row": self._ws(v.native_row, E),
+                "seg_first": self._ws(v.seg_first, E), "seg_count": self._ws(v.seg_count, E),
+                "segments": self._ws(v.segments, 5 * v.max_segments).view(v.max_segments, 5),
+                "n_segments": self._ws(v.n_segments, 1), "load": self._ws(v.load, R),
+                "replica": self._ws(v.replica, R * S).view(R, S),
+            })
+        return out
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and _lib is not None:
+            _lib.ep_handle_destroy(c_void_p(self.ptr))
+            self.ptr = None
+
+
+class Buffer:
+    """Framework-facing operations (NCCL EP paper listing, Table V)."""
+
+    def __init__(self, group: Group):
+        self.group = group
+
+    def handle(self, num_tokens: int, device=None) -> Handle:
+        return Handle(self.group, num_tokens, device)
+
+    def dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
+                 handle: Handle | None = None, fp8: bool = False, recv_meta: bool = True,
+                 out: torch.Tensor | None = None, stream=None):
+        """Plan (if ``handle`` is None or not yet planned with these indices) and
+        dispatch.  Returns ``recv_x, recv_i, recv_w, handle, event`` (plus the
+        FP8 scales as ``recv_x = (codes, scales)`` when ``fp8``)."""
+        T = x.shape[0]
+        if handle is None:
+            handle = Handle(self.group, T, x.device)
+            handle.plan(topk_idx, stream)
+        rows = handle.recv_rows
+        shape = self.group.recv_shape(T)
+        H = self.group.hidden
+        scales = None
+        if fp8:
+            recv = out if out is not None else torch.empty(shape, dtype=torch.float8_e4m3fn, device=x.device)
+            scales = torch.empty((rows, H // 128), dtype=torch.float32, device=x.device)
+        else:
+            recv = out if out is not None else torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+        ri = torch.empty(rows, dtype=torch.int32, device=x.device) if recv_meta else None
+        rw = torch.empty(rows, dtype=torch.float32, device=x.device) if (recv_meta and topk_weights is not None) else None
+        ep_dispatch(handle.ptr, x, topk_weights, recv, scales, ri, rw, stream)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream() if stream is None else stream)
+        recv_x = (recv, scales) if fp8 else recv
+        return recv_x, ri, rw, handle, ev
+
+    def combine(self, expert_out: torch.Tensor, handle: Handle,
+                topk_weights: torch.Tensor | None, out_dtype=torch.bfloat16,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        T, H = handle.num_tokens, self.group.hidden
+        y = out if out is not None else torch.empty((T, H), dtype=out_dtype, device=expert_out.device)
+        ep_combine(handle.ptr, expert_out, topk_weights, y, stream)
+        return y
+
+    def dispatch_bwd(self, grad_recv: torch.Tensor, handle: Handle, stream=None) -> torch.Tensor:
+        """Gradient of dispatch: sum of each token's received-row gradients."""
+        return self.combine(grad_recv, handle, None, stream=stream)
+
+    def combine_bwd(self, grad_y: torch.Tensor, expert_out: torch.Tensor,
+                    topk_weights: torch.Tensor, handle: Handle, stream=None):
+        grad_out = torch.empty_like(expert_out)
+        grad_w = torch.empty_like(topk_weights)
+        ep_combine_bwd(handle.ptr, grad_y, expert_out, topk_weights, grad_out, grad_w, stream)
+        return grad_out, grad_w
+
+    def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,
+                        handle: Handle, replica_expert: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+        ep_dup_grad_reduce(handle.ptr, replica_grads, replica_expert, owner_grads, stream)
+        return owner_grads

@@ -1,0 +1,417 @@
+// ep_api.cpp -- the C ABI declared in include/ep.h: argument validation,
+// group and handle bookkeeping, workspace carving and kernel selection.
+// Every check happens on the host before anything is enqueued; the only
+// HIP calls are the kernel launches and, in ep_handle_status, one copy and
+// one stream synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+struct ep_group {
+  ep_group_config_t cfg;
+  int32_t nbits;
+};
+
+struct ep_handle {
+  ep_group *g;
+  epk::Geometry geo;
+  epk::Workspace ws;
+  char *base;
+  size_t bytes;
+  bool planned;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+epk::Geometry make_geometry(const ep_group *g, int32_t T) {
+  const ep_group_config_t &c = g->cfg;
+  epk::Geometry geo{};
+  geo.T = T;
+  geo.k = c.top_k;
+  geo.E = c.num_experts;
+  geo.R = c.num_ranks;
+  geo.S = c.slots_per_rank;
+  geo.layout = c.layout;
+  geo.cap = c.capacity;
+  geo.n = (int64_t)T * c.top_k;
+  geo.C = (int32_t)((geo.n + c.num_ranks - 1) / c.num_ranks);
+  const int64_t tiles = (geo.n + epk::kTileEntries - 1) / epk::kTileEntries;
+  geo.ntiles = (int32_t)(tiles > 0 ? tiles : 1);
+  geo.nbits = g->nbits;
+  if (c.layout == EP_LAYOUT_HT) geo.rows = geo.n;
+  else if (c.layout == EP_LAYOUT_LL) geo.rows = (int64_t)c.num_experts * c.capacity;
+  else geo.rows = (int64_t)c.num_ranks * geo.C;
+  return geo;
+}
+
+int64_t numel(const ep_tensor_t *t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->sizes[i];
+  return n;
+}
+
+// Generic checks: non-NULL, tag, dtype, ndim in 1..4, sizes >= 0, data set.
+ep_status_t check_tensor(const ep_tensor_t *t, int32_t tag, int32_t dtype) {
+  if (!t) return EP_ERR_INVALID_ARG;
+  if (t->tag != tag) return EP_ERR_BAD_TAG;
+  if (t->dtype != dtype) return EP_ERR_BAD_DTYPE;
+  if (t->ndim < 1 || t->ndim > 4 || t->reserved != 0) return EP_ERR_BAD_SHAPE;
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->sizes[i] < 0) return EP_ERR_BAD_SHAPE;
+  if (!t->data && numel(t) > 0) return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+// Exactly [d0, d1] as a 2D tensor.
+bool is_2d(const ep_tensor_t *t, int64_t d0, int64_t d1) {
+  return t->ndim == 2 && t->sizes[0] == d0 && t->sizes[1] == d1;
+}
+
+// Leading sizes multiply to `rows`, last size `last` (any ndim >= 2), or a
+// 1D tensor of `rows` elements when last == 1 and allow_1d.
+bool is_rows(const ep_tensor_t *t, int64_t rows, int64_t last, bool allow_1d = false) {
+  if (allow_1d && t->ndim == 1) return last == 1 && t->sizes[0] == rows;
+  if (t->ndim < 2) return false;
+  int64_t lead = 1;
+  for (int i = 0; i + 1 < t->ndim; ++i) lead *= t->sizes[i];
+  return lead == rows && t->sizes[t->ndim - 1] == last;
+}
+
+ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+namespace epk {
+
+size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
+  size_t off = 0;
+  Workspace w{};
+  auto take = [&](size_t bytes) -> char * {
+    char *p = base ? base + off : nullptr;
+    off += align_up(bytes > 0 ? bytes : 1);
+    return p;
+  };
+  char *hdr = take(kAlign);
+  w.status = reinterpret_cast<uint32_t *>(hdr);
+  w.ticket = reinterpret_cast<uint32_t *>(hdr ? hdr + 4 : nullptr);
+  w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
+  w.offsets = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (g.E + 1)));
+  w.eidx = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.n));
+  w.lrank = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.n));
+  w.dst = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.n));
+  w.tile_hist = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)g.ntiles * g.E));
+  w.tile_flags = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * g.ntiles));
+  w.recv_src = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.rows));
+  if (g.layout == kStatic) {
+    w.keep = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
+    w.native_row = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
+    w.seg_first = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
+    w.seg_count = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
+    w.segments = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * 5 * (size_t)(g.E + g.R)));
+    w.n_segments = reinterpret_cast<int32_t *>(take(sizeof(int32_t)));
+    w.load = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.R));
+    w.replica = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)g.R * g.S));
+  }
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace epk
+
+extern "C" {
+
+const char *ep_status_string(ep_status_t st) {
+  switch (st) {
+    case EP_OK: return "EP_OK";
+    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+    case EP_ERR_BAD_TAG: return "EP_ERR_BAD_TAG";
+    case EP_ERR_BAD_DTYPE: return "EP_ERR_BAD_DTYPE";
+    case EP_ERR_BAD_SHAPE: return "EP_ERR_BAD_SHAPE";
+    case EP_ERR_NOT_PLANNED: return "EP_ERR_NOT_PLANNED";
+    case EP_ERR_WORKSPACE_TOO_SMALL: return "EP_ERR_WORKSPACE_TOO_SMALL";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+    case EP_ERR_HIP: return "EP_ERR_HIP";
+  }
+  return "EP_ERR_UNKNOWN";
+}
+
+ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
+  if (!cfg || !out) return EP_ERR_INVALID_ARG;
+  const ep_group_config_t &c = *cfg;
+  if (c.num_experts < 1 || c.num_experts > epk::kMaxExperts) return EP_ERR_INVALID_ARG;
+  if (c.num_ranks < 1 || c.num_experts % c.num_ranks != 0) return EP_ERR_INVALID_ARG;
+  if (c.hidden < 8 || c.hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (c.top_k < 1 || c.top_k > epk::kMaxTopK) return EP_ERR_INVALID_ARG;
+  if (c.max_tokens < 0) return EP_ERR_INVALID_ARG;
+  if ((int64_t)c.max_tokens * c.top_k > INT32_MAX) return EP_ERR_INVALID_ARG;
+  if (c.layout != EP_LAYOUT_LL && c.layout != EP_LAYOUT_HT && c.layout != EP_LAYOUT_STATIC)
+    return EP_ERR_INVALID_ARG;
+  if (c.layout == EP_LAYOUT_LL &&
+      (c.capacity < 1 || (int64_t)c.capacity * c.num_experts > INT32_MAX))
+    return EP_ERR_INVALID_ARG;
+  if (c.layout == EP_LAYOUT_STATIC && c.slots_per_rank < 0) return EP_ERR_INVALID_ARG;
+  const int32_t R = c.layout == EP_LAYOUT_STATIC ? c.num_ranks : 0;
+  if (epk::plan_lds_bytes(c.num_experts, R) + 256 > (size_t)epk::kLdsLimit)
+    return EP_ERR_UNSUPPORTED;
+  ep_group *g = new (std::nothrow) ep_group;
+  if (!g) return EP_ERR_INVALID_ARG;
+  g->cfg = c;
+  g->nbits = 1;
+  while ((1 << g->nbits) < c.num_experts) ++g->nbits;
+  *out = g;
+  return EP_OK;
+}
+
+ep_status_t ep_group_destroy(ep_group_t g) {
+  if (!g) return EP_ERR_INVALID_ARG;
+  delete g;
+  return EP_OK;
+}
+
+ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows) {
+  if (!g || !rows || num_tokens < 0 || num_tokens > g->cfg.max_tokens) return EP_ERR_INVALID_ARG;
+  *rows = make_geometry(g, num_tokens).rows;
+  return EP_OK;
+}
+
+ep_status_t ep_handle_workspace_bytes(ep_group_t g, int32_t num_tokens, size_t *bytes) {
+  if (!g || !bytes || num_tokens < 0 || num_tokens > g->cfg.max_tokens) return EP_ERR_INVALID_ARG;
+  *bytes = epk::carve_workspace(make_geometry(g, num_tokens), nullptr, nullptr);
+  return EP_OK;
+}
+
+ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
+                             size_t workspace_bytes, ep_handle_t *out) {
+  if (!g || !out || !workspace) return EP_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_tokens > g->cfg.max_tokens) return EP_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return EP_ERR_INVALID_ARG;
+  const epk::Geometry geo = make_geometry(g, num_tokens);
+  const size_t need = epk::carve_workspace(geo, nullptr, nullptr);
+  if (workspace_bytes < need) return EP_ERR_WORKSPACE_TOO_SMALL;
+  ep_handle *h = new (std::nothrow) ep_handle;
+  if (!h) return EP_ERR_INVALID_ARG;
+  h->g = g;
+  h->geo = geo;
+  h->base = static_cast<char *>(workspace);
+  h->bytes = workspace_bytes;
+  h->planned = false;
+  epk::carve_workspace(geo, h->base, &h->ws);
+  *out = h;
+  return EP_OK;
+}
+
+ep_status_t ep_handle_destroy(ep_handle_t h) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  delete h;
+  return EP_OK;
+}
+
+ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *v) {
+  if (!h || !v) return EP_ERR_INVALID_ARG;
+  std::memset(v, 0, sizeof *v);
+  const epk::Geometry &g = h->geo;
+  v->num_tokens = g.T;
+  v->top_k = g.k;
+  v->num_experts = g.E;
+  v->num_ranks = g.R;
+  v->recv_rows = g.rows;
+  v->rank_rows = g.layout == EP_LAYOUT_STATIC ? g.C
+                 : g.layout == EP_LAYOUT_LL  ? g.cap
+                                             : (int32_t)g.n;
+  v->max_segments = g.layout == EP_LAYOUT_STATIC ? g.E + g.R : 0;
+  v->counts = h->ws.counts;
+  v->offsets = h->ws.offsets;
+  v->dst = h->ws.dst;
+  v->recv_src = h->ws.recv_src;
+  v->status = h->ws.status;
+  v->keep = h->ws.keep;
+  v->native_row = h->ws.native_row;
+  v->seg_first = h->ws.seg_first;
+  v->seg_count = h->ws.seg_count;
+  v->segments = h->ws.segments;
+  v->n_segments = h->ws.n_segments;
+  v->load = h->ws.load;
+  v->replica = h->ws.replica;
+  return EP_OK;
+}
+
+ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags) {
+  if (!h || !flags) return EP_ERR_INVALID_ARG;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, h->ws.status, sizeof v, hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return EP_ERR_HIP;
+  *flags = v;
+  return EP_OK;
+}
+
+ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(topk_idx, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_idx, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = hip_status(epk::launch_plan(g, h->ws, static_cast<const int32_t *>(topk_idx->data),
+                                   as_stream(stream)));
+  if (st == EP_OK) h->planned = true;
+  return st;
+}
+
+ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens, const ep_tensor_t *topk_weights,
+                        ep_tensor_t *recv_tokens, ep_tensor_t *recv_scales,
+                        ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
+                        void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  const int32_t H = h->g->cfg.hidden;
+  ep_status_t st = check_tensor(tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_2d(tokens, g.T, H)) return EP_ERR_BAD_SHAPE;
+  const bool fp8 = recv_scales != nullptr;
+  st = check_tensor(recv_tokens, EP_TAG_TOKENS, fp8 ? EP_DTYPE_FP8_E4M3 : EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_rows(recv_tokens, g.rows, H)) return EP_ERR_BAD_SHAPE;
+  if (fp8) {
+    if (H % 128 != 0) return EP_ERR_UNSUPPORTED;
+    st = check_tensor(recv_scales, EP_TAG_FP8_SCALES, EP_DTYPE_FP32);
+    if (st != EP_OK) return st;
+    if (!is_rows(recv_scales, g.rows, H / 128)) return EP_ERR_BAD_SHAPE;
+  }
+  if (topk_weights) {
+    st = check_tensor(topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+    if (st != EP_OK) return st;
+    if (!is_2d(topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  }
+  if (recv_topk_idx) {
+    st = check_tensor(recv_topk_idx, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+    if (st != EP_OK) return st;
+    if (!(recv_topk_idx->ndim == 1 && recv_topk_idx->sizes[0] == g.rows)) return EP_ERR_BAD_SHAPE;
+  }
+  if (recv_topk_weights) {
+    if (!topk_weights) return EP_ERR_INVALID_ARG;
+    st = check_tensor(recv_topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+    if (st != EP_OK) return st;
+    if (!(recv_topk_weights->ndim == 1 && recv_topk_weights->sizes[0] == g.rows))
+      return EP_ERR_BAD_SHAPE;
+  }
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  if (fp8)
+    e = epk::launch_dispatch_fp8(g, h->ws, static_cast<const uint16_t *>(tokens->data), H,
+                                 static_cast<uint8_t *>(recv_tokens->data),
+                                 static_cast<float *>(recv_scales->data), s);
+  else
+    e = epk::launch_dispatch_bf16(g, h->ws, static_cast<const uint16_t *>(tokens->data), H,
+                                  static_cast<uint16_t *>(recv_tokens->data), s);
+  if (e == hipSuccess && (recv_topk_idx || recv_topk_weights))
+    e = epk::launch_recv_meta(
+        g, h->ws, topk_weights ? static_cast<const float *>(topk_weights->data) : nullptr,
+        recv_topk_idx ? static_cast<int32_t *>(recv_topk_idx->data) : nullptr,
+        recv_topk_weights ? static_cast<float *>(recv_topk_weights->data) : nullptr, s);
+  return hip_status(e);
+}
+
+ep_status_t ep_combine(ep_handle_t h, const ep_tensor_t *expert_out,
+                       const ep_tensor_t *topk_weights, ep_tensor_t *out_tokens, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  const int32_t H = h->g->cfg.hidden;
+  ep_status_t st = check_tensor(expert_out, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_rows(expert_out, g.rows, H)) return EP_ERR_BAD_SHAPE;
+  if (topk_weights) {
+    st = check_tensor(topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+    if (st != EP_OK) return st;
+    if (!is_2d(topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  }
+  if (!out_tokens) return EP_ERR_INVALID_ARG;
+  const bool out_fp32 = out_tokens->dtype == EP_DTYPE_FP32;
+  st = check_tensor(out_tokens, EP_TAG_TOKENS, out_fp32 ? EP_DTYPE_FP32 : EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_2d(out_tokens, g.T, H)) return EP_ERR_BAD_SHAPE;
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return hip_status(epk::launch_combine(
+      g, h->ws, static_cast<const uint16_t *>(expert_out->data), H,
+      topk_weights ? static_cast<const float *>(topk_weights->data) : nullptr, out_tokens->data,
+      out_fp32, as_stream(stream)));
+}
+
+ep_status_t ep_combine_bwd(ep_handle_t h, const ep_tensor_t *grad_tokens,
+                           const ep_tensor_t *expert_out, const ep_tensor_t *topk_weights,
+                           ep_tensor_t *grad_expert_out, ep_tensor_t *grad_topk_weights,
+                           void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  const int32_t H = h->g->cfg.hidden;
+  ep_status_t st = check_tensor(grad_tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_2d(grad_tokens, g.T, H)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(expert_out, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_rows(expert_out, g.rows, H)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(grad_expert_out, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  if (!is_rows(grad_expert_out, g.rows, H)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(grad_topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(grad_topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return hip_status(epk::launch_combine_bwd(
+      g, h->ws, static_cast<const uint16_t *>(grad_tokens->data),
+      static_cast<const uint16_t *>(expert_out->data), H,
+      static_cast<const float *>(topk_weights->data),
+      static_cast<uint16_t *>(grad_expert_out->data),
+      static_cast<float *>(grad_topk_weights->data), as_stream(stream)));
+}
+
+ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
+                               const ep_tensor_t *replica_expert, ep_tensor_t *owner_grads,
+                               void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  ep_status_t st = check_tensor(replica_grads, EP_TAG_EXPERT_GRADS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  st = check_tensor(owner_grads, EP_TAG_EXPERT_GRADS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (replica_grads->ndim < 2 || owner_grads->ndim < 2) return EP_ERR_BAD_SHAPE;
+  const int64_t n = replica_grads->sizes[0];
+  const int64_t P = numel(replica_grads) / (n > 0 ? n : 1);
+  const int64_t E_owner = owner_grads->sizes[0];
+  int64_t Po = 1;
+  for (int i = 1; i < owner_grads->ndim; ++i) Po *= owner_grads->sizes[i];
+  if (replica_grads->ndim != owner_grads->ndim) return EP_ERR_BAD_SHAPE;
+  for (int i = 1; i < owner_grads->ndim; ++i)
+    if (replica_grads->sizes[i] != owner_grads->sizes[i]) return EP_ERR_BAD_SHAPE;
+  if (n > 65535 || E_owner > INT32_MAX || Po != P) return EP_ERR_BAD_SHAPE;
+  const int32_t *rep_e = nullptr;
+  if (replica_expert) {
+    st = check_tensor(replica_expert, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+    if (st != EP_OK) return st;
+    if (!(replica_expert->ndim == 1 && replica_expert->sizes[0] == n)) return EP_ERR_BAD_SHAPE;
+    rep_e = static_cast<const int32_t *>(replica_expert->data);
+  } else {
+    if (h->geo.layout != EP_LAYOUT_STATIC) return EP_ERR_UNSUPPORTED;
+    if (n != (int64_t)h->geo.R * h->geo.S) return EP_ERR_BAD_SHAPE;
+    if (!h->planned) return EP_ERR_NOT_PLANNED;
+    rep_e = h->ws.replica;
+  }
+  return hip_status(epk::launch_dup_reduce(
+      static_cast<const uint16_t *>(replica_grads->data), rep_e, (int32_t)n, P, (int32_t)E_owner,
+      static_cast<float *>(owner_grads->data), h->ws.status, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// ep_internal.h -- internal declarations shared by the C ABI (ep_api.cpp) and
+// the gfx950 kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epk {
+
+// Layout tile: 16 waves x 4 chunks x 64 lanes of flat entries t*k + j.
+constexpr int kTileThreads = 1024;
+constexpr int kTileWaves = kTileThreads / 64;
+constexpr int kTileChunks = 4;
+constexpr int kTileEntries = kTileThreads * kTileChunks;  // 4096
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kLdsLimit = 65536;
+
+constexpr uint32_t kFlagIndexRange = 1u;
+constexpr uint32_t kFlagCapacity = 2u;
+constexpr uint32_t kFlagSlotBudget = 4u;
+
+enum Layout : int32_t { kLL = 0, kHT = 1, kStatic = 2 };
+
+// Device tables carved out of the caller's workspace (each 256-byte aligned).
+struct Workspace {
+  uint32_t *status;      // [1]  EP_FLAG_* bits
+  uint32_t *ticket;      // [1]  blocks of the layout kernel that finished
+  int32_t *counts;       // [E]
+  int32_t *offsets;      // [E+1]
+  int32_t *eidx;         // [n]  validated expert id of each entry (-1 = skipped)
+  int32_t *lrank;        // [n]  position of the entry among its expert's entries in its tile
+  int32_t *dst;          // [n]
+  int32_t *tile_hist;    // [ntiles][E] per-tile counts, then per-tile exclusive bases
+  uint32_t *tile_flags;  // [ntiles]
+  int32_t *recv_src;     // [rows]
+  // STATIC plan
+  int32_t *keep, *native_row, *seg_first, *seg_count;  // [E] each
+  int32_t *segments;     // [(E+R)*5]
+  int32_t *n_segments;   // [1]
+  int32_t *load;         // [R]
+  int32_t *replica;      // [R*S]
+};
+
+struct Geometry {
+  int32_t T, k, E, R, S, layout, cap;
+  int32_t C;        // STATIC rows per rank
+  int32_t ntiles;   // layout tiles (>= 1)
+  int32_t nbits;    // bits of an expert id, >= 1
+  int64_t n;        // T*k
+  int64_t rows;     // receive rows
+};
+
+// Byte size of the workspace for `g` (base == nullptr) or carve it (base != nullptr).
+size_t carve_workspace(const Geometry &g, char *base, Workspace *ws);
+size_t plan_lds_bytes(int32_t E, int32_t R);
+
+// Launchers (return the HIP error of the launch).
+hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,
+                       hipStream_t s);
+hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const uint16_t *x,
+                                int32_t H, uint16_t *recv, hipStream_t s);
+hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uint16_t *x,
+                               int32_t H, uint8_t *recv_q, float *recv_scale, hipStream_t s);
+hipError_t launch_recv_meta(const Geometry &g, const Workspace &ws, const float *topk_w,
+                            int32_t *recv_idx, float *recv_w, hipStream_t s);
+hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t *rows,
+                          int32_t H, const float *topk_w, void *out, bool out_fp32,
+                          hipStream_t s);
+hipError_t launch_combine_bwd(const Geometry &g, const Workspace &ws, const uint16_t *gy,
+                              const uint16_t *expert_out, int32_t H, const float *topk_w,
+                              uint16_t *grad_out, float *grad_w, hipStream_t s);
+hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
+                             int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
+
+}  // namespace epk

@@ -1,0 +1,410 @@
+// plan.hip -- layout of one pass on gfx950: per-expert counts, offsets,
+// stable destination rows for the LL / HT layouts (NCCL EP paper listing,
+// Table III; Figures 3-4) and the static-shape plan (MoonEP article,
+// paragraphs 3-5), all on the device with no host round trip (MoonEP
+// article, paragraph 4: no per-layer host synchronisation).
+//
+// k_plan_tiles: one 1024-thread workgroup per tile of 4096 flat entries.
+//   Each wave ranks its 256 entries chunk by chunk (64 lanes): lanes with
+//   the same expert are found with one ballot per bit of the expert id
+//   (multisplit), the rank inside the chunk is the popcount of lower peers,
+//   and a per-wave LDS counter per expert carries ranks across chunks.  A
+//   per-expert scan over the 16 waves gives ranks inside the tile and the
+//   tile histogram.  No atomics touch the ranks, so every output is
+//   deterministic.  The last workgroup to finish (ticket counter) scans the
+//   tile histograms into per-tile bases, counts and offsets, raises the
+//   flags and, for the static layout, runs the planner.  With a single tile
+//   that workgroup also writes the destinations, so small batches need one
+//   launch.
+// k_plan_dst: one thread per entry: dst from its tile base + tile rank.
+#include "device.h"
+#include "ep_internal.h"
+
+namespace epk {
+
+struct PlanArgs {
+  Geometry g;
+  Workspace ws;
+  const int32_t *idx;
+};
+
+// In-place exclusive scan of a[0, n) in LDS (n <= 4 * blockDim.x) by the
+// whole workgroup; returns the total.  tmp: LDS scratch of waves + 1 ints.
+__device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int per = (n + blockDim.x - 1) / blockDim.x;  // <= 4
+  const int beg = tid * per;
+  int32_t loc[4];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int32_t v = (i < per && beg + i < n) ? a[beg + i] : 0;
+    loc[i] = v;
+    sum += v;
+  }
+  int32_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int32_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < nw; ++i) {
+      int32_t v = tmp[i];
+      tmp[i] = run;
+      run += v;
+    }
+    tmp[nw] = run;
+  }
+  __syncthreads();
+  int32_t excl = tmp[w] + incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < per && beg + i < n) a[beg + i] = excl;
+    excl += loc[i];
+  }
+  const int32_t total = tmp[nw];
+  __syncthreads();
+  return total;
+}
+
+// Largest i in [0, n) with a[i] <= x, for non-decreasing a with a[0] <= x.
+__device__ __forceinline__ int32_t last_le(const int32_t *a, int32_t n, int32_t x) {
+  int32_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Receive row of an entry of expert e at position pos among e's entries.
+__device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace &ws,
+                                             const int32_t *offs, int32_t e, int32_t pos) {
+  if (g.layout == kHT) return offs[e] + pos;
+  if (g.layout == kLL) return pos < g.cap ? e * g.cap + pos : -1;
+  const int32_t m = g.E / g.R;
+  const int32_t kp = ws.keep[e];
+  if (pos < kp) return (e / m) * g.C + ws.native_row[e] + pos;
+  if (ws.seg_count[e] <= 0) return -1;
+  int32_t lo = ws.seg_first[e], hi = lo + ws.seg_count[e] - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if (ws.segments[mid * 5 + 2] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t *s = ws.segments + lo * 5;
+  return s[1] * g.C + s[4] + (pos - s[2]);
+}
+
+// Static-shape planner, run by one workgroup on the final counts.
+//  targets: rank r gets floor(N/R) + (r < N mod R) rows;
+//  donors (own rows > target) shed the tail rows of their hottest experts
+//  (count descending, id ascending) until they are at target;
+//  the shed pieces (donor rank, then walk order) and the receivers' deficits
+//  (rank order) are laid end to end; each overlap is one segment, placed in
+//  the receiver behind its own rows; a receiver's replica slot of a segment
+//  is the segment's rank among the pieces that reach that receiver.
+__device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_t *cnt,
+                            int32_t N, int32_t *pl, int32_t *tmp, uint32_t *s_flags) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int32_t E = g.E, R = g.R, S = g.S, m = E / R;
+  int32_t *tgt = pl;
+  int32_t *home = tgt + R;
+  int32_t *D = home + R;
+  int32_t *rbase = D + R;          // [R+1] receiver interval starts
+  int32_t *rord = rbase + R + 1;   // [R+1] receivers before r
+  int32_t *rshed = rord + R + 1;   // [R+1] spill base of rank r
+  int32_t *rnp = rshed + R + 1;    // [R+1] first piece of rank r
+  int32_t *ord = rnp + R + 1;      // [E]
+  int32_t *shed = ord + E;         // [E]
+  int32_t *piece_e = shed + E;     // [E]
+  int32_t *piece_start = piece_e + E;  // [E+1]
+  int32_t *nseg = piece_start + E + 1; // [E+1]
+
+  for (int r = tid; r < R; r += nt) {
+    const int32_t t = N / R + (r < N % R ? 1 : 0);
+    int32_t h = 0;
+    for (int i = 0; i < m; ++i) h += cnt[r * m + i];
+    tgt[r] = t;
+    home[r] = h;
+    D[r] = h < t ? t - h : 0;
+    rbase[r] = D[r];
+    rord[r] = D[r] > 0 ? 1 : 0;
+    ws.load[r] = t;
+  }
+  for (int i = tid; i < R * S; i += nt) ws.replica[i] = -1;
+  __syncthreads();
+
+  for (int e = tid; e < E; e += nt) {
+    const int32_t r = e / m, c = cnt[e];
+    int32_t o = 0, before = 0;
+    for (int i = 0; i < m; ++i) {
+      const int32_t e2 = r * m + i, c2 = cnt[e2];
+      const bool hotter = c2 > c || (c2 == c && e2 < e);
+      o += hotter ? 1 : 0;
+      before += hotter ? c2 : 0;
+    }
+    const int32_t X = home[r] - tgt[r];
+    int32_t s = 0;
+    if (X > 0) {
+      s = X - before;
+      s = s < 0 ? 0 : (s > c ? c : s);
+    }
+    ord[e] = o;
+    shed[e] = s;
+    ws.keep[e] = c - s;
+  }
+  __syncthreads();
+
+  for (int e = tid; e < E; e += nt) {
+    const int32_t r = e / m;
+    int32_t row = 0;
+    for (int32_t e2 = r * m; e2 < e; ++e2) row += cnt[e2] - shed[e2];
+    ws.native_row[e] = row;
+    ws.seg_first[e] = 0;
+    ws.seg_count[e] = 0;
+  }
+  for (int r = tid; r < R; r += nt) {
+    int32_t s = 0, np = 0;
+    for (int i = 0; i < m; ++i) {
+      const int32_t v = shed[r * m + i];
+      s += v;
+      np += v > 0 ? 1 : 0;
+    }
+    rshed[r] = s;
+    rnp[r] = np;
+  }
+  __syncthreads();
+  block_exclusive_scan(rbase, R, tmp);
+  block_exclusive_scan(rord, R, tmp);
+  block_exclusive_scan(rshed, R, tmp);
+  const int32_t npieces = block_exclusive_scan(rnp, R, tmp);
+
+  for (int e = tid; e < E; e += nt) {
+    if (shed[e] == 0) continue;
+    const int32_t r = e / m;
+    int32_t within = 0, cb = 0;
+    for (int i = 0; i < m; ++i) {
+      const int32_t e2 = r * m + i;
+      if (shed[e2] > 0 && ord[e2] < ord[e]) {
+        within += shed[e2];
+        ++cb;
+      }
+    }
+    const int32_t p = rnp[r] + cb;
+    piece_e[p] = e;
+    piece_start[p] = rshed[r] + within;
+  }
+  __syncthreads();
+
+  for (int p = tid; p < npieces; p += nt) {
+    const int32_t e = piece_e[p], a0 = piece_start[p], b0 = a0 + shed[e];
+    const int32_t rlo = last_le(rbase, R, a0), rhi = last_le(rbase, R, b0 - 1);
+    nseg[p] = rord[rhi] - rord[rlo] + 1;
+  }
+  __syncthreads();
+  const int32_t nsegs = block_exclusive_scan(nseg, npieces, tmp);
+  if (tid == 0) *ws.n_segments = nsegs;
+
+  for (int p = tid; p < npieces; p += nt) {
+    const int32_t e = piece_e[p], a0 = piece_start[p], b0 = a0 + shed[e];
+    const int32_t kp = cnt[e] - shed[e];
+    const int32_t rlo = last_le(rbase, R, a0), rhi = last_le(rbase, R, b0 - 1);
+    int32_t sid = nseg[p];
+    ws.seg_first[e] = sid;
+    ws.seg_count[e] = rord[rhi] - rord[rlo] + 1;
+    for (int32_t r = rlo; r <= rhi; ++r) {
+      if (D[r] == 0) continue;
+      const int32_t lo = a0 > rbase[r] ? a0 : rbase[r];
+      const int32_t hi = b0 < rbase[r] + D[r] ? b0 : rbase[r] + D[r];
+      int32_t *s = ws.segments + (int64_t)sid * 5;
+      s[0] = e;
+      s[1] = r;
+      s[2] = kp + (lo - a0);
+      s[3] = hi - lo;
+      s[4] = home[r] + (lo - rbase[r]);
+      ++sid;
+      const int32_t slot = p - last_le(piece_start, npieces, rbase[r]);
+      if (slot < S) ws.replica[r * S + slot] = e;
+      else atomicOr(s_flags, kFlagSlotBudget);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
+  extern __shared__ int32_t lds[];
+  __shared__ uint32_t s_flags;
+  __shared__ int32_t s_last;
+  __shared__ int32_t s_tmp[kTileWaves + 2];
+  const Geometry &g = a.g;
+  const Workspace &ws = a.ws;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t E = g.E;
+  uint16_t *wcnt = reinterpret_cast<uint16_t *>(lds);  // [waves][E], <= 256 each
+
+  for (int i = tid; i < kTileWaves * E; i += kTileThreads) wcnt[i] = 0;
+  if (tid == 0) s_flags = 0;
+  __syncthreads();
+
+  const int64_t wbase = (int64_t)blockIdx.x * kTileEntries + (int64_t)w * (64 * kTileChunks);
+  int32_t ev[kTileChunks], rr[kTileChunks];
+  uint32_t flags = 0;
+#pragma unroll
+  for (int c = 0; c < kTileChunks; ++c) {
+    const int64_t f = wbase + c * 64 + lane;
+    int32_t e = -1;
+    if (f < g.n) {
+      const int32_t raw = a.idx[f];
+      if (raw >= 0 && raw < E) e = raw;
+      else if (raw != -1) flags |= kFlagIndexRange;
+      ws.eidx[f] = e;
+    }
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < g.nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    int32_t r = 0;
+    if (valid) {
+      const int32_t before = wcnt[w * E + e];
+      r = before + __popcll(peers & ((1ull << lane) - 1ull));
+      if ((peers >> lane) == 1ull) wcnt[w * E + e] = (uint16_t)(before + __popcll(peers));
+    }
+    ev[c] = e;
+    rr[c] = r;
+  }
+  __syncthreads();
+
+  for (int e = tid; e < E; e += kTileThreads) {
+    int32_t run = 0;
+    for (int ww = 0; ww < kTileWaves; ++ww) {
+      const int32_t v = wcnt[ww * E + e];
+      wcnt[ww * E + e] = (uint16_t)run;
+      run += v;
+    }
+    ws.tile_hist[(int64_t)blockIdx.x * E + e] = run;
+  }
+  if (flags) atomicOr(&s_flags, flags);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kTileChunks; ++c) {
+    if (ev[c] >= 0) {
+      rr[c] += wcnt[w * E + ev[c]];
+      if (gridDim.x > 1) ws.lrank[wbase + c * 64 + lane] = rr[c];
+    }
+  }
+  if (tid == 0) ws.tile_flags[blockIdx.x] = s_flags;
+  for (int64_t r = (int64_t)blockIdx.x * kTileThreads + tid; r < g.rows;
+       r += (int64_t)gridDim.x * kTileThreads)
+    ws.recv_src[r] = -1;
+
+  // Publish this tile; the last one to arrive finishes the layout.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t t = atomicAdd(ws.ticket, 1u);
+    s_last = (t == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  int32_t *cnt = lds;           // [E]
+  int32_t *offs = lds + E;      // [E+1]
+  int32_t *pl = lds + 2 * E + 1;
+  const int32_t ntiles = gridDim.x;
+  for (int e = tid; e < E; e += kTileThreads) {
+    int32_t run = 0;
+    for (int32_t t = 0; t < ntiles; ++t) {
+      const int64_t i = (int64_t)t * E + e;
+      const int32_t v = ws.tile_hist[i];
+      ws.tile_hist[i] = run;
+      run += v;
+    }
+    cnt[e] = run;
+    offs[e] = run;
+    ws.counts[e] = run;
+  }
+  if (tid == 0) {
+    uint32_t fl = 0;
+    for (int32_t t = 0; t < ntiles; ++t) fl |= ws.tile_flags[t];
+    s_flags = fl;
+    *ws.ticket = 0;
+  }
+  __syncthreads();
+  const int32_t total = block_exclusive_scan(offs, E, s_tmp);
+  if (tid == 0) offs[E] = total;
+  __syncthreads();
+  for (int e = tid; e <= E; e += kTileThreads) ws.offsets[e] = offs[e];
+  if (g.layout == kLL) {
+    for (int e = tid; e < E; e += kTileThreads)
+      if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
+  } else if (g.layout == kStatic) {
+    plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) *ws.status = s_flags;
+
+  if (ntiles == 1) {
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c) {
+      const int64_t f = wbase + c * 64 + lane;
+      if (f < g.n) {
+        int32_t d = ev[c] >= 0 ? entry_dst(g, ws, offs, ev[c], rr[c]) : -1;
+        if (d >= g.rows) d = -1;
+        ws.dst[f] = d;
+        if (d >= 0) ws.recv_src[d] = (int32_t)f;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_plan_dst(PlanArgs a) {
+  const Geometry &g = a.g;
+  const Workspace &ws = a.ws;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= g.n) return;
+  const int32_t e = ws.eidx[f];
+  int32_t d = -1;
+  if (e >= 0) {
+    const int64_t tile = f / kTileEntries;
+    const int32_t pos = ws.tile_hist[tile * g.E + e] + ws.lrank[f];
+    d = entry_dst(g, ws, ws.offsets, e, pos);
+    if (d >= g.rows) d = -1;
+  }
+  ws.dst[f] = d;
+  if (d >= 0) ws.recv_src[d] = (int32_t)f;
+}
+
+size_t plan_lds_bytes(int32_t E, int32_t R) {
+  const size_t tiles = (size_t)kTileWaves * E * sizeof(uint16_t);
+  const size_t fin = (size_t)(2 * E + 1) * sizeof(int32_t) +
+                     (R > 0 ? (size_t)(5 * E + 7 * R + 8) * sizeof(int32_t) : 0);
+  return tiles > fin ? tiles : fin;
+}
+
+hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,
+                       hipStream_t s) {
+  PlanArgs a{g, ws, topk_idx};
+  const size_t lds = plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0);
+  hipLaunchKernelGGL(k_plan_tiles, dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (g.ntiles > 1) {
+    const int64_t blocks = (g.n + 255) / 256;
+    hipLaunchKernelGGL(k_plan_dst, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace epk

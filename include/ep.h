@@ -1,0 +1,267 @@
+/*
+ * ep.h -- C ABI of libep_mi355x.so: MoE expert-parallel token dispatch,
+ * combine, combine backward, static-shape planning and duplicated-expert
+ * gradient reduction, as hand-written HIP kernels for MI355X (gfx950).
+ *
+ * Logical expert-parallel ranks are regions of one receive buffer in the
+ * GPU's HBM; nothing here talks to another GPU.
+ *
+ * Sources the operations follow (cited by page title and section):
+ *   NCCL EP paper listing (arXiv 2603.13606): abstract (low-latency and
+ *     high-throughput modes), Table II (long-lived groups, per-pass
+ *     handles; combine gathers expert outputs back to token order),
+ *     Figure 2 (group once, then handle -> dispatch -> expert FFN ->
+ *     combine), Table III (LL: 3D expert-major output; HT: 2D output with
+ *     token counts), Table IV (tensor tags: tokens, top-k indices, top-k
+ *     weights, FP8 scales), Table V (dispatch returns received tokens,
+ *     indices and weights plus the handle), Figure 5 (one handle shared by
+ *     the forward and backward passes).
+ *   MoonEP article (Open Source For You), paragraphs 3-5: fixed per-rank
+ *     workload from a GPU planner that picks redundant experts from the
+ *     current routing; rows written straight to expert-grouped positions;
+ *     static shapes, no per-layer host synchronisation; at most E/R replica
+ *     slots per rank in training; duplicated-expert gradients folded into
+ *     the owner's gradients through a reduce buffer.
+ *
+ * Conventions shared by every call
+ *   Memory.     Every tensor is a non-owning view of caller-allocated device
+ *               memory, row-major and contiguous.  The library never
+ *               allocates or frees device memory.  A handle borrows the
+ *               caller's workspace until ep_handle_destroy.
+ *   Streams.    `stream` is a hipStream_t (NULL = the default stream).  All
+ *               compute calls only enqueue work and return at once.
+ *   Errors.     Argument errors are found on the host and returned before
+ *               anything is enqueued.  A failed kernel launch returns
+ *               EP_ERR_HIP.  Conditions only the data reveals (an expert id
+ *               out of range, an LL expert over capacity, a receiver needing
+ *               more replica slots than it has) are OR-ed into a device
+ *               status word as EP_FLAG_* bits and read with
+ *               ep_handle_status, the only call that waits for the GPU.
+ *   Dtypes.     tokens bf16; top-k indices int32; top-k weights fp32; FP8
+ *               rows OCP e4m3fn (bias 7, max 448); FP8 scales fp32.
+ *   Sizes.      H % 8 == 0 (16-byte rows); H % 128 == 0 for FP8 dispatch;
+ *               1 <= top_k <= 16; 1 <= E <= 1024; E % R == 0.
+ *   Threads.    A handle is used by one stream at a time; calls on one
+ *               handle from two streams without ordering race.
+ */
+#ifndef EP_MI355X_EP_H
+#define EP_MI355X_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = 1,         /* null pointer, bad size or inconsistent config */
+  EP_ERR_BAD_TAG = 2,             /* tensor tag does not match the argument's role */
+  EP_ERR_BAD_DTYPE = 3,
+  EP_ERR_BAD_SHAPE = 4,
+  EP_ERR_NOT_PLANNED = 5,         /* dispatch/combine before any ep_plan on the handle */
+  EP_ERR_WORKSPACE_TOO_SMALL = 6,
+  EP_ERR_UNSUPPORTED = 7,         /* a valid request this build does not serve */
+  EP_ERR_HIP = 8                  /* a HIP launch or copy failed */
+} ep_status_t;
+
+/* Device-detected conditions (bits of the status word, see ep_handle_status). */
+#define EP_FLAG_INDEX_RANGE 1u  /* a top-k index outside [0, E) other than -1; entry skipped */
+#define EP_FLAG_CAPACITY 2u     /* LL: an expert got more than `capacity` entries; extra dropped */
+#define EP_FLAG_SLOT_BUDGET 4u  /* STATIC: a rank needs more replica slots than slots_per_rank */
+
+/* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS is
+ * this library's addition for the duplicated-expert gradient reduce. */
+typedef enum ep_tensor_tag {
+  EP_TAG_TOKENS = 0,        /* token rows: dispatch in/out, combine in/out, their grads */
+  EP_TAG_TOPK_IDX = 1,      /* expert ids (int32); -1 = no expert */
+  EP_TAG_TOPK_WEIGHTS = 2,  /* router weights (fp32) and their gradients */
+  EP_TAG_FP8_SCALES = 3,    /* one fp32 scale per 128 channels of an FP8 row */
+  EP_TAG_EXPERT_GRADS = 4   /* expert parameter gradients */
+} ep_tensor_tag_t;
+
+typedef enum ep_dtype {
+  EP_DTYPE_BF16 = 0,
+  EP_DTYPE_FP32 = 1,
+  EP_DTYPE_FP8_E4M3 = 2,
+  EP_DTYPE_INT32 = 3
+} ep_dtype_t;
+
+/* Receive-buffer layouts (NCCL EP listing, Table III; MoonEP article, par. 3-4). */
+typedef enum ep_layout {
+  EP_LAYOUT_LL = 0,     /* [E, capacity, H]: expert-major, row e*capacity + position */
+  EP_LAYOUT_HT = 1,     /* [T*k, H]: rows grouped by expert, expert e from offsets[e] */
+  EP_LAYOUT_STATIC = 2  /* [R, C, H], C = ceil(T*k / R): every rank holds exactly its
+                           share of rows; hot experts' tail rows go to replicas */
+} ep_layout_t;
+
+/* Non-owning view of a contiguous row-major device tensor. */
+typedef struct ep_tensor {
+  void *data;           /* device pointer (may be NULL only if the tensor is empty) */
+  int32_t dtype;        /* ep_dtype_t */
+  int32_t tag;          /* ep_tensor_tag_t */
+  int32_t ndim;         /* 1..4 */
+  int32_t reserved;     /* must be 0 */
+  int64_t sizes[4];     /* sizes[0..ndim-1], outermost first */
+} ep_tensor_t;
+
+/* Long-lived configuration (NCCL EP listing, Table II: groups). */
+typedef struct ep_group_config {
+  int32_t num_experts;     /* E, 1..1024 */
+  int32_t num_ranks;       /* R logical ranks, E % R == 0; expert e lives on rank e / (E/R) */
+  int32_t hidden;          /* H, multiple of 8 */
+  int32_t top_k;           /* k, 1..16 */
+  int32_t max_tokens;      /* largest T a handle of this group may take */
+  int32_t layout;          /* ep_layout_t */
+  int32_t capacity;        /* LL only: rows per expert, >= 1 */
+  int32_t slots_per_rank;  /* STATIC only: replica slots S per rank, >= 0 */
+} ep_group_config_t;
+
+typedef struct ep_group *ep_group_t;
+typedef struct ep_handle *ep_handle_t;
+
+/* Device pointers into a handle's workspace, valid while the handle lives.
+ * Contents are defined once the producing call has completed on the stream. */
+typedef struct ep_handle_view {
+  int32_t num_tokens;      /* T */
+  int32_t top_k;           /* k */
+  int32_t num_experts;     /* E */
+  int32_t num_ranks;       /* R */
+  int64_t recv_rows;       /* rows of the receive buffer: T*k (HT), E*cap (LL), R*C (STATIC) */
+  int32_t rank_rows;       /* STATIC: C; LL: capacity; HT: T*k */
+  int32_t max_segments;    /* STATIC: E + R (size of the segment table), else 0 */
+  int32_t *counts;         /* [E]   entries routed to each expert (ep_plan) */
+  int32_t *offsets;        /* [E+1] exclusive prefix sum of counts; offsets[E] = total */
+  int32_t *dst;            /* [T*k] receive row of entry t*k+j, -1 if skipped/dropped */
+  int32_t *recv_src;       /* [recv_rows] entry t*k+j held by each row, -1 if none */
+  uint32_t *status;        /* [1]   EP_FLAG_* bits of the last ep_plan (+ dup reduce) */
+  /* STATIC only (NULL otherwise): */
+  int32_t *keep;           /* [E] rows of e kept on its home rank */
+  int32_t *native_row;     /* [E] first row of e's kept rows inside its home rank */
+  int32_t *seg_first;      /* [E] first segment of e (segments of e are consecutive) */
+  int32_t *seg_count;      /* [E] number of segments of e */
+  int32_t *segments;       /* [max_segments][5]: expert, rank, pos_begin, len, row_begin */
+  int32_t *n_segments;     /* [1] */
+  int32_t *load;           /* [R] rows used on each rank */
+  int32_t *replica;        /* [R][S] expert held in each replica slot, -1 if empty */
+} ep_handle_view_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *ep_status_string(ep_status_t st);
+
+/* Validate `cfg` and create a group (host memory only).
+ * Errors: EP_ERR_INVALID_ARG for a NULL argument or a value outside the
+ * ranges above; EP_ERR_UNSUPPORTED if the planner's on-chip tables for E
+ * and R would not fit. */
+ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out);
+ep_status_t ep_group_destroy(ep_group_t g);
+
+/* Bytes of device workspace a handle for `num_tokens` tokens needs. */
+ep_status_t ep_handle_workspace_bytes(ep_group_t g, int32_t num_tokens, size_t *bytes);
+
+/* Rows of the receive buffer for `num_tokens` tokens (see recv_rows). */
+ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
+
+/* Create a per-pass handle (NCCL EP listing, Table II: handles) over a
+ * caller-owned device workspace of `workspace_bytes` bytes, 256-byte
+ * aligned, whose first 256 bytes are zero when the handle is created (every
+ * ep_plan leaves them zero again).  Host bookkeeping only: nothing is
+ * enqueued.  Errors: EP_ERR_INVALID_ARG (NULL, misaligned, num_tokens < 0 or
+ * > max_tokens), EP_ERR_WORKSPACE_TOO_SMALL. */
+ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
+                             size_t workspace_bytes, ep_handle_t *out);
+ep_status_t ep_handle_destroy(ep_handle_t h);
+ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *view);
+
+/* Wait for `stream`, then return the status word's EP_FLAG_* bits in *flags.
+ * The only blocking call of the library; meant for tests and error checks. */
+ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
+
+/* Layout (and, for EP_LAYOUT_STATIC, the static-shape plan) of one pass.
+ * topk_idx: int32 [T, k], tag EP_TAG_TOPK_IDX.  Writes counts, offsets,
+ * dst, recv_src and the status word; STATIC also writes the plan tables.
+ * Rows inside one expert keep the order of the flat entry index t*k + j.
+ * HT:     dst = offsets[e] + position of the entry among e's entries.
+ * LL:     dst = e*capacity + position; entries past capacity are dropped
+ *         (dst = -1, EP_FLAG_CAPACITY).
+ * STATIC: every rank r gets exactly floor(N/R) + (r < N mod R) rows (N =
+ *         valid entries).  Ranks whose own experts exceed that shed the last
+ *         rows of their hottest experts (count descending, id ascending);
+ *         the shed runs fill the short ranks in rank order, behind their own
+ *         rows; each short rank numbers the distinct experts it receives as
+ *         replica slots 0, 1, ... (more than S sets EP_FLAG_SLOT_BUDGET).
+ * Entries equal to -1 are skipped; other ids outside [0, E) are skipped and
+ * set EP_FLAG_INDEX_RANGE.  Enqueues one kernel if T*k <= 4096, else two.
+ * Re-planning a handle invalidates the layout every earlier output used. */
+ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream);
+
+/* Write every routed token row to its receive row (MoonEP article, par. 4:
+ * straight into the expert-grouped position, no staging copy).
+ * tokens:            bf16 [T, H], tag TOKENS.
+ * topk_weights:      fp32 [T, k], tag TOPK_WEIGHTS; needed only for
+ *                    recv_topk_weights, may be NULL otherwise.
+ * recv_tokens:       tag TOKENS, [recv_rows, H] or any shape whose leading
+ *                    sizes multiply to recv_rows (e.g. [E, cap, H],
+ *                    [R, C, H]); bf16 (bit copy) or, when recv_scales is not
+ *                    NULL, FP8 e4m3: per token and 128-channel block,
+ *                    scale = amax/448 (fp32 division; 1 if amax == 0),
+ *                    code = e4m3(clamp(x / scale, -448, 448)), round to
+ *                    nearest even.
+ * recv_scales:       NULL or fp32 [recv_rows, H/128], tag FP8_SCALES.
+ * recv_topk_idx:     NULL or int32 [recv_rows], tag TOPK_IDX: the expert of
+ *                    each row, -1 for rows no entry maps to.
+ * recv_topk_weights: NULL or fp32 [recv_rows], tag TOPK_WEIGHTS: the router
+ *                    weight of each row's entry, 0 for rows no entry maps to.
+ * Rows no entry maps to are not written.  EP_ERR_NOT_PLANNED before ep_plan. */
+ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens,
+                        const ep_tensor_t *topk_weights, ep_tensor_t *recv_tokens,
+                        ep_tensor_t *recv_scales, ep_tensor_t *recv_topk_idx,
+                        ep_tensor_t *recv_topk_weights, void *stream);
+
+/* Gather each token's expert outputs back to its place (NCCL EP listing,
+ * Table II):  out[t, :] = sum_j w[t, j] * expert_out[dst[t*k+j], :], j
+ * ascending, skipped entries contribute nothing, accumulated in fp32.
+ * expert_out:   bf16 [recv_rows, H] (any leading shape), tag TOKENS.
+ * topk_weights: fp32 [T, k], tag TOPK_WEIGHTS; NULL = all weights 1, which
+ *               is the backward of dispatch (sum of a token's row grads).
+ * out_tokens:   bf16 or fp32 [T, H], tag TOKENS (rounded to nearest even). */
+ep_status_t ep_combine(ep_handle_t h, const ep_tensor_t *expert_out,
+                       const ep_tensor_t *topk_weights, ep_tensor_t *out_tokens,
+                       void *stream);
+
+/* Backward of ep_combine (NCCL EP listing, Figure 5: same handle as the
+ * forward pass).  For every routed entry f = t*k + j with row d = dst[f]:
+ *   grad_expert_out[d, h] = bf16(w[t, j] * grad_tokens[t, h])  (the exact
+ *                           product rounded once, to nearest even)
+ *   grad_topk_weights[t, j] = sum_h grad_tokens[t, h] * expert_out[d, h]
+ *                           (fp32 accumulation; 0 for skipped entries)
+ * grad_tokens bf16 [T, H] tag TOKENS; expert_out bf16 [recv_rows, H] tag
+ * TOKENS; topk_weights fp32 [T, k]; grad_expert_out bf16 [recv_rows, H]
+ * tag TOKENS (rows no entry maps to are not written); grad_topk_weights
+ * fp32 [T, k] tag TOPK_WEIGHTS. */
+ep_status_t ep_combine_bwd(ep_handle_t h, const ep_tensor_t *grad_tokens,
+                           const ep_tensor_t *expert_out, const ep_tensor_t *topk_weights,
+                           ep_tensor_t *grad_expert_out, ep_tensor_t *grad_topk_weights,
+                           void *stream);
+
+/* Fold duplicated-expert gradients into the owners' gradients (MoonEP
+ * article, paragraph 5):
+ *   owner[e, p] <- fp32(owner[e, p] + sum_{i : expert[i] == e} replica[i, p])
+ * the sum taken in fp64 in replica order and rounded once.
+ * replica_grads:  bf16 [n, P...], tag EXPERT_GRADS.
+ * replica_expert: int32 [n], tag TOPK_IDX (owner expert of each replica,
+ *                 -1 = skip; other out-of-range ids are skipped and set
+ *                 EP_FLAG_INDEX_RANGE), or NULL to use the handle's STATIC
+ *                 replica table, in which case n must be R*S (slot-major).
+ * owner_grads:    fp32 [E_owner, P...], tag EXPERT_GRADS; same P.
+ * Does not need ep_plan unless replica_expert is NULL. */
+ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
+                               const ep_tensor_t *replica_expert, ep_tensor_t *owner_grads,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_EP_H */

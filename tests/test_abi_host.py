@@ -1,0 +1,245 @@
+"""Host-side tests of the C ABI: the library loads without a GPU, exports
+every entry point include/ep.h declares, and rejects bad arguments on the
+host before anything would be enqueued.  No kernel is launched here: every
+call either fails validation or is pure bookkeeping."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_ep_plan_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced by these tests
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ep.library_path()):
+        from combine_ep_plan_amd import build
+        build.build()
+    return ep.load_library()
+
+
+def declared_functions() -> list[str]:
+    names = []
+    with open(os.path.join(ROOT, "include", "ep.h")) as fh:
+        text = fh.read()
+    for m in re.finditer(r"^(?:const char \*|ep_status_t )(ep_\w+)\(", text, re.M):
+        names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    for need in ("ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd", "ep_dup_grad_reduce",
+                 "ep_group_create", "ep_handle_create", "ep_handle_status"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(ep._STATUS):
+        assert ep.ep_status_string(code) == name
+    assert ep.ep_status_string(99) == "EP_ERR_UNKNOWN"
+
+
+def cfg(**kw):
+    base = dict(num_experts=8, num_ranks=4, hidden=256, top_k=2, max_tokens=64,
+                layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0)
+    base.update(kw)
+    return ep.ep_group_config_t(*[base[f] for f, _ in ep.ep_group_config_t._fields_])
+
+
+def create(lib, **kw):
+    g = ctypes.c_void_p()
+    rc = lib.ep_group_create(ctypes.byref(cfg(**kw)), ctypes.byref(g))
+    return rc, g
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_experts=0), dict(num_experts=1025), dict(num_ranks=3), dict(num_ranks=0),
+    dict(hidden=12), dict(hidden=0), dict(top_k=0), dict(top_k=17), dict(max_tokens=-1),
+    dict(layout=7), dict(layout=ep.LAYOUT_LL, capacity=0), dict(layout=ep.LAYOUT_STATIC, slots_per_rank=-1),
+])
+def test_group_config_validation(lib, bad):
+    rc, _ = create(lib, **bad)
+    assert rc == 1  # EP_ERR_INVALID_ARG
+
+
+def test_group_null_arguments(lib):
+    g = ctypes.c_void_p()
+    assert lib.ep_group_create(None, ctypes.byref(g)) == 1
+    assert lib.ep_group_create(ctypes.byref(cfg()), None) == 1
+    assert lib.ep_group_destroy(None) == 1
+
+
+def test_group_planner_table_limit(lib):
+    rc, g = create(lib, num_experts=1024, num_ranks=1024, layout=ep.LAYOUT_STATIC, slots_per_rank=1)
+    assert rc == 0
+    lib.ep_group_destroy(g)
+
+
+@pytest.mark.parametrize("layout,kw,T,rows", [
+    (ep.LAYOUT_HT, {}, 64, 128),
+    (ep.LAYOUT_LL, dict(capacity=64), 64, 8 * 64),
+    (ep.LAYOUT_STATIC, dict(slots_per_rank=2), 63, 4 * 32),   # ceil(126/4) = 32
+    (ep.LAYOUT_HT, {}, 0, 0),
+])
+def test_recv_rows_and_workspace(lib, layout, kw, T, rows):
+    rc, g = create(lib, layout=layout, **kw)
+    assert rc == 0
+    r = ctypes.c_int64()
+    assert lib.ep_group_recv_rows(g, T, ctypes.byref(r)) == 0 and r.value == rows
+    b = ctypes.c_size_t()
+    assert lib.ep_handle_workspace_bytes(g, T, ctypes.byref(b)) == 0
+    assert b.value >= 4 * rows and b.value % 256 == 0
+    assert lib.ep_handle_workspace_bytes(g, 65, ctypes.byref(b)) == 1   # > max_tokens
+    lib.ep_group_destroy(g)
+
+
+def make_handle(lib, T=64, **kw):
+    rc, g = create(lib, **kw)
+    assert rc == 0
+    b = ctypes.c_size_t()
+    lib.ep_handle_workspace_bytes(g, T, ctypes.byref(b))
+    h = ctypes.c_void_p()
+    assert lib.ep_handle_create(g, T, ctypes.c_void_p(FAKE), b.value, ctypes.byref(h)) == 0
+    return g, h, b.value
+
+
+def test_handle_create_validation(lib):
+    rc, g = create(lib)
+    b = ctypes.c_size_t()
+    lib.ep_handle_workspace_bytes(g, 64, ctypes.byref(b))
+    h = ctypes.c_void_p()
+    assert lib.ep_handle_create(g, 64, None, b.value, ctypes.byref(h)) == 1
+    assert lib.ep_handle_create(g, 64, ctypes.c_void_p(FAKE + 8), b.value, ctypes.byref(h)) == 1
+    assert lib.ep_handle_create(g, 64, ctypes.c_void_p(FAKE), b.value - 1, ctypes.byref(h)) == 6
+    assert lib.ep_handle_create(g, 65, ctypes.c_void_p(FAKE), 1 << 30, ctypes.byref(h)) == 1
+    assert lib.ep_handle_create(g, -1, ctypes.c_void_p(FAKE), 1 << 30, ctypes.byref(h)) == 1
+    lib.ep_group_destroy(g)
+
+
+def test_handle_view_points_into_workspace(lib):
+    g, h, nbytes = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    v = ep.ep_handle_view_t()
+    assert lib.ep_handle_query(h, ctypes.byref(v)) == 0
+    assert v.num_tokens == 64 and v.top_k == 2 and v.num_experts == 8 and v.num_ranks == 4
+    assert v.recv_rows == 128 and v.rank_rows == 32 and v.max_segments == 12
+    for name in ("counts", "offsets", "dst", "recv_src", "status", "keep", "native_row",
+                 "seg_first", "seg_count", "segments", "n_segments", "load", "replica"):
+        p = getattr(v, name)
+        assert p is not None and FAKE <= p < FAKE + nbytes and p % 256 == 0
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def T(dtype, tag, *sizes, data=FAKE):
+    t = ep.ep_tensor_t()
+    t.data = data
+    t.dtype = dtype
+    t.tag = tag
+    t.ndim = len(sizes)
+    t.reserved = 0
+    for i, s in enumerate(sizes):
+        t.sizes[i] = s
+    return ctypes.pointer(t)
+
+
+BF16, F32, FP8, I32 = 0, 1, 2, 3
+
+
+def test_plan_argument_validation(lib):
+    g, h, _ = make_handle(lib)
+    assert lib.ep_plan(h, None, None) == 1
+    assert lib.ep_plan(h, T(I32, ep.TAG_TOKENS, 64, 2), None) == 2
+    assert lib.ep_plan(h, T(F32, ep.TAG_TOPK_IDX, 64, 2), None) == 3
+    assert lib.ep_plan(h, T(I32, ep.TAG_TOPK_IDX, 64, 3), None) == 4
+    assert lib.ep_plan(h, T(I32, ep.TAG_TOPK_IDX, 128), None) == 4
+    assert lib.ep_plan(h, T(I32, ep.TAG_TOPK_IDX, 64, 2, data=None), None) == 1
+    assert lib.ep_plan(None, T(I32, ep.TAG_TOPK_IDX, 64, 2), None) == 1
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_dispatch_argument_validation(lib):
+    g, h, _ = make_handle(lib)
+    x = T(BF16, ep.TAG_TOKENS, 64, 256)
+    w = T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2)
+    recv = T(BF16, ep.TAG_TOKENS, 128, 256)
+    D = lib.ep_dispatch
+    assert D(h, T(BF16, ep.TAG_TOKENS, 64, 255), w, recv, None, None, None, None) == 4
+    assert D(h, x, w, T(BF16, ep.TAG_TOKENS, 127, 256), None, None, None, None) == 4
+    assert D(h, x, w, T(F32, ep.TAG_TOKENS, 128, 256), None, None, None, None) == 3
+    assert D(h, x, w, T(BF16, ep.TAG_FP8_SCALES, 128, 256), None, None, None, None) == 2
+    assert D(h, x, T(F32, ep.TAG_TOPK_WEIGHTS, 64, 3), recv, None, None, None, None) == 4
+    # FP8 output needs FP8 rows and H % 128 == 0 (H = 256 here: fine)
+    assert D(h, x, w, recv, T(F32, ep.TAG_FP8_SCALES, 128, 2), None, None, None) == 3
+    assert D(h, x, w, T(FP8, ep.TAG_TOKENS, 128, 256), T(F32, ep.TAG_FP8_SCALES, 128, 3),
+             None, None, None) == 4
+    assert D(h, x, None, recv, None, None, T(F32, ep.TAG_TOPK_WEIGHTS, 128), None) == 1
+    assert D(h, x, w, recv, None, T(I32, ep.TAG_TOPK_IDX, 127), None, None) == 4
+    # valid arguments, but the handle has never been planned
+    assert D(h, x, w, recv, None, T(I32, ep.TAG_TOPK_IDX, 128), T(F32, ep.TAG_TOPK_WEIGHTS, 128), None) == 5
+    assert D(h, x, w, T(BF16, ep.TAG_TOKENS, 4, 32, 256), None, None, None, None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_fp8_needs_hidden_multiple_of_128(lib):
+    g, h, _ = make_handle(lib, hidden=136)
+    x = T(BF16, ep.TAG_TOKENS, 64, 136)
+    assert lib.ep_dispatch(h, x, None, T(FP8, ep.TAG_TOKENS, 128, 136),
+                           T(F32, ep.TAG_FP8_SCALES, 128, 1), None, None, None) == 7
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_combine_and_bwd_argument_validation(lib):
+    g, h, _ = make_handle(lib)
+    rows = T(BF16, ep.TAG_TOKENS, 128, 256)
+    w = T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2)
+    y = T(BF16, ep.TAG_TOKENS, 64, 256)
+    C = lib.ep_combine
+    assert C(h, rows, w, None, None) == 1
+    assert C(h, rows, w, T(BF16, ep.TAG_TOKENS, 63, 256), None) == 4
+    assert C(h, rows, w, T(I32, ep.TAG_TOKENS, 64, 256), None) == 3
+    assert C(h, T(BF16, ep.TAG_TOPK_IDX, 128, 256), w, y, None) == 2
+    assert C(h, rows, w, y, None) == 5
+    assert C(h, rows, None, T(F32, ep.TAG_TOKENS, 64, 256), None) == 5
+    B = lib.ep_combine_bwd
+    gw = T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2)
+    assert B(h, y, rows, None, rows, gw, None) == 1
+    assert B(h, y, rows, w, rows, T(F32, ep.TAG_TOKENS, 64, 2), None) == 2
+    assert B(h, y, rows, w, T(BF16, ep.TAG_TOKENS, 128, 128), gw, None) == 4
+    assert B(h, y, rows, w, rows, gw, None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_dup_reduce_argument_validation(lib):
+    g, h, _ = make_handle(lib)
+    rep = T(BF16, ep.TAG_EXPERT_GRADS, 2, 64, 16)
+    own = T(F32, ep.TAG_EXPERT_GRADS, 8, 64, 16)
+    ids = T(I32, ep.TAG_TOPK_IDX, 2)
+    R = lib.ep_dup_grad_reduce
+    assert R(h, T(BF16, ep.TAG_TOKENS, 2, 64, 16), ids, own, None) == 2
+    assert R(h, rep, ids, T(F32, ep.TAG_EXPERT_GRADS, 8, 64, 8), None) == 4
+    assert R(h, rep, T(I32, ep.TAG_TOPK_IDX, 3), own, None) == 4
+    assert R(h, rep, None, own, None) == 7      # replica table only exists for STATIC
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+    g, h, _ = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    assert R(h, T(BF16, ep.TAG_EXPERT_GRADS, 7, 64, 16), None, own, None) == 4   # n != R*S
+    assert R(h, T(BF16, ep.TAG_EXPERT_GRADS, 8, 64, 16), None, own, None) == 5   # not planned
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
