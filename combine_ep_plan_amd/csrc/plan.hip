@@ -306,39 +306,52 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
        r += (int64_t)gridDim.x * kTileThreads)
     ws.recv_src[r] = -1;
 
-  // Publish this tile; the last one to arrive finishes the layout.
-  __threadfence();
+  // Publish this tile; the last one to arrive finishes the layout.  The
+  // barrier waits for every wave's stores; then a single wave makes them
+  // visible to the other XCDs (agent-scope release: one L2 write-back per
+  // workgroup, not one per wave) and takes a ticket.  The last workgroup's
+  // agent-scope acquire (one invalidate) lets all its waves see every tile.
+  // A single tile is the whole layout and needs no handshake at all.
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t t = atomicAdd(ws.ticket, 1u);
-    s_last = (t == gridDim.x - 1) ? 1 : 0;
+  if (gridDim.x > 1) {
+    if (tid == 0) {
+      __threadfence();
+      const uint32_t t = atomicAdd(ws.ticket, 1u);
+      s_last = (t == gridDim.x - 1) ? 1 : 0;
+      if (s_last) __threadfence();
+    }
+    __syncthreads();
+    if (!s_last) return;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
 
   int32_t *cnt = lds;           // [E]
   int32_t *offs = lds + E;      // [E+1]
   int32_t *pl = lds + 2 * E + 1;
   const int32_t ntiles = gridDim.x;
+  // Per-expert exclusive scan over the tiles.  The loads of 8 tiles are
+  // issued together so the scan costs ntiles/8 memory latencies, not ntiles.
   for (int e = tid; e < E; e += kTileThreads) {
     int32_t run = 0;
-    for (int32_t t = 0; t < ntiles; ++t) {
-      const int64_t i = (int64_t)t * E + e;
-      const int32_t v = ws.tile_hist[i];
-      ws.tile_hist[i] = run;
-      run += v;
+    for (int32_t t0 = 0; t0 < ntiles; t0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = t0 + u < ntiles ? ws.tile_hist[(int64_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < ntiles) ws.tile_hist[(int64_t)(t0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
     cnt[e] = run;
     offs[e] = run;
     ws.counts[e] = run;
   }
-  if (tid == 0) {
-    uint32_t fl = 0;
-    for (int32_t t = 0; t < ntiles; ++t) fl |= ws.tile_flags[t];
-    s_flags = fl;
-    *ws.ticket = 0;
+  for (int32_t t = tid; t < ntiles; t += kTileThreads) {
+    const uint32_t fl = ws.tile_flags[t];
+    if (fl) atomicOr(&s_flags, fl);
   }
+  if (tid == 0 && ntiles > 1) *ws.ticket = 0;
   __syncthreads();
   const int32_t total = block_exclusive_scan(offs, E, s_tmp);
   if (tid == 0) offs[E] = total;
@@ -350,7 +363,6 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   } else if (g.layout == kStatic) {
     plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
   }
-  __threadfence();
   __syncthreads();
   if (tid == 0) *ws.status = s_flags;
 

@@ -74,3 +74,18 @@ def sample_problem(dst: np.ndarray, tokens: np.ndarray, rows: torch.Tensor):
     else:
         gb = np.zeros((0, rows.shape[-1]), np.uint16)
     return local, gb, used
+
+
+def same_up_to_zero_sign_np(a: np.ndarray, b: np.ndarray) -> bool:
+    """bf16 bit patterns equal once -0 (0x8000) is read as +0."""
+    a = np.where(a == 0x8000, 0, a)
+    b = np.where(b == 0x8000, 0, b)
+    return bool(np.array_equal(a, b))
+
+
+def same_up_to_zero_sign(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Device version for bf16 tensors of equal shape."""
+    ai, bi = a.view(torch.int16), b.view(torch.int16)
+    neg0 = torch.tensor(-32768, dtype=torch.int16, device=a.device)
+    zero = torch.zeros((), dtype=torch.int16, device=a.device)
+    return bool(torch.equal(torch.where(ai == neg0, zero, ai), torch.where(bi == neg0, zero, bi)))

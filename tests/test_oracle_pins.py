@@ -426,7 +426,12 @@ def test_combine_roundtrip_identity_experts_is_exact():
     L = oracle.layout(inp.topk_idx, inp.cfg.E, "ht")
     recv = oracle.dispatch(inp.x, L.dst, L.rows)
     y = oracle.combine(recv, L.dst, inp.topk_w)
-    assert np.array_equal(y, inp.x)
+    # up to the sign of zero: the sum starts from +0, so -0 inputs come back +0
+    assert np.array_equal(np.where(y == 0x8000, 0, y), np.where(inp.x == 0x8000, 0, inp.x))
+    neg = np.array([[0x8000, 0x3F80]], np.uint16)
+    Ln = oracle.layout(np.array([[0, 1]], np.int32), 2, "ht")
+    yn = oracle.combine(oracle.dispatch(neg, Ln.dst, Ln.rows), Ln.dst, np.float32([[0.5, 0.5]]))
+    assert yn.tolist() == [[0x0000, 0x3F80]]
 
 
 def test_combine_one_hot_weights_copy_rows():
