@@ -12,7 +12,7 @@
 
 namespace epk {
 
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 512;
 
 template <int K, bool WEIGHTED, bool OUT_F32>
 __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict__ rows,

@@ -12,8 +12,8 @@
 
 namespace epk {
 
-constexpr int kRowThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kRowThreads = 512;
+constexpr int kUnroll = 2;
 
 template <int K>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__restrict__ x,
@@ -91,16 +91,26 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
   }
 }
 
-// Per receive row: expert id and router weight of the entry it holds.
-__global__ __launch_bounds__(256) void k_recv_meta(const int32_t *__restrict__ recv_src,
-                                                   const int32_t *__restrict__ eidx,
+// Per receive row: expert id and router weight of the entry it holds (-1 / 0
+// for rows no entry maps to: past offsets[E] in HT, past min(count, cap) in
+// an LL expert block, past load[r] in a STATIC rank block).
+__global__ __launch_bounds__(256) void k_recv_meta(Geometry g, Workspace ws,
                                                    const float *__restrict__ w,
                                                    int32_t *__restrict__ recv_idx,
-                                                   float *__restrict__ recv_w, int64_t rows) {
+                                                   float *__restrict__ recv_w) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const int32_t src = recv_src[r];
-  if (recv_idx) recv_idx[r] = src >= 0 ? eidx[src] : -1;
+  if (r >= g.rows) return;
+  bool used;
+  if (g.layout == kHT) {
+    used = r < ws.offsets[g.E];
+  } else {
+    const int32_t len = g.layout == kLL ? g.cap : g.C;
+    const int32_t b = (int32_t)r / len, slot = (int32_t)r - b * len;
+    const int32_t n = g.layout == kLL ? ws.counts[b] : ws.load[b];
+    used = slot < n;
+  }
+  const int32_t src = used ? ws.recv_src[r] : -1;
+  if (recv_idx) recv_idx[r] = src >= 0 ? ws.eidx[src] : -1;
   if (recv_w) recv_w[r] = src >= 0 ? w[src] : 0.0f;
 }
 
@@ -135,8 +145,8 @@ hipError_t launch_recv_meta(const Geometry &g, const Workspace &ws, const float 
                             int32_t *recv_idx, float *recv_w, hipStream_t s) {
   if (g.rows == 0) return hipSuccess;
   const int64_t blocks = (g.rows + 255) / 256;
-  hipLaunchKernelGGL(k_recv_meta, dim3((unsigned)blocks), dim3(256), 0, s, ws.recv_src, ws.eidx,
-                     topk_w, recv_idx, recv_w, g.rows);
+  hipLaunchKernelGGL(k_recv_meta, dim3((unsigned)blocks), dim3(256), 0, s, g, ws, topk_w,
+                     recv_idx, recv_w);
   return hipGetLastError();
 }
 

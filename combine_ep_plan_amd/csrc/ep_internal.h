@@ -7,11 +7,11 @@
 
 namespace epk {
 
-// Layout tile: 16 waves x 4 chunks x 64 lanes of flat entries t*k + j.
+// Layout tile: 16 waves x 2 chunks x 64 lanes of flat entries t*k + j.
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / 64;
-constexpr int kTileChunks = 4;
-constexpr int kTileEntries = kTileThreads * kTileChunks;  // 4096
+constexpr int kTileChunks = 2;
+constexpr int kTileEntries = kTileThreads * kTileChunks;  // 2048
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kLdsLimit = 65536;

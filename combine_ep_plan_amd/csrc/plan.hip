@@ -4,8 +4,8 @@
 // paragraphs 3-5), all on the device with no host round trip (MoonEP
 // article, paragraph 4: no per-layer host synchronisation).
 //
-// k_plan_tiles: one 1024-thread workgroup per tile of 4096 flat entries.
-//   Each wave ranks its 256 entries chunk by chunk (64 lanes): lanes with
+// k_plan_tiles: one 1024-thread workgroup per tile of 2048 flat entries.
+//   Each wave ranks its 128 entries chunk by chunk (64 lanes): lanes with
 //   the same expert are found with one ballot per bit of the expert id
 //   (multisplit), the rank inside the chunk is the popcount of lower peers,
 //   and a per-wave LDS counter per expert carries ranks across chunks.  A
@@ -13,10 +13,12 @@
 //   tile histogram.  No atomics touch the ranks, so every output is
 //   deterministic.  The last workgroup to finish (ticket counter) scans the
 //   tile histograms into per-tile bases, counts and offsets, raises the
-//   flags and, for the static layout, runs the planner.  With a single tile
-//   that workgroup also writes the destinations, so small batches need one
-//   launch.
+//   flags and, for the static layout, runs the planner.  A single tile keeps
+//   its histogram in LDS, needs no handshake and also writes the
+//   destinations, so small batches take one launch.
 // k_plan_dst: one thread per entry: dst from its tile base + tile rank.
+// recv_src is written for the rows that hold an entry; which rows those are
+// follows from counts (LL), load (STATIC) or offsets[E] (HT).
 #include "device.h"
 #include "ep_internal.h"
 
@@ -28,48 +30,30 @@ struct PlanArgs {
   const int32_t *idx;
 };
 
-// In-place exclusive scan of a[0, n) in LDS (n <= 4 * blockDim.x) by the
-// whole workgroup; returns the total.  tmp: LDS scratch of waves + 1 ints.
-__device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *tmp) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nw = blockDim.x >> 6;
-  const int per = (n + blockDim.x - 1) / blockDim.x;  // <= 4
-  const int beg = tid * per;
-  int32_t loc[4];
+// In-place exclusive scan of a[0, n) in LDS by the 64 lanes of the calling
+// wave; returns the total to every lane.  Each lane scans a contiguous run
+// of ceil(n/64) elements and the lane totals are scanned with shuffles, so
+// the scan needs no workgroup barrier (the caller synchronises around it).
+__device__ int32_t wave_exclusive_scan(int32_t *a, int32_t n) {
+  const int lane = threadIdx.x & 63;
+  const int32_t per = (n + 63) >> 6;
+  const int32_t beg = lane * per;
+  const int32_t end = beg + per < n ? beg + per : n;
   int32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int32_t v = (i < per && beg + i < n) ? a[beg + i] : 0;
-    loc[i] = v;
-    sum += v;
-  }
+  for (int32_t j = beg; j < end; ++j) sum += a[j];
   int32_t incl = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int32_t o = __shfl_up(incl, d);
+    const int32_t o = __shfl_up(incl, d);
     if (lane >= d) incl += o;
   }
-  if (lane == 63) tmp[w] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < nw; ++i) {
-      int32_t v = tmp[i];
-      tmp[i] = run;
-      run += v;
-    }
-    tmp[nw] = run;
+  int32_t run = incl - sum;
+  for (int32_t j = beg; j < end; ++j) {
+    const int32_t v = a[j];
+    a[j] = run;
+    run += v;
   }
-  __syncthreads();
-  int32_t excl = tmp[w] + incl - sum;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < per && beg + i < n) a[beg + i] = excl;
-    excl += loc[i];
-  }
-  const int32_t total = tmp[nw];
-  __syncthreads();
-  return total;
+  return __shfl(incl, 63);
 }
 
 // Largest i in [0, n) with a[i] <= x, for non-decreasing a with a[0] <= x.
@@ -110,22 +94,25 @@ __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace 
 //  (rank order) are laid end to end; each overlap is one segment, placed in
 //  the receiver behind its own rows; a receiver's replica slot of a segment
 //  is the segment's rank among the pieces that reach that receiver.
+// Every phase is parallel over ranks, experts, pieces or segments; the five
+// prefix sums are single-wave scans (four of them on four waves at once).
 __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_t *cnt,
-                            int32_t N, int32_t *pl, int32_t *tmp, uint32_t *s_flags) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+                            int32_t N, int32_t *pl, int32_t *s_small, uint32_t *s_flags) {
+  const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6;
   const int32_t E = g.E, R = g.R, S = g.S, m = E / R;
   int32_t *tgt = pl;
   int32_t *home = tgt + R;
   int32_t *D = home + R;
-  int32_t *rbase = D + R;          // [R+1] receiver interval starts
-  int32_t *rord = rbase + R + 1;   // [R+1] receivers before r
-  int32_t *rshed = rord + R + 1;   // [R+1] spill base of rank r
-  int32_t *rnp = rshed + R + 1;    // [R+1] first piece of rank r
-  int32_t *ord = rnp + R + 1;      // [E]
-  int32_t *shed = ord + E;         // [E]
-  int32_t *piece_e = shed + E;     // [E]
+  int32_t *recv_rank = D + R;          // [R] rank of the i-th receiver
+  int32_t *rbase = recv_rank + R;      // [R+1] receiver interval starts
+  int32_t *rord = rbase + R + 1;       // [R+1] receivers before r
+  int32_t *rshed = rord + R + 1;       // [R+1] spill base of rank r
+  int32_t *rnp = rshed + R + 1;        // [R+1] first piece of rank r
+  int32_t *ord = rnp + R + 1;          // [E]
+  int32_t *shed = ord + E;             // [E]
+  int32_t *piece_e = shed + E;         // [E]
   int32_t *piece_start = piece_e + E;  // [E+1]
-  int32_t *nseg = piece_start + E + 1; // [E+1]
+  int32_t *nseg = piece_start + E + 1; // [E+1] segments of piece p, then first segment
 
   for (int r = tid; r < R; r += nt) {
     const int32_t t = N / R + (r < N % R ? 1 : 0);
@@ -167,8 +154,10 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     int32_t row = 0;
     for (int32_t e2 = r * m; e2 < e; ++e2) row += cnt[e2] - shed[e2];
     ws.native_row[e] = row;
-    ws.seg_first[e] = 0;
-    ws.seg_count[e] = 0;
+    if (shed[e] == 0) {
+      ws.seg_first[e] = 0;
+      ws.seg_count[e] = 0;
+    }
   }
   for (int r = tid; r < R; r += nt) {
     int32_t s = 0, np = 0;
@@ -181,11 +170,18 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     rnp[r] = np;
   }
   __syncthreads();
-  block_exclusive_scan(rbase, R, tmp);
-  block_exclusive_scan(rord, R, tmp);
-  block_exclusive_scan(rshed, R, tmp);
-  const int32_t npieces = block_exclusive_scan(rnp, R, tmp);
+  if (w == 0) wave_exclusive_scan(rbase, R);
+  else if (w == 1) wave_exclusive_scan(rord, R);
+  else if (w == 2) wave_exclusive_scan(rshed, R);
+  else if (w == 3) {
+    const int32_t np = wave_exclusive_scan(rnp, R);
+    if ((tid & 63) == 0) s_small[0] = np;
+  }
+  __syncthreads();
+  const int32_t npieces = s_small[0];
 
+  for (int r = tid; r < R; r += nt)
+    if (D[r] > 0) recv_rank[rord[r]] = r;
   for (int e = tid; e < E; e += nt) {
     if (shed[e] == 0) continue;
     const int32_t r = e / m;
@@ -209,32 +205,47 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     nseg[p] = rord[rhi] - rord[rlo] + 1;
   }
   __syncthreads();
-  const int32_t nsegs = block_exclusive_scan(nseg, npieces, tmp);
-  if (tid == 0) *ws.n_segments = nsegs;
-
-  for (int p = tid; p < npieces; p += nt) {
-    const int32_t e = piece_e[p], a0 = piece_start[p], b0 = a0 + shed[e];
-    const int32_t kp = cnt[e] - shed[e];
-    const int32_t rlo = last_le(rbase, R, a0), rhi = last_le(rbase, R, b0 - 1);
-    int32_t sid = nseg[p];
-    ws.seg_first[e] = sid;
-    ws.seg_count[e] = rord[rhi] - rord[rlo] + 1;
-    for (int32_t r = rlo; r <= rhi; ++r) {
-      if (D[r] == 0) continue;
-      const int32_t lo = a0 > rbase[r] ? a0 : rbase[r];
-      const int32_t hi = b0 < rbase[r] + D[r] ? b0 : rbase[r] + D[r];
-      int32_t *s = ws.segments + (int64_t)sid * 5;
-      s[0] = e;
-      s[1] = r;
-      s[2] = kp + (lo - a0);
-      s[3] = hi - lo;
-      s[4] = home[r] + (lo - rbase[r]);
-      ++sid;
-      const int32_t slot = p - last_le(piece_start, npieces, rbase[r]);
-      if (slot < S) ws.replica[r * S + slot] = e;
-      else atomicOr(s_flags, kFlagSlotBudget);
+  if (w == 0) {
+    const int32_t ns = wave_exclusive_scan(nseg, npieces);
+    if ((tid & 63) == 0) {
+      s_small[1] = ns;
+      *ws.n_segments = ns;
     }
   }
+  __syncthreads();
+  const int32_t nsegs = s_small[1];
+
+  for (int p = tid; p < npieces; p += nt) {
+    const int32_t e = piece_e[p];
+    ws.seg_first[e] = nseg[p];
+    ws.seg_count[e] = (p + 1 < npieces ? nseg[p + 1] : nsegs) - nseg[p];
+  }
+  // one thread per segment: its piece, its receiver, its rows and its slot
+  for (int sid = tid; sid < nsegs; sid += nt) {
+    const int32_t p = last_le(nseg, npieces, sid);
+    const int32_t e = piece_e[p], a0 = piece_start[p], b0 = a0 + shed[e];
+    const int32_t r = recv_rank[rord[last_le(rbase, R, a0)] + (sid - nseg[p])];
+    const int32_t lo = a0 > rbase[r] ? a0 : rbase[r];
+    const int32_t hi = b0 < rbase[r] + D[r] ? b0 : rbase[r] + D[r];
+    int32_t *sg = ws.segments + (int64_t)sid * 5;
+    sg[0] = e;
+    sg[1] = r;
+    sg[2] = (cnt[e] - shed[e]) + (lo - a0);
+    sg[3] = hi - lo;
+    sg[4] = home[r] + (lo - rbase[r]);
+    const int32_t slot = p - last_le(piece_start, npieces, rbase[r]);
+    if (slot < S) ws.replica[r * S + slot] = e;
+    else atomicOr(s_flags, kFlagSlotBudget);
+  }
+}
+
+// LDS of the layout kernel, in int32 words: region A holds the per-wave
+// counters while ranking and the planner's tables afterwards; then the
+// counts [E] and offsets [E+1].
+__host__ __device__ inline int32_t plan_region_a(int32_t E, int32_t R) {
+  const int32_t waves = (kTileWaves * E + 1) / 2;            // uint16 counters
+  const int32_t planner = R > 0 ? 5 * E + 8 * R + 8 : 0;
+  return waves > planner ? waves : planner;
 }
 
 __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
@@ -246,7 +257,11 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   const Workspace &ws = a.ws;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int32_t E = g.E;
-  uint16_t *wcnt = reinterpret_cast<uint16_t *>(lds);  // [waves][E], <= 256 each
+  const bool single = gridDim.x == 1;
+  uint16_t *wcnt = reinterpret_cast<uint16_t *>(lds);   // [waves][E], <= 256 each
+  int32_t *pl = lds;                                     // planner tables (after ranking)
+  int32_t *cnt = lds + plan_region_a(E, g.layout == kStatic ? g.R : 0);   // [E]
+  int32_t *offs = cnt + E;                               // [E+1]
 
   for (int i = tid; i < kTileWaves * E; i += kTileThreads) wcnt[i] = 0;
   if (tid == 0) s_flags = 0;
@@ -256,14 +271,19 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   int32_t ev[kTileChunks], rr[kTileChunks];
   uint32_t flags = 0;
 #pragma unroll
+  for (int c = 0; c < kTileChunks; ++c) {   // all loads in flight before any ranking
+    const int64_t f = wbase + c * 64 + lane;
+    ev[c] = f < g.n ? a.idx[f] : -1;
+  }
+#pragma unroll
   for (int c = 0; c < kTileChunks; ++c) {
     const int64_t f = wbase + c * 64 + lane;
     int32_t e = -1;
     if (f < g.n) {
-      const int32_t raw = a.idx[f];
+      const int32_t raw = ev[c];
       if (raw >= 0 && raw < E) e = raw;
       else if (raw != -1) flags |= kFlagIndexRange;
-      ws.eidx[f] = e;
+      if (!single) ws.eidx[f] = e;
     }
     const bool valid = e >= 0;
     uint64_t peers = __ballot(valid);
@@ -284,13 +304,17 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   __syncthreads();
 
   for (int e = tid; e < E; e += kTileThreads) {
+    int32_t v[kTileWaves];
+#pragma unroll
+    for (int ww = 0; ww < kTileWaves; ++ww) v[ww] = wcnt[ww * E + e];
     int32_t run = 0;
+#pragma unroll
     for (int ww = 0; ww < kTileWaves; ++ww) {
-      const int32_t v = wcnt[ww * E + e];
       wcnt[ww * E + e] = (uint16_t)run;
-      run += v;
+      run += v[ww];
     }
-    ws.tile_hist[(int64_t)blockIdx.x * E + e] = run;
+    if (single) cnt[e] = run;                              // the tile is the whole layout
+    else ws.tile_hist[(int64_t)blockIdx.x * E + e] = run;
   }
   if (flags) atomicOr(&s_flags, flags);
   __syncthreads();
@@ -298,22 +322,18 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   for (int c = 0; c < kTileChunks; ++c) {
     if (ev[c] >= 0) {
       rr[c] += wcnt[w * E + ev[c]];
-      if (gridDim.x > 1) ws.lrank[wbase + c * 64 + lane] = rr[c];
+      if (!single) ws.lrank[wbase + c * 64 + lane] = rr[c];
     }
   }
-  if (tid == 0) ws.tile_flags[blockIdx.x] = s_flags;
-  for (int64_t r = (int64_t)blockIdx.x * kTileThreads + tid; r < g.rows;
-       r += (int64_t)gridDim.x * kTileThreads)
-    ws.recv_src[r] = -1;
 
-  // Publish this tile; the last one to arrive finishes the layout.  The
-  // barrier waits for every wave's stores; then a single wave makes them
-  // visible to the other XCDs (agent-scope release: one L2 write-back per
-  // workgroup, not one per wave) and takes a ticket.  The last workgroup's
-  // agent-scope acquire (one invalidate) lets all its waves see every tile.
-  // A single tile is the whole layout and needs no handshake at all.
-  __syncthreads();
-  if (gridDim.x > 1) {
+  if (!single) {
+    // Publish this tile; the last one to arrive finishes the layout.  The
+    // barrier waits for every wave's stores; then a single wave makes them
+    // visible to the other XCDs (agent-scope release: one L2 write-back per
+    // workgroup, not one per wave) and takes a ticket.  The last workgroup's
+    // agent-scope acquire (one invalidate) lets all its waves see every tile.
+    if (tid == 0) ws.tile_flags[blockIdx.x] = s_flags;
+    __syncthreads();
     if (tid == 0) {
       __threadfence();
       const uint32_t t = atomicAdd(ws.ticket, 1u);
@@ -322,41 +342,43 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-  }
 
-  int32_t *cnt = lds;           // [E]
-  int32_t *offs = lds + E;      // [E+1]
-  int32_t *pl = lds + 2 * E + 1;
-  const int32_t ntiles = gridDim.x;
-  // Per-expert exclusive scan over the tiles.  The loads of 8 tiles are
-  // issued together so the scan costs ntiles/8 memory latencies, not ntiles.
-  for (int e = tid; e < E; e += kTileThreads) {
-    int32_t run = 0;
-    for (int32_t t0 = 0; t0 < ntiles; t0 += 8) {
-      int32_t v[8];
+    const int32_t ntiles = gridDim.x;
+    // Per-expert exclusive scan over the tiles.  The loads of 16 tiles are
+    // issued together so the scan costs ntiles/16 memory latencies, not ntiles.
+    for (int e = tid; e < E; e += kTileThreads) {
+      int32_t run = 0;
+      for (int32_t t0 = 0; t0 < ntiles; t0 += 16) {
+        int32_t v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = t0 + u < ntiles ? ws.tile_hist[(int64_t)(t0 + u) * E + e] : 0;
+        for (int u = 0; u < 16; ++u)
+          v[u] = t0 + u < ntiles ? ws.tile_hist[(int64_t)(t0 + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (t0 + u < ntiles) ws.tile_hist[(int64_t)(t0 + u) * E + e] = run;
-        run += v[u];
+        for (int u = 0; u < 16; ++u) {
+          if (t0 + u < ntiles) ws.tile_hist[(int64_t)(t0 + u) * E + e] = run;
+          run += v[u];
+        }
       }
+      cnt[e] = run;
     }
-    cnt[e] = run;
-    offs[e] = run;
-    ws.counts[e] = run;
+    for (int32_t t = tid; t < ntiles; t += kTileThreads) {
+      const uint32_t fl = ws.tile_flags[t];
+      if (fl) atomicOr(&s_flags, fl);
+    }
+    if (tid == 0) *ws.ticket = 0;
   }
-  for (int32_t t = tid; t < ntiles; t += kTileThreads) {
-    const uint32_t fl = ws.tile_flags[t];
-    if (fl) atomicOr(&s_flags, fl);
+  // From here on the layout lives in LDS; global results are written at the
+  // end, because every barrier waits for the wave's outstanding global
+  // stores as well as its loads.
+  __syncthreads();
+  for (int e = tid; e < E; e += kTileThreads) offs[e] = cnt[e];
+  __syncthreads();
+  if (w == 0) {
+    const int32_t tot = wave_exclusive_scan(offs, E);
+    if (lane == 0) offs[E] = tot;
   }
-  if (tid == 0 && ntiles > 1) *ws.ticket = 0;
   __syncthreads();
-  const int32_t total = block_exclusive_scan(offs, E, s_tmp);
-  if (tid == 0) offs[E] = total;
-  __syncthreads();
-  for (int e = tid; e <= E; e += kTileThreads) ws.offsets[e] = offs[e];
+  const int32_t total = offs[E];
   if (g.layout == kLL) {
     for (int e = tid; e < E; e += kTileThreads)
       if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
@@ -364,15 +386,20 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
     plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
   }
   __syncthreads();
+  for (int e = tid; e <= E; e += kTileThreads) {
+    ws.offsets[e] = offs[e];
+    if (e < E) ws.counts[e] = cnt[e];
+  }
   if (tid == 0) *ws.status = s_flags;
 
-  if (ntiles == 1) {
+  if (single) {
 #pragma unroll
     for (int c = 0; c < kTileChunks; ++c) {
       const int64_t f = wbase + c * 64 + lane;
       if (f < g.n) {
         int32_t d = ev[c] >= 0 ? entry_dst(g, ws, offs, ev[c], rr[c]) : -1;
         if (d >= g.rows) d = -1;
+        ws.eidx[f] = ev[c];
         ws.dst[f] = d;
         if (d >= 0) ws.recv_src[d] = (int32_t)f;
       }
@@ -380,28 +407,28 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   }
 }
 
+// Several tiles: one thread per entry (destination from its tile base and
+// tile rank).
 __global__ __launch_bounds__(256) void k_plan_dst(PlanArgs a) {
   const Geometry &g = a.g;
   const Workspace &ws = a.ws;
-  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (f >= g.n) return;
-  const int32_t e = ws.eidx[f];
-  int32_t d = -1;
-  if (e >= 0) {
-    const int64_t tile = f / kTileEntries;
-    const int32_t pos = ws.tile_hist[tile * g.E + e] + ws.lrank[f];
-    d = entry_dst(g, ws, ws.offsets, e, pos);
-    if (d >= g.rows) d = -1;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < g.n) {
+    const int32_t e = ws.eidx[i];
+    int32_t d = -1;
+    if (e >= 0) {
+      const int64_t tile = i / kTileEntries;
+      const int32_t pos = ws.tile_hist[tile * g.E + e] + ws.lrank[i];
+      d = entry_dst(g, ws, ws.offsets, e, pos);
+      if (d >= g.rows) d = -1;
+    }
+    ws.dst[i] = d;
+    if (d >= 0) ws.recv_src[d] = (int32_t)i;
   }
-  ws.dst[f] = d;
-  if (d >= 0) ws.recv_src[d] = (int32_t)f;
 }
 
 size_t plan_lds_bytes(int32_t E, int32_t R) {
-  const size_t tiles = (size_t)kTileWaves * E * sizeof(uint16_t);
-  const size_t fin = (size_t)(2 * E + 1) * sizeof(int32_t) +
-                     (R > 0 ? (size_t)(5 * E + 7 * R + 8) * sizeof(int32_t) : 0);
-  return tiles > fin ? tiles : fin;
+  return (size_t)(plan_region_a(E, R) + 2 * E + 1) * sizeof(int32_t);
 }
 
 hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,

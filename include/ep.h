@@ -134,7 +134,10 @@ typedef struct ep_handle_view {
   int32_t *counts;         /* [E]   entries routed to each expert (ep_plan) */
   int32_t *offsets;        /* [E+1] exclusive prefix sum of counts; offsets[E] = total */
   int32_t *dst;            /* [T*k] receive row of entry t*k+j, -1 if skipped/dropped */
-  int32_t *recv_src;       /* [recv_rows] entry t*k+j held by each row, -1 if none */
+  int32_t *recv_src;       /* [recv_rows] entry t*k+j held by each row; written only
+                              for rows that hold one: HT rows < offsets[E], LL slots
+                              < min(counts[e], capacity) of expert e, STATIC rows
+                              < load[r] of rank r.  Other rows are left unchanged. */
   uint32_t *status;        /* [1]   EP_FLAG_* bits of the last ep_plan (+ dup reduce) */
   /* STATIC only (NULL otherwise): */
   int32_t *keep;           /* [E] rows of e kept on its home rank */
@@ -180,7 +183,8 @@ ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
 
 /* Layout (and, for EP_LAYOUT_STATIC, the static-shape plan) of one pass.
  * topk_idx: int32 [T, k], tag EP_TAG_TOPK_IDX.  Writes counts, offsets,
- * dst, recv_src and the status word; STATIC also writes the plan tables.
+ * dst, recv_src (rows that hold an entry) and the status word; STATIC also
+ * writes the plan tables.
  * Rows inside one expert keep the order of the flat entry index t*k + j.
  * HT:     dst = offsets[e] + position of the entry among e's entries.
  * LL:     dst = e*capacity + position; entries past capacity are dropped
@@ -192,7 +196,7 @@ ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
  *         rows; each short rank numbers the distinct experts it receives as
  *         replica slots 0, 1, ... (more than S sets EP_FLAG_SLOT_BUDGET).
  * Entries equal to -1 are skipped; other ids outside [0, E) are skipped and
- * set EP_FLAG_INDEX_RANGE.  Enqueues one kernel if T*k <= 4096, else two.
+ * set EP_FLAG_INDEX_RANGE.  Enqueues one kernel if T*k <= 2048, else two.
  * Re-planning a handle invalidates the layout every earlier output used. */
 ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream);
 

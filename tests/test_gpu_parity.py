@@ -1,5 +1,5 @@
 """GPU parity of every step of the path against the CPU oracle, at sizes the
-oracle finishes in seconds that still span several layout tiles (4096
+oracle finishes in seconds that still span several layout tiles (2048
 entries each) and a ragged tail, plus edge cases: empty batch, single entry,
 masked / out-of-range / duplicate expert ids, LL capacity overflow, replica
 slot overflow, k outside the specialised set, the largest E.
@@ -52,6 +52,8 @@ CASES = [
     ("single", 1, 8, 1, 1, "ht", 0, 1, 0, 0.0, 0.0, 0.0, 0.0, 12),
     ("k1_ll", 513, 24, 5, 1, "ll", 200, 5, 0, 0.0, 0.0, 0.0, 0.5, 13),
     ("exact_tile", 512, 32, 256, 8, "static", 0, 32, 8, 0.0, 0.0, 0.0, 1.1, 14),
+    ("one_full_tile", 256, 40, 64, 8, "ht", 0, 8, 0, 0.0, 0.0, 0.0, 1.0, 15),
+    ("ll_multi_tile_masked", 700, 48, 96, 8, "ll", 90, 8, 0, 0.08, 0.01, 0.0, 1.3, 16),
 ]
 
 
