@@ -71,6 +71,7 @@ def _L():
             "orc_combine": (None, [i32, i32, i32, P, P, P, i32, P]),
             "orc_combine_bwd": (None, [i32, i32, i32, P, P, P, P, P, P]),
             "orc_dup_reduce": (None, [i32, i64, P, P, i32, P]),
+            "orc_route": (None, [i32, i32, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -292,3 +293,14 @@ def dup_reduce(rep_bits: np.ndarray, rep_e: np.ndarray, owner: np.ndarray) -> np
     E = own.shape[0]
     _L().orc_dup_reduce(n, P, _p(rep), _p(re), E, _p(own))
     return own
+
+
+def route(logits: np.ndarray, k: int):
+    """Top-k experts per token (descending logit, ties to the lower id) and the
+    softmax over the chosen logits.  Returns (topk_idx int32 [T,k], w fp32 [T,k])."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    _L().orc_route(T, E, k, _p(lg), _p(idx), _p(w))
+    return idx, w

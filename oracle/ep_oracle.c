@@ -573,3 +573,49 @@ void orc_dup_reduce(int32_t n, int64_t P, const uint16_t *rep, const int32_t *re
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* top-k routing                                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [UL-MoE] sections 2.1 and 3.1: the gate's scores pick a few experts per
+ * token (top-k); section 3.2 names a fused top-k + routing operator.  The
+ * NCCL EP listing's Table IV takes the chosen indices and weights as inputs.
+ * READING: experts in descending logit order, equal logits to the lower
+ * expert id, choice j = 0 the largest; weights are the softmax over the k
+ * chosen logits.  With fewer than k experts the extra choices are -1 with
+ * weight 0.  Logits must be finite.
+ * Selection: k rounds, each taking the largest logit not yet taken (first
+ * index wins a tie).  Softmax in double, rounded once to fp32.
+ */
+void orc_route(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *idx, float *w) {
+  int64_t t;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    const float *l = logits + t * E;
+    char *taken = (char *)calloc((size_t)(E > 0 ? E : 1), 1);
+    double z[64];
+    int32_t n = 0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      idx[t * k + j] = best;
+      if (best >= 0) {
+        taken[best] = 1;
+        ++n;
+      }
+    }
+    double m = n > 0 ? (double)l[idx[t * k]] : 0.0;
+    double sum = 0.0;
+    for (int32_t j = 0; j < n; ++j) {
+      z[j] = exp((double)l[idx[t * k + j]] - m);
+      sum += z[j];
+    }
+    for (int32_t j = 0; j < k; ++j) w[t * k + j] = j < n ? (float)(z[j] / sum) : 0.0f;
+    free(taken);
+  }
+}

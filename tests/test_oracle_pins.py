@@ -538,3 +538,41 @@ def test_dup_reduce_rounds_once():
     r = workloads.f32_to_bf16_bits(np.full((2, 8), 2.0 ** -24, np.float32))
     got = oracle.dup_reduce(r, np.array([0, 0], np.int32), owner)
     assert np.all(got == np.float32(1 + 2.0 ** -23))
+
+
+# ---------------------------------------------------------------------------
+# top-k routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["A", "B", "C"])
+def test_route_golden(case):
+    g = read_golden("route_small.txt")[case]
+    E, k = int(g["E"][0]), int(g["k"][0])
+    lg = floats(g["logits"]).astype(np.float32).reshape(1, E)
+    idx, w = oracle.route(lg, k)
+    assert idx.ravel().tolist() == ints(g["idx"]).tolist()
+    assert np.allclose(w.ravel(), floats(g["w"]), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("T,E,k,std", [(300, 256, 8, 1.0), (200, 384, 8, 1.5), (64, 8, 2, 1.0),
+                                       (50, 1024, 16, 1.0), (40, 5, 5, 1.0)])
+def test_route_matches_numpy(T, E, k, std):
+    rng = np.random.default_rng(T + E)
+    lg = (rng.standard_normal((T, E)) * std).astype(np.float32)
+    lg[:, E // 2] = lg[:, 0]                     # exact ties in every row
+    idx, w = oracle.route(lg, k)
+    want = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    assert np.array_equal(idx, want)
+    ch = np.take_along_axis(lg, want, axis=1).astype(np.float64)
+    z = np.exp(ch - ch.max(axis=1, keepdims=True))
+    ref = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    assert np.array_equal(w, ref) or np.max(np.abs(w - ref) / ref) < 2.0 ** -23
+    assert np.allclose(w.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_route_feeds_the_workload_inputs():
+    # the routing the workloads use to draw topk_idx / topk_w is the same rule
+    inp = workloads.make_inputs("training", T=512)
+    idx, w = oracle.route(inp.logits, inp.cfg.k)
+    assert np.array_equal(idx, inp.topk_idx)
+    assert np.max(np.abs(w - inp.topk_w)) <= 2.0 ** -23
