@@ -40,6 +40,8 @@ def parse():
                    choices=["prefill", "decode", "tiny", "sweep", "training"])
     p.add_argument("--rho", type=float, default=8.0, help="sweep: max/mean expert load")
     p.add_argument("--fp8", action="store_true", help="decode: FP8 e4m3 dispatch")
+    p.add_argument("--route", action="store_true",
+                   help="start the step from router logits (ep_route before ep_plan)")
     p.add_argument("--cold", action="store_true",
                    help="write a 512 MB buffer before every step (Infinity Cache flushed); "
                         "steps are then timed one by one")
@@ -56,6 +58,7 @@ def algorithmic_bytes(c, fp8=False):
     N = c.T * c.k
     row = c.H * 2
     b = {
+        "route": c.T * c.E * 4 + N * 8,                          # logits read, idx + weights written
         "plan": N * 4 + N * 4,                                   # topk_idx read, dst written
         "dispatch": c.T * row + N * (c.H + c.H // 128 * 4 if fp8 else row) + N * 4,
         "combine": N * row + N * 4 + N * 4 + c.T * row,          # rows, dst, w read; y written
@@ -184,6 +187,10 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if a.cold else None
 
     ops = []
+    if a.route:   # the pass starts from router logits: plan and combine use the routed outputs
+        logits = torch.from_numpy(inp.logits).to(dev)
+        idx, w = torch.empty_like(idx), torch.empty_like(w)
+        ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, stream)))
     ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, stream)))
     if a.fp8:
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
@@ -280,7 +287,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
-                   "step": " -> ".join(nm for nm, _ in ops)},
+                   "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route},
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": chain_bytes,

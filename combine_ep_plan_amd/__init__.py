@@ -26,7 +26,7 @@ __all__ = [
     "FLAG_SLOT_BUDGET", "Group", "Handle", "Buffer", "library_path", "load_library",
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
-    "ep_handle_status", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
+    "ep_handle_status", "ep_route", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce",
 ]
 
@@ -37,6 +37,7 @@ LAYOUT_LL, LAYOUT_HT, LAYOUT_STATIC = 0, 1, 2
 _LAYOUTS = {"ll": LAYOUT_LL, "ht": LAYOUT_HT, "static": LAYOUT_STATIC}
 FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET = 1, 2, 4
 TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0, 1, 2, 3, 4
+TAG_ROUTER_LOGITS = 5
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
 _STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
            "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",
@@ -99,6 +100,7 @@ def load_library():
         "ep_handle_destroy": (S, [c_void_p]),
         "ep_handle_query": (S, [c_void_p, POINTER(ep_handle_view_t)]),
         "ep_handle_status": (S, [c_void_p, c_void_p, POINTER(c_uint32)]),
+        "ep_route": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_plan": (S, [c_void_p, _T, c_void_p]),
         "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
@@ -203,6 +205,14 @@ def ep_handle_status(h: int, stream=None) -> int:
     return out.value
 
 
+def ep_route(h: int, logits: torch.Tensor, topk_idx: torch.Tensor,
+             topk_weights: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_route(c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
+                                   _tensor(topk_idx, TAG_TOPK_IDX),
+                                   _tensor(topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)),
+           "ep_route")
+
+
 def ep_plan(h: int, topk_idx: torch.Tensor, stream=None) -> None:
     _check(load_library().ep_plan(c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _stream(stream)),
            "ep_plan")
@@ -301,6 +311,14 @@ class Handle:
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.ptr = ep_handle_create(group.ptr, num_tokens, self.workspace.data_ptr(), nbytes)
         self._view = ep_handle_query(self.ptr)
+
+    def route(self, logits: torch.Tensor, stream=None):
+        """Top-k routing of this pass: returns (topk_idx int32 [T,k], weights fp32 [T,k])."""
+        k = self.group.top_k
+        idx = torch.empty((self.num_tokens, k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((self.num_tokens, k), dtype=torch.float32, device=logits.device)
+        ep_route(self.ptr, logits, idx, w, stream)
+        return idx, w
 
     def plan(self, topk_idx: torch.Tensor, stream=None) -> "Handle":
         ep_plan(self.ptr, topk_idx, stream)

@@ -256,6 +256,25 @@ ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags) {
   return EP_OK;
 }
 
+ep_status_t ep_route(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk_idx,
+                     ep_tensor_t *topk_weights, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(logits, EP_TAG_ROUTER_LOGITS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(logits, g.T, g.E)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(topk_idx, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_idx, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  return hip_status(epk::launch_route(static_cast<const float *>(logits->data), g.T, g.E, g.k,
+                                      static_cast<int32_t *>(topk_idx->data),
+                                      static_cast<float *>(topk_weights->data),
+                                      as_stream(stream)));
+}
+
 ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream) {
   if (!h) return EP_ERR_INVALID_ARG;
   const epk::Geometry &g = h->geo;

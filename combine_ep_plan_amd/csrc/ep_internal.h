@@ -70,6 +70,8 @@ hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t
 hipError_t launch_combine_bwd(const Geometry &g, const Workspace &ws, const uint16_t *gy,
                               const uint16_t *expert_out, int32_t H, const float *topk_w,
                               uint16_t *grad_out, float *grad_w, hipStream_t s);
+hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx,
+                        float *w, hipStream_t s);
 hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
                              int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
 

@@ -71,14 +71,16 @@ typedef enum ep_status {
 #define EP_FLAG_CAPACITY 2u     /* LL: an expert got more than `capacity` entries; extra dropped */
 #define EP_FLAG_SLOT_BUDGET 4u  /* STATIC: a rank needs more replica slots than slots_per_rank */
 
-/* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS is
- * this library's addition for the duplicated-expert gradient reduce. */
+/* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS and
+ * EP_TAG_ROUTER_LOGITS are this library's additions for the duplicated-expert
+ * gradient reduce and the routing step. */
 typedef enum ep_tensor_tag {
   EP_TAG_TOKENS = 0,        /* token rows: dispatch in/out, combine in/out, their grads */
   EP_TAG_TOPK_IDX = 1,      /* expert ids (int32); -1 = no expert */
   EP_TAG_TOPK_WEIGHTS = 2,  /* router weights (fp32) and their gradients */
   EP_TAG_FP8_SCALES = 3,    /* one fp32 scale per 128 channels of an FP8 row */
-  EP_TAG_EXPERT_GRADS = 4   /* expert parameter gradients */
+  EP_TAG_EXPERT_GRADS = 4,  /* expert parameter gradients */
+  EP_TAG_ROUTER_LOGITS = 5  /* router scores per token and expert (fp32) */
 } ep_tensor_tag_t;
 
 typedef enum ep_dtype {
@@ -180,6 +182,20 @@ ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *view);
 /* Wait for `stream`, then return the status word's EP_FLAG_* bits in *flags.
  * The only blocking call of the library; meant for tests and error checks. */
 ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
+
+/* Top-k routing, the gate step before ep_plan ("Ultra-Large MoE Models"
+ * article, sections 2.1 and 3.1-3.2: top-k selection over the gate scores,
+ * a fused top-k + routing operator).  For every token: the k experts with the
+ * largest logits, in descending order (equal logits: lower expert id first;
+ * choice 0 is the largest), and weights = softmax over those k logits (fp32,
+ * they sum to 1).  With fewer than k experts (E < k) the extra choices are
+ * -1 with weight 0.  Logits must be finite.
+ * logits:       fp32 [T, E], tag ROUTER_LOGITS.
+ * topk_idx:     int32 [T, k] output, tag TOPK_IDX (the input of ep_plan).
+ * topk_weights: fp32 [T, k] output, tag TOPK_WEIGHTS.
+ * Needs no ep_plan; T, E and k are the handle's. */
+ep_status_t ep_route(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk_idx,
+                     ep_tensor_t *topk_weights, void *stream);
 
 /* Layout (and, for EP_LAYOUT_STATIC, the static-shape plan) of one pass.
  * topk_idx: int32 [T, k], tag EP_TAG_TOPK_IDX.  Writes counts, offsets,

@@ -243,3 +243,20 @@ def test_dup_reduce_argument_validation(lib):
     assert R(h, T(BF16, ep.TAG_EXPERT_GRADS, 8, 64, 16), None, own, None) == 5   # not planned
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
+
+
+def test_route_argument_validation(lib):
+    g, h, _ = make_handle(lib)
+    lg = T(F32, ep.TAG_ROUTER_LOGITS, 64, 8)
+    idx = T(I32, ep.TAG_TOPK_IDX, 64, 2)
+    w = T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2)
+    Rt = lib.ep_route
+    assert Rt(h, T(F32, ep.TAG_TOKENS, 64, 8), idx, w, None) == 2
+    assert Rt(h, T(BF16, ep.TAG_ROUTER_LOGITS, 64, 8), idx, w, None) == 3
+    assert Rt(h, T(F32, ep.TAG_ROUTER_LOGITS, 64, 9), idx, w, None) == 4
+    assert Rt(h, lg, T(I32, ep.TAG_TOPK_IDX, 64, 3), w, None) == 4
+    assert Rt(h, lg, idx, T(F32, ep.TAG_TOPK_IDX, 64, 2), None) == 2
+    assert Rt(h, lg, idx, None, None) == 1
+    assert Rt(None, lg, idx, w, None) == 1
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)

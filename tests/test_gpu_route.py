@@ -1,0 +1,101 @@
+"""GPU parity of top-k routing (router logits -> top-k experts and the
+softmax over the chosen logits) with the oracle: indices bit-exact (the
+selection compares fp32 logits exactly on both sides, equal logits go to
+the lower expert id), weights within 1e-5 relative (fp32 exp and division
+against the oracle's double).  Also the whole pass from logits: route ->
+plan -> dispatch -> combine with identity experts returns x."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_plan_amd as ep
+import oracle
+import workloads
+from tests.gpu_util import dev_bf16, dev_f32, host, host_bits, make_group, same_up_to_zero_sign_np
+
+pytestmark = pytest.mark.gpu
+W_TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.load_library()
+    oracle.build(force=False)
+
+
+def _route_gpu(lg: np.ndarray, k: int, R: int = 1):
+    T, E = lg.shape
+    g = make_group(E, R, 8, k, T, "ht")
+    h = ep.Handle(g, T)
+    idx, w = h.route(dev_f32(lg))
+    torch.cuda.synchronize()
+    return host(idx), host(w)
+
+
+def _check(lg, k):
+    gi, gw = _route_gpu(lg, k)
+    ri, rw = oracle.route(lg, k)
+    assert np.array_equal(gi, ri)
+    m = ri >= 0
+    assert np.all(gw[~m] == 0)
+    assert np.all(np.abs(gw[m] - rw[m]) <= W_TOL * rw[m] + 1e-30)
+
+
+@pytest.mark.parametrize("name,rho", [("tiny", 1.0), ("decode", 1.0), ("prefill", 1.0),
+                                      ("sweep", 8.0), ("training", 1.0)])
+def test_route_workloads(name, rho):
+    inp = workloads.make_inputs(name, rho=rho) if name == "sweep" else workloads.make_inputs(name)
+    print(f"[route] {name} T={inp.cfg.T} E={inp.cfg.E} k={inp.cfg.k}", flush=True)
+    _check(inp.logits, inp.cfg.k)
+    gi, _ = _route_gpu(inp.logits, inp.cfg.k)
+    assert np.array_equal(gi, inp.topk_idx)          # the routing the workloads were drawn with
+
+
+@pytest.mark.parametrize("T,E,k", [(777, 1024, 16), (300, 384, 8), (129, 65, 3), (50, 5, 7),
+                                   (33, 1, 1), (0, 16, 4), (1000, 64, 1)])
+def test_route_shapes_and_ties(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if T and E > 3:
+        lg[:, E - 1] = lg[:, 0]                          # exact ties across lanes
+        lg[: T // 2, 1:4] = 2.5                          # exact ties inside the top-k
+        lg[T // 2:, :] = np.round(lg[T // 2:, :])        # many ties
+    _check(lg, k)
+
+
+def test_route_then_the_whole_pass():
+    inp = workloads.make_inputs("prefill")
+    c = inp.cfg
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht")
+    h = ep.Handle(g, c.T)
+    buf = ep.Buffer(g)
+    idx, w = h.route(dev_f32(inp.logits))
+    h.plan(idx)
+    x = dev_bf16(inp.x)
+    recv, _, _, _, _ = buf.dispatch(x, idx, w, handle=h, recv_meta=False)
+    y = buf.combine(recv, h, w)
+    assert same_up_to_zero_sign_np(host_bits(y), inp.x)
+    assert h.status() == 0
+
+
+def test_route_signed_zero_and_infinities():
+    # -0 and +0 compare equal (the lower expert id first); -inf logits are
+    # chosen only when nothing larger is left and get weight exp(-inf) = 0.
+    T, E, k = 96, 48, 6
+    lg = np.zeros((T, E), np.float32)
+    lg[:, ::2] = -0.0
+    lg[::3, 5] = 1.0
+    lg[1::3, 7:20] = -np.inf
+    lg[2::3, 3:] = -np.inf
+    _check(lg, k)
+    big = np.zeros((8, E), np.float32)
+    big[:, 9] = np.inf
+    big[:, 30] = -0.0
+    gi, _ = _route_gpu(big, k)
+    ri, _ = oracle.route(big, k)
+    assert np.array_equal(gi, ri)
