@@ -28,6 +28,8 @@ FLAG_CAPACITY = 2
 FLAG_SLOT_BUDGET = 4
 
 LAYOUT_CODE = {"ll": 0, "ht": 1, "static": 2}
+SLOTS_TRAINING = 0     # a rank needing more than S slots raises SLOT_BUDGET
+SLOTS_INFERENCE = 1    # segments past the S-th slot read the owner directly
 
 
 def build(force: bool = True) -> str:
@@ -62,7 +64,8 @@ def _L():
             "orc_e4m3_to_double": (ctypes.c_double, [ctypes.c_uint8]),
             "orc_layout": (u32, [i32, i32, i32, P, P, P, P]),
             "orc_dst_ht_ll": (u32, [i32, i32, i32, i32, P, P, P, P]),
-            "orc_plan": (i32, [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]),
+            "orc_plan": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]),
+            "orc_prefetch": (i32, [i32, i32, i32, i64, P, P, P]),
             "orc_dst_static": (None, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]),
             "orc_dispatch": (None, [i32, i32, i32, P, P, P]),
             "orc_recv_meta": (None, [i32, i32, i64, P, P, P, P, P, P]),
@@ -146,6 +149,7 @@ class Plan:
     segments: np.ndarray   # [n_seg, 5]: expert, rank, pos_begin, len, row_begin
     load: np.ndarray       # [R]
     replica: np.ndarray    # [R, S]
+    seg_slot: np.ndarray   # [n_seg] slot of each segment on its rank, -1 if none
     flags: int
 
 
@@ -159,7 +163,7 @@ def layout_counts(topk_idx: np.ndarray, E: int):
     return counts, offsets, pos, int(flags)
 
 
-def plan(counts: np.ndarray, R: int, S: int, C: int) -> Plan:
+def plan(counts: np.ndarray, R: int, S: int, C: int, slot_mode: int = SLOTS_TRAINING) -> Plan:
     counts = _c(counts, np.int32)
     E = counts.shape[0]
     keep = np.zeros(E, np.int32)
@@ -170,14 +174,16 @@ def plan(counts: np.ndarray, R: int, S: int, C: int) -> Plan:
     n_seg = np.zeros(1, np.int32)
     load = np.zeros(R, np.int32)
     replica = np.zeros(R * S if S > 0 else 1, np.int32)
+    seg_slot = np.zeros(E + R, np.int32)
     flags = np.zeros(1, np.uint32)
-    rc = _L().orc_plan(E, R, S, C, _p(counts), _p(keep), _p(native_row), _p(seg_first),
-                       _p(seg_count), _p(seg), _p(n_seg), _p(load), _p(replica), _p(flags))
+    rc = _L().orc_plan(E, R, S, C, slot_mode, _p(counts), _p(keep), _p(native_row),
+                       _p(seg_first), _p(seg_count), _p(seg), _p(n_seg), _p(load), _p(replica),
+                       _p(seg_slot), _p(flags))
     if rc != 0:
         raise ValueError("orc_plan: inconsistent arguments")
     ns = int(n_seg[0])
     return Plan(C, keep, native_row, seg_first, seg_count, seg[: ns * 5].reshape(ns, 5).copy(),
-                load, replica[: R * S].reshape(R, S).copy(), int(flags[0]))
+                load, replica[: R * S].reshape(R, S).copy(), seg_slot[:ns].copy(), int(flags[0]))
 
 
 def static_rows_per_rank(T: int, k: int, R: int) -> int:
@@ -186,7 +192,7 @@ def static_rows_per_rank(T: int, k: int, R: int) -> int:
 
 
 def layout(topk_idx: np.ndarray, E: int, kind: str, cap: int = 0, R: int = 1,
-           S: int = 0) -> Layout:
+           S: int = 0, slot_mode: int = SLOTS_TRAINING) -> Layout:
     """Counts, offsets, positions and destination rows for layout ``kind``."""
     idx = _c(topk_idx, np.int32)
     T, k = idx.shape
@@ -199,7 +205,7 @@ def layout(topk_idx: np.ndarray, E: int, kind: str, cap: int = 0, R: int = 1,
         rows = T * k if kind == "ht" else E * cap
     elif kind == "static":
         C = static_rows_per_rank(T, k, R)
-        pl = plan(counts, R, S, C)
+        pl = plan(counts, R, S, C, slot_mode)
         flags |= pl.flags
         segflat = np.ascontiguousarray(pl.segments.reshape(-1)) if pl.segments.size else np.zeros(5, np.int32)
         _L().orc_dst_static(T, k, E, R, C, _p(idx), _p(pos), _p(pl.keep), _p(pl.native_row),
@@ -293,6 +299,24 @@ def dup_reduce(rep_bits: np.ndarray, rep_e: np.ndarray, owner: np.ndarray) -> np
     E = own.shape[0]
     _L().orc_dup_reduce(n, P, _p(rep), _p(re), E, _p(own))
     return own
+
+
+def prefetch(weights: np.ndarray, replica: np.ndarray, slots: np.ndarray) -> np.ndarray:
+    """Replica-weight prefetch: returns a copy of ``slots`` ([R, S, ...]) in
+    which every slot (r, s) with replica[r, s] = e >= 0 holds expert e's row
+    of ``weights`` ([E, ...], any dtype); empty slots keep their contents."""
+    w = np.ascontiguousarray(weights)
+    out = np.array(slots, copy=True, order="C")
+    rep = _c(replica, np.int32)
+    R, S = rep.shape
+    E = w.shape[0]
+    row_bytes = w[0].nbytes if E else 0
+    if out.dtype != w.dtype or out.shape[:2] != (R, S) or out.shape[2:] != w.shape[1:]:
+        raise ValueError("prefetch: slots must be [R, S] + weights.shape[1:] of the same dtype")
+    rc = _L().orc_prefetch(E, R, S, row_bytes, _p(rep), _p(w), _p(out))
+    if rc != 0:
+        raise ValueError("orc_prefetch: a slot names an expert outside [0, E)")
+    return out
 
 
 def route(logits: np.ndarray, k: int):

@@ -13,9 +13,10 @@
  *            paragraph 3 (predictable per-rank workload, GPU planner choosing
  *            redundant experts from the current router output), paragraph 4
  *            (rows go straight to expert-grouped positions, static shapes),
- *            paragraph 5 (prefetch slots bounded by E/R in training; a
- *            dedicated reduce buffer folds duplicated-expert gradients into
- *            the owner's gradients).
+ *            paragraph 5 (prefetch slots bounded by E/R in training, a
+ *            small fixed number in inference with overflow read from the
+ *            owner directly; a dedicated reduce buffer folds
+ *            duplicated-expert gradients into the owner's gradients).
  *   [NCCLEP] listing of the NCCL EP paper (arXiv 2603.13606): abstract
  *            (LL and HT modes), Table II (combine gathers expert outputs and
  *            reduces them to the original token order), Table III (LL: 3D
@@ -241,8 +242,13 @@ uint32_t orc_dst_ht_ll(int32_t T, int32_t k, int32_t layout, int32_t cap,
  *  6. a rank's rows are its own experts' kept rows in expert order, then the
  *     segments it received in sequence order;
  *  7. a receiver numbers the distinct experts it received 0, 1, ... in
- *     sequence order; these are its replica slots.  More than S slots
- *     raises SLOT_BUDGET (the plan is still complete).
+ *     sequence order; the first S of them get its replica slots.  A segment
+ *     past the S-th has no slot: in training mode (slot_mode 0) that raises
+ *     SLOT_BUDGET, since a training rank reserves slots for all of its
+ *     duplicates; in inference mode (slot_mode 1) it is the overflow case
+ *     of [MoonEP] paragraph 5 -- a small fixed number of slots, the rest
+ *     read from the owner's weights directly -- and raises nothing.  The
+ *     plan's rows are the same in both modes.
  *
  * Outputs (arrays sized by the caller):
  *   keep[E], native_row[E]     kept rows of e and their first row in home rank
@@ -251,15 +257,17 @@ uint32_t orc_dst_ht_ll(int32_t T, int32_t k, int32_t layout, int32_t cap,
  *   *n_seg                     number of segments
  *   load[R]                    rows used on each rank (= target)
  *   replica[R*S]               expert in each replica slot, -1 if empty
+ *   seg_slot[E+R]              slot of each segment on its rank, -1 if none
  *   *flags                     ORed with SLOT_BUDGET if a receiver needs > S
+ *                              in training mode
  * Returns 0, or -1 if the arguments are inconsistent (E % R != 0, C too small,
  * negative counts).
  */
-int32_t orc_plan(int32_t E, int32_t R, int32_t S, int32_t C, const int32_t *counts,
-                 int32_t *keep, int32_t *native_row, int32_t *seg_first,
-                 int32_t *seg_count, int32_t *seg, int32_t *n_seg, int32_t *load,
-                 int32_t *replica, uint32_t *flags) {
-  if (E <= 0 || R <= 0 || E % R != 0 || S < 0) return -1;
+int32_t orc_plan(int32_t E, int32_t R, int32_t S, int32_t C, int32_t slot_mode,
+                 const int32_t *counts, int32_t *keep, int32_t *native_row,
+                 int32_t *seg_first, int32_t *seg_count, int32_t *seg, int32_t *n_seg,
+                 int32_t *load, int32_t *replica, int32_t *seg_slot, uint32_t *flags) {
+  if (E <= 0 || R <= 0 || E % R != 0 || S < 0 || slot_mode < 0 || slot_mode > 1) return -1;
   int32_t m = E / R;
   int64_t N = 0;
   for (int32_t e = 0; e < E; ++e) {
@@ -350,8 +358,13 @@ int32_t orc_plan(int32_t E, int32_t R, int32_t S, int32_t C, const int32_t *coun
         seg[ns * 5 + 3] = (int32_t)(b - a);
         seg[ns * 5 + 4] = (int32_t)(home[r] + (a - d_lo));  /* row in rank r */
         /* step 7: replica slot on the receiver */
-        if (slots_used[r] < S) replica[r * S + slots_used[r]] = e;
-        else *flags |= ORC_FLAG_SLOT_BUDGET;
+        if (slots_used[r] < S) {
+          replica[r * S + slots_used[r]] = e;
+          seg_slot[ns] = slots_used[r];
+        } else {
+          seg_slot[ns] = -1;
+          if (slot_mode == 0) *flags |= ORC_FLAG_SLOT_BUDGET;
+        }
         slots_used[r] += 1;
         ++ns;
       }
@@ -365,6 +378,28 @@ int32_t orc_plan(int32_t E, int32_t R, int32_t S, int32_t C, const int32_t *coun
   free(slots_used);
   free(target); free(home); free(shed); free(order);
   free(pc_e); free(pc_start); free(pc_len);
+  return 0;
+}
+
+/*
+ * Replica-weight prefetch, [MoonEP] paragraphs 3 and 5: the planner picks
+ * redundant experts from the current routing and their weights are
+ * prefetched into dedicated slots of the receiving rank; the weights of
+ * each expert projection sit contiguously.  Definition: for every slot
+ * (r, s) with replica[r*S+s] = e >= 0, slot (r, s) becomes a byte copy of
+ * expert e's row of `weights`; empty slots are left as they are.
+ *   weights  [E][row_bytes]      each expert's projection, contiguous
+ *   slots    [R*S][row_bytes]    the ranks' prefetch slots
+ * Returns -1 if a slot names an expert outside [0, E), else 0.
+ */
+int32_t orc_prefetch(int32_t E, int32_t R, int32_t S, int64_t row_bytes,
+                     const int32_t *replica, const uint8_t *weights, uint8_t *slots) {
+  for (int64_t i = 0; i < (int64_t)R * S; ++i) {
+    const int32_t e = replica[i];
+    if (e < 0) continue;
+    if (e >= E) return -1;
+    for (int64_t b = 0; b < row_bytes; ++b) slots[i * row_bytes + b] = weights[(int64_t)e * row_bytes + b];
+  }
   return 0;
 }
 

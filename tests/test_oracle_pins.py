@@ -198,8 +198,16 @@ def test_planner_golden(case):
     assert p.segments.ravel().tolist() == ints(g["segments"]).tolist()
     assert p.load.tolist() == ints(g["load"]).tolist()
     assert p.replica.ravel().tolist() == ints(g["replica"]).tolist()
+    assert p.seg_slot.tolist() == ints(g["seg_slot"]).tolist()
     assert L.flags == int(g["flags"][0])
     assert L.dst.ravel().tolist() == ints(g["dst"]).tolist()
+    # inference slot mode: same rows and tables, overflow raises nothing
+    Li = oracle.layout(idx, E, "static", R=R, S=S, slot_mode=oracle.SLOTS_INFERENCE)
+    assert Li.flags == int(g["flags_inference"][0])
+    assert np.array_equal(Li.dst, L.dst)
+    assert np.array_equal(Li.plan.segments, p.segments)
+    assert np.array_equal(Li.plan.replica, p.replica)
+    assert np.array_equal(Li.plan.seg_slot, p.seg_slot)
 
 
 def check_plan_invariants(counts: np.ndarray, R: int, S: int, C: int, p: "oracle.Plan"):
@@ -244,6 +252,12 @@ def check_plan_invariants(counts: np.ndarray, R: int, S: int, C: int, p: "oracle
         row = p.replica[r]
         assert list(row[: min(S, len(exps))]) == exps[:S]
         assert np.all(row[min(S, len(exps)):] == -1)
+        # a segment's slot is its order among the rank's segments, none past S
+        slots = p.seg_slot[seg[:, 1] == r] if seg.size else np.zeros(0, np.int32)
+        assert slots.tolist() == [i if i < S else -1 for i in range(len(exps))]
+        for e, sl in zip(exps, slots):
+            if sl >= 0:
+                assert row[sl] == e
     if all(len(seg[seg[:, 1] == r]) <= S for r in range(R)) if seg.size else True:
         assert not (p.flags & oracle.FLAG_SLOT_BUDGET)
 
@@ -257,6 +271,22 @@ def test_planner_invariants_random(R, m, S, data):
     C = -(-N // R) + data.draw(st.integers(0, 3))
     p = oracle.plan(counts, R, S, C)
     check_plan_invariants(counts, R, S, C, p)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 8), st.integers(1, 6), st.integers(0, 3), st.data())
+def test_planner_inference_slot_mode_random(R, m, S, data):
+    # inference mode changes nothing but the SLOT_BUDGET flag, which it never raises
+    E = R * m
+    counts = np.array(data.draw(st.lists(st.integers(0, 40), min_size=E, max_size=E)), np.int32)
+    C = -(-int(counts.sum()) // R)
+    pt = oracle.plan(counts, R, S, C, oracle.SLOTS_TRAINING)
+    pi = oracle.plan(counts, R, S, C, oracle.SLOTS_INFERENCE)
+    for f in ("keep", "native_row", "seg_first", "seg_count", "segments", "load", "replica",
+              "seg_slot"):
+        assert np.array_equal(getattr(pt, f), getattr(pi, f)), f
+    assert pi.flags == 0
+    assert bool(pt.flags & oracle.FLAG_SLOT_BUDGET) == bool(np.any(pt.seg_slot < 0))
 
 
 def test_planner_uniform_reduces_to_ht():
@@ -287,7 +317,43 @@ def test_planner_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.plan(np.array([1, 2, 3], np.int32), 2, 1, 4)      # E % R != 0
     with pytest.raises(ValueError):
+        oracle.plan(np.array([1, 2], np.int32), 2, 1, 4, 2)      # no slot mode 2
+    with pytest.raises(ValueError):
         oracle.plan(np.array([5, 5], np.int32), 2, 1, 4)         # C < ceil(N/R)
+
+
+# ---------------------------------------------------------------------------
+# replica-weight prefetch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["A", "B"])
+def test_prefetch_golden(case):
+    g = read_golden("prefetch_small.txt")[case]
+    E, R, S = (int(g[x][0]) for x in ("E", "R", "S"))
+    w = ints(g["weights"]).astype(np.uint8).reshape(E, -1)
+    rep = ints(g["replica"]).astype(np.int32).reshape(R, S)
+    before = ints(g["slots_before"]).astype(np.uint8).reshape(R, S, -1)
+    out = oracle.prefetch(w, rep, before)
+    assert out.ravel().tolist() == ints(g["slots_after"]).tolist()
+
+
+def test_prefetch_follows_the_plan_of_case_c():
+    # planner case C (E=4, R=4, S=1): rank2 and rank3 each prefetch expert 0;
+    # bf16 rows of 3 elements, distinct per expert, are copied bit for bit
+    g = read_golden("planner_small.txt")["C"]
+    idx = ints(g["idx"]).reshape(4, 2).astype(np.int32)
+    L = oracle.layout(idx, 4, "static", R=4, S=1)
+    w = (np.arange(12, dtype=np.uint16) + 0x3F80).reshape(4, 3)
+    out = oracle.prefetch(w, L.plan.replica, np.full((4, 1, 3), 0xFFFF, np.uint16))
+    assert out[0, 0].tolist() == [0xFFFF] * 3 and out[1, 0].tolist() == [0xFFFF] * 3
+    assert out[2, 0].tolist() == [0x3F80, 0x3F81, 0x3F82]
+    assert out[3, 0].tolist() == [0x3F80, 0x3F81, 0x3F82]
+
+
+def test_prefetch_rejects_bad_expert():
+    with pytest.raises(ValueError):
+        oracle.prefetch(np.zeros((2, 4), np.uint8), np.array([[2]], np.int32),
+                        np.zeros((1, 1, 4), np.uint8))
 
 
 # ---------------------------------------------------------------------------
