@@ -42,6 +42,13 @@ def parse():
     p.add_argument("--fp8", action="store_true", help="decode: FP8 e4m3 dispatch")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
+    p.add_argument("--prefetch", action="store_true",
+                   help="STATIC workloads: add the replica-weight prefetch of one [4096, 1536] "
+                        "bf16 projection per expert after the plan")
+    p.add_argument("--slot-mode", choices=("training", "inference"), default="training",
+                   help="STATIC workloads: what the plan does past a rank's S-th replica slot")
+    p.add_argument("--slots", type=int, default=None,
+                   help="STATIC workloads: replica slots per rank (default: the workload's)")
     p.add_argument("--cold", action="store_true",
                    help="write a 512 MB buffer before every step (Infinity Cache flushed); "
                         "steps are then timed one by one")
@@ -52,7 +59,10 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(c, fp8=False):
+PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
+
+
+def algorithmic_bytes(c, fp8=False, filled_slots=0):
     """Bytes each kernel must move by definition: x read once, every routed row
     written once and read once, outputs written once, int32/fp32 metadata."""
     N = c.T * c.k
@@ -68,6 +78,7 @@ def algorithmic_bytes(c, fp8=False):
         b["dispatch_bwd"] = N * row + N * 4 + c.T * row
         P = 4096 * 1536
         b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
+    b["prefetch"] = filled_slots * PREFETCH_P * 2 * 2            # each filled slot: owner row read, slot written
     return b
 
 
@@ -163,7 +174,13 @@ def main():
     name = a.workload
     inp = workloads.make_inputs(name, 0, a.rho) if name == "sweep" else workloads.make_inputs(name)
     c = inp.cfg
-    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S)
+    S = c.S if a.slots is None else a.slots
+    if (a.prefetch or a.slots is not None or a.slot_mode != "training") and c.layout != "static":
+        print("bench.py: --prefetch, --slots and --slot-mode need a STATIC workload (sweep, training)",
+              file=sys.stderr)
+        sys.exit(2)
+    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=S,
+                 slot_mode=a.slot_mode)
     h = ep.Handle(g, c.T)
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(inp.topk_idx).to(dev)
@@ -192,6 +209,10 @@ def main():
         idx, w = torch.empty_like(idx), torch.empty_like(w)
         ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, stream)))
     ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, stream)))
+    if a.prefetch:
+        wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
+        slots = torch.empty((c.R, S, PREFETCH_P), dtype=torch.bfloat16, device=dev)
+        ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, stream)))
     if a.fp8:
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
         ep.ep_plan(h.ptr, idx, stream)
@@ -256,7 +277,8 @@ def main():
     per_us = {nm: 1000.0 * sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(K)) / K
               for i, (nm, _) in enumerate(ops)}
 
-    ab = algorithmic_bytes(c, a.fp8)
+    filled = int((h.tables()["replica"] >= 0).sum()) if c.layout == "static" and S > 0 else 0
+    ab = algorithmic_bytes(c, a.fp8, filled)
     chain_bytes = sum(ab[nm] for nm, _ in ops)
     step_s = step_ms / 1000.0
     dom = max((nm for nm in ("dispatch", "combine", "combine_bwd") if nm in per_us),
@@ -288,6 +310,7 @@ def main():
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route},
+        **({"prefetch": {"filled_slots": filled, "slot_bytes": PREFETCH_P * 2}} if a.prefetch else {}),
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": chain_bytes,

@@ -27,7 +27,7 @@ __all__ = [
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
-    "ep_dup_grad_reduce",
+    "ep_dup_grad_reduce", "ep_prefetch_replicas", "SLOTS_TRAINING", "SLOTS_INFERENCE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +37,9 @@ LAYOUT_LL, LAYOUT_HT, LAYOUT_STATIC = 0, 1, 2
 _LAYOUTS = {"ll": LAYOUT_LL, "ht": LAYOUT_HT, "static": LAYOUT_STATIC}
 FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET = 1, 2, 4
 TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0, 1, 2, 3, 4
-TAG_ROUTER_LOGITS = 5
+TAG_ROUTER_LOGITS, TAG_EXPERT_WEIGHTS = 5, 6
+SLOTS_TRAINING, SLOTS_INFERENCE = 0, 1
+_SLOT_MODES = {"training": SLOTS_TRAINING, "inference": SLOTS_INFERENCE}
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
 _STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
            "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",
@@ -59,7 +61,7 @@ class ep_tensor_t(ctypes.Structure):
 class ep_group_config_t(ctypes.Structure):
     _fields_ = [("num_experts", c_int32), ("num_ranks", c_int32), ("hidden", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
-                ("capacity", c_int32), ("slots_per_rank", c_int32)]
+                ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32)]
 
 
 class ep_handle_view_t(ctypes.Structure):
@@ -68,7 +70,7 @@ class ep_handle_view_t(ctypes.Structure):
                 ("max_segments", c_int32)] + [
         (n, c_void_p) for n in ("counts", "offsets", "dst", "recv_src", "status", "keep",
                                 "native_row", "seg_first", "seg_count", "segments",
-                                "n_segments", "load", "replica")]
+                                "n_segments", "load", "replica", "seg_slot")]
 
 
 _lib = None
@@ -106,6 +108,7 @@ def load_library():
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
+        "ep_prefetch_replicas": (S, [c_void_p, _T, _T, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -252,6 +255,13 @@ def ep_dup_grad_reduce(h: int, replica_grads: torch.Tensor, replica_expert: torc
         _tensor(owner_grads, TAG_EXPERT_GRADS), _stream(stream)), "ep_dup_grad_reduce")
 
 
+def ep_prefetch_replicas(h: int, expert_weights: torch.Tensor, slot_weights: torch.Tensor,
+                         stream=None) -> None:
+    _check(load_library().ep_prefetch_replicas(
+        c_void_p(h), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
+        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _stream(stream)), "ep_prefetch_replicas")
+
+
 # ---------------------------------------------------------------------------
 # group / handle / buffer objects
 # ---------------------------------------------------------------------------
@@ -261,10 +271,11 @@ class Group:
 
     def __init__(self, num_experts: int, num_ranks: int, hidden: int, top_k: int,
                  max_tokens: int, layout: str | int = "ht", capacity: int = 0,
-                 slots_per_rank: int = 0):
+                 slots_per_rank: int = 0, slot_mode: str | int = "training"):
         self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+        mode = _SLOT_MODES[slot_mode] if isinstance(slot_mode, str) else int(slot_mode)
         self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
-                                     self.layout, capacity, slots_per_rank)
+                                     self.layout, capacity, slots_per_rank, mode)
         self.ptr = ep_group_create(self.cfg)
 
     @property
@@ -360,6 +371,7 @@ class Handle:
                 "segments": self._ws(v.segments, 5 * v.max_segments).view(v.max_segments, 5),
                 "n_segments": self._ws(v.n_segments, 1), "load": self._ws(v.load, R),
                 "replica": self._ws(v.replica, R * S).view(R, S),
+                "seg_slot": self._ws(v.seg_slot, v.max_segments),
             })
         return out
 
@@ -423,6 +435,18 @@ class Buffer:
         grad_w = torch.empty_like(topk_weights)
         ep_combine_bwd(handle.ptr, grad_y, expert_out, topk_weights, grad_out, grad_w, stream)
         return grad_out, grad_w
+
+    def prefetch_replicas(self, expert_weights: torch.Tensor, handle: Handle,
+                          slots: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Copy the plan's replica experts' weights ([E, P...]) into their
+        prefetch slots ([R, S, P...]); slots the plan leaves empty keep their
+        contents (uninitialised if ``slots`` is None)."""
+        c = self.group.cfg
+        if slots is None:
+            slots = torch.empty((c.num_ranks, c.slots_per_rank) + tuple(expert_weights.shape[1:]),
+                                dtype=expert_weights.dtype, device=expert_weights.device)
+        ep_prefetch_replicas(handle.ptr, expert_weights, slots, stream)
+        return slots
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,
                         handle: Handle, replica_expert: torch.Tensor | None = None,

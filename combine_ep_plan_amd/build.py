@@ -22,7 +22,8 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           f"-I{INCLUDE}", f"-I{CSRC}"]
-SOURCES = ["route.hip", "plan.hip", "dispatch.hip", "combine.hip", "dup_reduce.hip", "ep_api.cpp"]
+SOURCES = ["route.hip", "plan.hip", "dispatch.hip", "combine.hip", "dup_reduce.hip", "prefetch.hip",
+           "ep_api.cpp"]
 
 
 def hipcc() -> str:

@@ -40,6 +40,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.E = c.num_experts;
   geo.R = c.num_ranks;
   geo.S = c.slots_per_rank;
+  geo.slot_mode = c.slot_mode;
   geo.layout = c.layout;
   geo.cap = c.capacity;
   geo.n = (int64_t)T * c.top_k;
@@ -122,6 +123,7 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
     w.n_segments = reinterpret_cast<int32_t *>(take(sizeof(int32_t)));
     w.load = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.R));
     w.replica = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)g.R * g.S));
+    w.seg_slot = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)(g.E + g.R)));
   }
   if (ws) *ws = w;
   return off;
@@ -160,7 +162,12 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
   if (c.layout == EP_LAYOUT_LL &&
       (c.capacity < 1 || (int64_t)c.capacity * c.num_experts > INT32_MAX))
     return EP_ERR_INVALID_ARG;
-  if (c.layout == EP_LAYOUT_STATIC && c.slots_per_rank < 0) return EP_ERR_INVALID_ARG;
+  if (c.layout == EP_LAYOUT_STATIC &&
+      (c.slots_per_rank < 0 || (int64_t)c.num_ranks * c.slots_per_rank > INT32_MAX))
+    return EP_ERR_INVALID_ARG;
+  if (c.slot_mode != EP_SLOTS_TRAINING &&
+      !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))
+    return EP_ERR_INVALID_ARG;
   const int32_t R = c.layout == EP_LAYOUT_STATIC ? c.num_ranks : 0;
   if (epk::plan_lds_bytes(c.num_experts, R) + 256 > (size_t)epk::kLdsLimit)
     return EP_ERR_UNSUPPORTED;
@@ -243,6 +250,7 @@ ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *v) {
   v->n_segments = h->ws.n_segments;
   v->load = h->ws.load;
   v->replica = h->ws.replica;
+  v->seg_slot = h->ws.seg_slot;
   return EP_OK;
 }
 
@@ -431,6 +439,42 @@ ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
   return hip_status(epk::launch_dup_reduce(
       static_cast<const uint16_t *>(replica_grads->data), rep_e, (int32_t)n, P, (int32_t)E_owner,
       static_cast<float *>(owner_grads->data), h->ws.status, as_stream(stream)));
+}
+
+ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weights,
+                                 ep_tensor_t *slot_weights, void *stream) {
+  if (!h || !expert_weights || !slot_weights) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  const int32_t dt = expert_weights->dtype;
+  if (dt != EP_DTYPE_BF16 && dt != EP_DTYPE_FP32 && dt != EP_DTYPE_FP8_E4M3)
+    return EP_ERR_BAD_DTYPE;
+  ep_status_t st = check_tensor(expert_weights, EP_TAG_EXPERT_WEIGHTS, dt);
+  if (st != EP_OK) return st;
+  st = check_tensor(slot_weights, EP_TAG_EXPERT_WEIGHTS, dt);
+  if (st != EP_OK) return st;
+  if (g.layout != EP_LAYOUT_STATIC) return EP_ERR_UNSUPPORTED;
+  // expert_weights [E, P...]; slot_weights [R, S, P...] or [R*S, P...]
+  const ep_tensor_t *w = expert_weights, *sl = slot_weights;
+  if (w->ndim < 2 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
+  int64_t P = 1;
+  for (int i = 1; i < w->ndim; ++i) P *= w->sizes[i];
+  const int tail = w->ndim - 1;  // dims of one row
+  if (sl->ndim == tail + 2) {
+    if (sl->sizes[0] != g.R || sl->sizes[1] != g.S) return EP_ERR_BAD_SHAPE;
+  } else if (sl->ndim == tail + 1) {
+    if (sl->sizes[0] != (int64_t)g.R * g.S) return EP_ERR_BAD_SHAPE;
+  } else {
+    return EP_ERR_BAD_SHAPE;
+  }
+  for (int i = 0; i < tail; ++i)
+    if (sl->sizes[sl->ndim - tail + i] != w->sizes[1 + i]) return EP_ERR_BAD_SHAPE;
+  const int64_t elem = dt == EP_DTYPE_FP32 ? 4 : dt == EP_DTYPE_BF16 ? 2 : 1;
+  const int64_t row_bytes = P * elem;
+  if (row_bytes % 16 != 0) return EP_ERR_BAD_SHAPE;
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return hip_status(epk::launch_prefetch(g, h->ws, static_cast<const uint8_t *>(w->data),
+                                         row_bytes, static_cast<uint8_t *>(sl->data),
+                                         as_stream(stream)));
 }
 
 }  // extern "C"

@@ -40,10 +40,12 @@ struct Workspace {
   int32_t *n_segments;   // [1]
   int32_t *load;         // [R]
   int32_t *replica;      // [R*S]
+  int32_t *seg_slot;     // [E+R] slot of each segment on its rank, -1 if none
 };
 
 struct Geometry {
   int32_t T, k, E, R, S, layout, cap;
+  int32_t slot_mode;  // 0 training (overflow flags SLOT_BUDGET), 1 inference
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
   int32_t nbits;    // bits of an expert id, >= 1
@@ -72,6 +74,8 @@ hipError_t launch_combine_bwd(const Geometry &g, const Workspace &ws, const uint
                               uint16_t *grad_out, float *grad_w, hipStream_t s);
 hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx,
                         float *w, hipStream_t s);
+hipError_t launch_prefetch(const Geometry &g, const Workspace &ws, const uint8_t *weights,
+                           int64_t row_bytes, uint8_t *slots, hipStream_t s);
 hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
                              int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
 

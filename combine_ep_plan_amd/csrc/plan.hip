@@ -93,7 +93,9 @@ __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace 
 //  the shed pieces (donor rank, then walk order) and the receivers' deficits
 //  (rank order) are laid end to end; each overlap is one segment, placed in
 //  the receiver behind its own rows; a receiver's replica slot of a segment
-//  is the segment's rank among the pieces that reach that receiver.
+//  is the segment's rank among the pieces that reach that receiver.  Past
+//  the S-th slot a segment has none: an error in training, the direct-read
+//  overflow in inference (MoonEP article, par. 5).
 // Every phase is parallel over ranks, experts, pieces or segments; the five
 // prefix sums are single-wave scans (four of them on four waves at once).
 __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_t *cnt,
@@ -234,8 +236,9 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     sg[3] = hi - lo;
     sg[4] = home[r] + (lo - rbase[r]);
     const int32_t slot = p - last_le(piece_start, npieces, rbase[r]);
+    ws.seg_slot[sid] = slot < S ? slot : -1;
     if (slot < S) ws.replica[r * S + slot] = e;
-    else atomicOr(s_flags, kFlagSlotBudget);
+    else if (g.slot_mode == 0) atomicOr(s_flags, kFlagSlotBudget);  // inference: direct read
   }
 }
 

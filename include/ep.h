@@ -19,9 +19,11 @@
  *   MoonEP article (Open Source For You), paragraphs 3-5: fixed per-rank
  *     workload from a GPU planner that picks redundant experts from the
  *     current routing; rows written straight to expert-grouped positions;
- *     static shapes, no per-layer host synchronisation; at most E/R replica
- *     slots per rank in training; duplicated-expert gradients folded into
- *     the owner's gradients through a reduce buffer.
+ *     static shapes, no per-layer host synchronisation; redundant experts'
+ *     weights prefetched into dedicated slots, at most E/R per rank in
+ *     training, a small fixed number in inference with the overflow read
+ *     from the owner directly; duplicated-expert gradients folded into the
+ *     owner's gradients through a reduce buffer.
  *
  * Conventions shared by every call
  *   Memory.     Every tensor is a non-owning view of caller-allocated device
@@ -69,18 +71,21 @@ typedef enum ep_status {
 /* Device-detected conditions (bits of the status word, see ep_handle_status). */
 #define EP_FLAG_INDEX_RANGE 1u  /* a top-k index outside [0, E) other than -1; entry skipped */
 #define EP_FLAG_CAPACITY 2u     /* LL: an expert got more than `capacity` entries; extra dropped */
-#define EP_FLAG_SLOT_BUDGET 4u  /* STATIC: a rank needs more replica slots than slots_per_rank */
+#define EP_FLAG_SLOT_BUDGET 4u  /* STATIC, training slot mode: a rank needs more replica slots
+                                   than slots_per_rank (the plan is still complete) */
 
-/* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS and
- * EP_TAG_ROUTER_LOGITS are this library's additions for the duplicated-expert
- * gradient reduce and the routing step. */
+/* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS,
+ * EP_TAG_ROUTER_LOGITS and EP_TAG_EXPERT_WEIGHTS are this library's additions
+ * for the duplicated-expert gradient reduce, the routing step and the
+ * replica-weight prefetch. */
 typedef enum ep_tensor_tag {
   EP_TAG_TOKENS = 0,        /* token rows: dispatch in/out, combine in/out, their grads */
   EP_TAG_TOPK_IDX = 1,      /* expert ids (int32); -1 = no expert */
   EP_TAG_TOPK_WEIGHTS = 2,  /* router weights (fp32) and their gradients */
   EP_TAG_FP8_SCALES = 3,    /* one fp32 scale per 128 channels of an FP8 row */
   EP_TAG_EXPERT_GRADS = 4,  /* expert parameter gradients */
-  EP_TAG_ROUTER_LOGITS = 5  /* router scores per token and expert (fp32) */
+  EP_TAG_ROUTER_LOGITS = 5,  /* router scores per token and expert (fp32) */
+  EP_TAG_EXPERT_WEIGHTS = 6  /* expert parameters: owners' weights and prefetch slots */
 } ep_tensor_tag_t;
 
 typedef enum ep_dtype {
@@ -97,6 +102,14 @@ typedef enum ep_layout {
   EP_LAYOUT_STATIC = 2  /* [R, C, H], C = ceil(T*k / R): every rank holds exactly its
                            share of rows; hot experts' tail rows go to replicas */
 } ep_layout_t;
+
+/* What a STATIC plan does with a replica past a rank's S-th slot (MoonEP
+ * article, par. 5).  The plan's rows are the same in both modes. */
+typedef enum ep_slot_mode {
+  EP_SLOTS_TRAINING = 0,  /* every duplicate needs a slot: overflow sets EP_FLAG_SLOT_BUDGET */
+  EP_SLOTS_INFERENCE = 1  /* a small fixed S; overflow segments read the owner's weights
+                             directly (seg_slot -1) and set no flag */
+} ep_slot_mode_t;
 
 /* Non-owning view of a contiguous row-major device tensor. */
 typedef struct ep_tensor {
@@ -118,6 +131,7 @@ typedef struct ep_group_config {
   int32_t layout;          /* ep_layout_t */
   int32_t capacity;        /* LL only: rows per expert, >= 1 */
   int32_t slots_per_rank;  /* STATIC only: replica slots S per rank, >= 0 */
+  int32_t slot_mode;       /* ep_slot_mode_t (STATIC only; 0 otherwise) */
 } ep_group_config_t;
 
 typedef struct ep_group *ep_group_t;
@@ -150,6 +164,8 @@ typedef struct ep_handle_view {
   int32_t *n_segments;     /* [1] */
   int32_t *load;           /* [R] rows used on each rank */
   int32_t *replica;        /* [R][S] expert held in each replica slot, -1 if empty */
+  int32_t *seg_slot;       /* [max_segments] slot of segment i on its rank (segments[i][1]),
+                              -1 if it has none (past the S-th: overflow) */
 } ep_handle_view_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -210,7 +226,9 @@ ep_status_t ep_route(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk
  *         rows of their hottest experts (count descending, id ascending);
  *         the shed runs fill the short ranks in rank order, behind their own
  *         rows; each short rank numbers the distinct experts it receives as
- *         replica slots 0, 1, ... (more than S sets EP_FLAG_SLOT_BUDGET).
+ *         replica slots 0, 1, ...; a segment past the S-th slot has none
+ *         (seg_slot -1), which sets EP_FLAG_SLOT_BUDGET in the training
+ *         slot mode and is the direct-read overflow in the inference mode.
  * Entries equal to -1 are skipped; other ids outside [0, E) are skipped and
  * set EP_FLAG_INDEX_RANGE.  Enqueues one kernel if T*k <= 2048, else two.
  * Re-planning a handle invalidates the layout every earlier output used. */
@@ -279,6 +297,24 @@ ep_status_t ep_combine_bwd(ep_handle_t h, const ep_tensor_t *grad_tokens,
 ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
                                const ep_tensor_t *replica_expert, ep_tensor_t *owner_grads,
                                void *stream);
+
+/* Replica-weight prefetch (MoonEP article, par. 3 and 5: the planner's
+ * redundant experts get their weights prefetched into dedicated slots; each
+ * expert projection's weights are contiguous).  After ep_plan of a STATIC
+ * handle: for every segment i with seg_slot[i] = s >= 0 on rank
+ * r = segments[i][1], slot (r, s) becomes a byte copy of expert
+ * segments[i][0]'s row of expert_weights.  Slots the plan leaves empty, and
+ * segments without a slot, are not touched (the overflow of the inference
+ * slot mode reads the owner's row directly).  Call it once per projection.
+ * expert_weights: [E, P...], tag EXPERT_WEIGHTS, dtype bf16, fp32 or FP8.
+ * slot_weights:   [R, S, P...] output, tag EXPERT_WEIGHTS, same dtype; the
+ *                 2-D form [R*S, P] is accepted too.
+ * A row (P elements) must be a multiple of 16 bytes.  Errors:
+ * EP_ERR_UNSUPPORTED for a non-STATIC handle, EP_ERR_NOT_PLANNED before
+ * ep_plan, EP_ERR_BAD_SHAPE for mismatched sizes.  Reads only the plan
+ * tables on the device; enqueues one kernel (none if R*S or P is 0). */
+ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weights,
+                                 ep_tensor_t *slot_weights, void *stream);
 
 #ifdef __cplusplus
 }

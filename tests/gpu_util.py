@@ -31,8 +31,8 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
-def make_group(E, R, H, k, T, kind, cap=0, S=0) -> ep.Group:
-    return ep.Group(E, R, H, k, max(T, 1), kind, capacity=cap, slots_per_rank=S)
+def make_group(E, R, H, k, T, kind, cap=0, S=0, mode="training") -> ep.Group:
+    return ep.Group(E, R, H, k, max(T, 1), kind, capacity=cap, slots_per_rank=S, slot_mode=mode)
 
 
 def check_layout(h: ep.Handle, L: "oracle.Layout", kind: str, idx: np.ndarray, w: np.ndarray | None):
@@ -57,6 +57,7 @@ def check_layout(h: ep.Handle, L: "oracle.Layout", kind: str, idx: np.ndarray, w
         assert np.array_equal(tb["segments"][:ns], p.segments), "segments"
         assert np.array_equal(tb["load"], p.load), "load"
         assert np.array_equal(tb["replica"], p.replica), "replica"
+        assert np.array_equal(tb["seg_slot"][:ns], p.seg_slot), "seg_slot"
         assert h.rank_rows == p.C
 
 

@@ -54,7 +54,7 @@ def test_status_strings(lib):
 
 def cfg(**kw):
     base = dict(num_experts=8, num_ranks=4, hidden=256, top_k=2, max_tokens=64,
-                layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0)
+                layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0, slot_mode=0)
     base.update(kw)
     return ep.ep_group_config_t(*[base[f] for f, _ in ep.ep_group_config_t._fields_])
 
@@ -69,6 +69,9 @@ def create(lib, **kw):
     dict(num_experts=0), dict(num_experts=1025), dict(num_ranks=3), dict(num_ranks=0),
     dict(hidden=12), dict(hidden=0), dict(top_k=0), dict(top_k=17), dict(max_tokens=-1),
     dict(layout=7), dict(layout=ep.LAYOUT_LL, capacity=0), dict(layout=ep.LAYOUT_STATIC, slots_per_rank=-1),
+    dict(layout=ep.LAYOUT_STATIC, slot_mode=2), dict(layout=ep.LAYOUT_STATIC, slot_mode=-1),
+    dict(slot_mode=ep.SLOTS_INFERENCE),               # the inference slot mode is STATIC only
+    dict(layout=ep.LAYOUT_STATIC, num_experts=1024, num_ranks=1024, slots_per_rank=1 << 22),
 ])
 def test_group_config_validation(lib, bad):
     rc, _ = create(lib, **bad)
@@ -136,7 +139,8 @@ def test_handle_view_points_into_workspace(lib):
     assert v.num_tokens == 64 and v.top_k == 2 and v.num_experts == 8 and v.num_ranks == 4
     assert v.recv_rows == 128 and v.rank_rows == 32 and v.max_segments == 12
     for name in ("counts", "offsets", "dst", "recv_src", "status", "keep", "native_row",
-                 "seg_first", "seg_count", "segments", "n_segments", "load", "replica"):
+                 "seg_first", "seg_count", "segments", "n_segments", "load", "replica",
+                 "seg_slot"):
         p = getattr(v, name)
         assert p is not None and FAKE <= p < FAKE + nbytes and p % 256 == 0
     lib.ep_handle_destroy(h)
@@ -258,5 +262,38 @@ def test_route_argument_validation(lib):
     assert Rt(h, lg, idx, T(F32, ep.TAG_TOPK_IDX, 64, 2), None) == 2
     assert Rt(h, lg, idx, None, None) == 1
     assert Rt(None, lg, idx, w, None) == 1
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_inference_slot_mode_accepted(lib):
+    rc, g = create(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=1, slot_mode=ep.SLOTS_INFERENCE)
+    assert rc == 0
+    lib.ep_group_destroy(g)
+
+
+def test_prefetch_argument_validation(lib):
+    P = lib.ep_prefetch_replicas
+    W = ep.TAG_EXPERT_WEIGHTS
+    g, h, _ = make_handle(lib)                       # HT: no replica slots
+    assert P(h, T(BF16, W, 8, 64), T(BF16, W, 4, 2, 64), None) == 7
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+    g, h, _ = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    w = T(BF16, W, 8, 64)
+    sl = T(BF16, W, 4, 2, 64)
+    assert P(h, None, sl, None) == 1
+    assert P(None, w, sl, None) == 1
+    assert P(h, T(BF16, ep.TAG_EXPERT_GRADS, 8, 64), sl, None) == 2
+    assert P(h, w, T(F32, W, 4, 2, 64), None) == 3       # dtypes differ
+    assert P(h, T(I32, W, 8, 64), T(I32, W, 4, 2, 64), None) == 3
+    assert P(h, T(BF16, W, 7, 64), sl, None) == 4        # not E experts
+    assert P(h, w, T(BF16, W, 4, 3, 64), None) == 4      # not [R, S, ...]
+    assert P(h, w, T(BF16, W, 4, 2, 32), None) == 4      # rows differ
+    assert P(h, w, T(BF16, W, 9, 64), None) == 4         # 2-D form needs R*S rows
+    assert P(h, T(BF16, W, 8, 4), T(BF16, W, 4, 2, 4), None) == 4   # 8-byte rows
+    assert P(h, w, sl, None) == 5                        # not planned
+    assert P(h, w, T(BF16, W, 8, 64), None) == 5         # 2-D form, not planned
+    assert P(h, T(FP8, W, 8, 2, 16), T(FP8, W, 4, 2, 2, 16), None) == 5
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
