@@ -128,19 +128,33 @@ def cpu_baseline(name, rho, fp8, budget_s):
         recv = oracle.dispatch(x, L.dst, L.rows)
         oracle.combine(recv, L.dst, w, out_fp32=c.out_fp32)
 
-    chain()
-    runs, t0 = 0, time.perf_counter()
-    while True:
+    def timed(seconds):
         chain()
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": Ts * runs / el, "unit": "tokens/s", "cores": oracle.get_threads(),
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            chain()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return runs, el
+
+    cores = oracle.get_threads()
+    runs, el = timed(budget_s * 0.75)
+    oracle.set_threads(1)
+    runs1, el1 = timed(budget_s * 0.25)
+    oracle.set_threads(cores)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": Ts * runs / el, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {Ts} of {c.T} tokens of the {name} workload, full "
                       f"layout{'+plan' if c.layout == 'static' else ''}+dispatch+combine chain, "
-                      f"{runs} runs in {el:.1f} s"}
+                      f"{runs} runs in {el:.1f} s on {cores} threads",
+            "value_1_thread": round(Ts * runs1 / el1, 1), "cpu_model": model}
 
 
 def main():
@@ -241,15 +255,22 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_host = time.perf_counter()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]
         e0.record(stream)
-        for _ in range(K):
+        for i in range(K):
             step()
+            if i < K - 1:
+                marks[i].record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
         t_host = time.perf_counter() - t_host
         step_ms = e0.elapsed_time(e1) / K
+        bounds = [e0] + marks + [e1]
+        step_list = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(K))
+        median_ms = step_list[K // 2] if K % 2 else 0.5 * (step_list[K // 2 - 1] + step_list[K // 2])
     else:
         tot = 0.0
+        steps_cold = []
         t_host = time.perf_counter()
         for _ in range(K):
             flush.fill_(1)
@@ -259,8 +280,11 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             tot += e0.elapsed_time(e1)
+            steps_cold.append(e0.elapsed_time(e1))
         t_host = time.perf_counter() - t_host
         step_ms = tot / K
+        step_list = sorted(steps_cold)
+        median_ms = step_list[K // 2] if K % 2 else 0.5 * (step_list[K // 2 - 1] + step_list[K // 2])
 
     # timed region 2: the same steps with an event pair around every launch
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -302,6 +326,7 @@ def main():
         "steps": K,
         "warmup": a.warmup,
         "ms_per_step": round(step_ms, 4),
+        "median_ms_per_step": round(median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -75,6 +75,7 @@ def _L():
             "orc_combine_bwd": (None, [i32, i32, i32, P, P, P, P, P, P]),
             "orc_dup_reduce": (None, [i32, i64, P, P, i32, P]),
             "orc_route": (None, [i32, i32, i32, P, P, P]),
+            "orc_grouped_gemm": (None, [i32, P, i32, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -317,6 +318,60 @@ def prefetch(weights: np.ndarray, replica: np.ndarray, slots: np.ndarray) -> np.
     if rc != 0:
         raise ValueError("orc_prefetch: a slot names an expert outside [0, E)")
     return out
+
+
+def expert_groups(L: Layout, kind: str, E: int, cap: int = 0, R: int = 1, S: int = 0,
+                  use_slots: bool = False) -> np.ndarray:
+    """Groups of consecutive receive rows that share one weight matrix, as
+    rows (row0, rows, widx).  widx < E is an owner expert; E + r*S + s is
+    prefetch slot s of rank r (used for a STATIC segment with a slot when
+    ``use_slots``; otherwise, and for overflow segments, the owner).
+      HT: expert e holds rows [offsets[e], offsets[e+1]).
+      LL: expert e holds rows [e*cap, e*cap + min(counts[e], cap)).
+      STATIC: e's kept rows on its home rank e // (E/R) at native_row[e],
+              and each segment's rows on its receiving rank."""
+    g = []
+    if kind == "ht":
+        for e in range(E):
+            n = int(L.offsets[e + 1] - L.offsets[e])
+            if n:
+                g.append((int(L.offsets[e]), n, e))
+    elif kind == "ll":
+        for e in range(E):
+            n = min(int(L.counts[e]), cap)
+            if n:
+                g.append((e * cap, n, e))
+    elif kind == "static":
+        p = L.plan
+        m = E // R
+        for e in range(E):
+            if p.keep[e]:
+                g.append(((e // m) * p.C + int(p.native_row[e]), int(p.keep[e]), e))
+        for i, (e, r, _, ln, row) in enumerate(p.segments.tolist()):
+            sl = int(p.seg_slot[i])
+            g.append((r * p.C + row, ln, E + r * S + sl if (use_slots and sl >= 0) else e))
+    else:
+        raise ValueError(kind)
+    return np.array(g, np.int32).reshape(-1, 3)
+
+
+def grouped_gemm(x_bits: np.ndarray, w_bits: np.ndarray, groups: np.ndarray,
+                 y_bits: np.ndarray | None = None) -> np.ndarray:
+    """Y[row0+i, n] = bf16(sum_c X[row0+i, c] * W[widx, n, c]) for every group;
+    other rows of Y keep ``y_bits`` (zeros if None).  x_bits [rows, K] and
+    w_bits [nW, N, K] are bf16 bit patterns."""
+    x = _c(x_bits, np.uint16)
+    w = _c(w_bits, np.uint16)
+    nW, N, K = w.shape
+    if x.shape[1] != K:
+        raise ValueError("grouped_gemm: X and W disagree on K")
+    gr = _c(groups, np.int32).reshape(-1, 3)
+    if gr.size and (gr[:, 0].min() < 0 or (gr[:, 0] + gr[:, 1]).max() > x.shape[0]
+                    or gr[:, 2].min() < 0 or gr[:, 2].max() >= nW):
+        raise ValueError("grouped_gemm: a group is outside X or names no weight matrix")
+    y = np.zeros((x.shape[0], N), np.uint16) if y_bits is None else np.array(y_bits, np.uint16, copy=True, order="C")
+    _L().orc_grouped_gemm(gr.shape[0], _p(gr), K, N, _p(x), _p(w), _p(y))
+    return y
 
 
 def route(logits: np.ndarray, k: int):

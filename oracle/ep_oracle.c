@@ -24,8 +24,9 @@
  *            (tensor roles: tokens, top-k indices, top-k weights, FP8
  *            scales), Figures 3-5.
  *   [ULMoE]  "Ultra-Large MoE Models: Open-Source Evolution and Heterogeneous
- *            Inference Adaptation", section 4.1 (experts split over devices
- *            in contiguous blocks).
+ *            Inference Adaptation", section 3.1 (top-k routing operator;
+ *            grouped GEMM over the tokens grouped by expert), section 4.1
+ *            (experts split over devices in contiguous blocks).
  * Every point those pages leave open is marked READING below and listed in
  * the design notes of the repository.
  *
@@ -605,6 +606,48 @@ void orc_dup_reduce(int32_t n, int64_t P, const uint16_t *rep, const int32_t *re
       for (int32_t i = 0; i < n; ++i)
         if (rep_e[i] == e) acc += orc_bf16_to_double(rep[(int64_t)i * P + p]);
       owner[(int64_t)e * P + p] = (float)acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* grouped GEMM of the experts                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ULMoE] section 3.1: the core of the expert computation is a grouped GEMM
+ * -- the tokens, grouped by expert, are multiplied by their expert's weights,
+ * one irregularly sized matrix product per expert.  [NCCLEP] Figure 2 puts
+ * the expert FFN between dispatch and combine, on the dispatched rows.
+ * READING: one product per group of consecutive receive rows that share a
+ * weight matrix; the weights of each expert are one [N][K] matrix (a linear
+ * layer's layout, K contiguous), and a prefetch slot holds a copy of one.
+ * Definition, for every group g = (row0, rows, widx), row i < rows and
+ * column n < N:
+ *   Y[row0 + i][n] = bf16( sum_{c < K} X[row0 + i][c] * W[widx][n][c] )
+ * with the sum taken in double (each bf16 x bf16 product is exact there)
+ * and rounded once, to nearest even.  Rows of Y that no group covers are
+ * left unchanged.
+ *   groups  [ngroups][3]   row0, rows, widx
+ *   X       [.][K] bf16    the receive buffer
+ *   W       [.][N][K] bf16 the table of weight matrices
+ *   Y       [.][N] bf16
+ */
+void orc_grouped_gemm(int32_t ngroups, const int32_t *groups, int32_t K, int32_t N,
+                      const uint16_t *X, const uint16_t *W, uint16_t *Y) {
+  for (int32_t g = 0; g < ngroups; ++g) {
+    const int64_t row0 = groups[g * 3 + 0], rows = groups[g * 3 + 1], widx = groups[g * 3 + 2];
+    const uint16_t *Wg = W + widx * (int64_t)N * K;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < rows; ++i) {
+      const uint16_t *x = X + (row0 + i) * K;
+      for (int32_t n = 0; n < N; ++n) {
+        const uint16_t *w = Wg + (int64_t)n * K;
+        double acc = 0.0;
+        for (int32_t c = 0; c < K; ++c) acc += orc_bf16_to_double(x[c]) * orc_bf16_to_double(w[c]);
+        Y[(row0 + i) * N + n] = orc_bf16_from_double(acc);
+      }
     }
   }
 }

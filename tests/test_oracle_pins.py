@@ -642,3 +642,90 @@ def test_route_feeds_the_workload_inputs():
     idx, w = oracle.route(inp.logits, inp.cfg.k)
     assert np.array_equal(idx, inp.topk_idx)
     assert np.max(np.abs(w - inp.topk_w)) <= 2.0 ** -23
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM of the experts
+# ---------------------------------------------------------------------------
+
+def _bits(vals) -> np.ndarray:
+    return _torch_bf16_bits(np.asarray(vals, np.float32))
+
+
+@pytest.mark.parametrize("case", ["A", "B"])
+def test_grouped_gemm_golden(case):
+    g = read_golden("gemm_small.txt")[case]
+    K, N = int(g["K"][0]), int(g["N"][0])
+    x = _bits(floats(g["X"])).reshape(-1, K)
+    w = _bits(floats(g["W"])).reshape(-1, N, K)
+    groups = ints(g["groups"]).reshape(-1, 3)
+    y = oracle.grouped_gemm(x, w, groups)
+    assert bf16_bits_to_f32(y).ravel().tolist() == floats(g["Y"]).tolist()
+    if "idx" in g:   # the groups are the HT layout's experts
+        E, T, k = int(g["E"][0]), int(g["T"][0]), int(g["k"][0])
+        L = oracle.layout(ints(g["idx"]).reshape(T, k).astype(np.int32), E, "ht")
+        assert oracle.expert_groups(L, "ht", E).tolist() == groups.tolist()
+
+
+def test_grouped_gemm_integer_inputs_match_numpy_exactly():
+    # small-integer bf16 inputs: every sum is exact in float64, so numpy's
+    # matmul and the bf16 rounding of torch give the only correct answer
+    rng = np.random.default_rng(41)
+    K, N, rows = 96, 40, 70
+    xf = rng.integers(-8, 9, (rows, K)).astype(np.float32)
+    wf = rng.integers(-8, 9, (3, N, K)).astype(np.float32) * 0.5
+    groups = np.array([[0, 20, 2], [20, 1, 0], [30, 40, 1]], np.int32)   # rows 21..29 uncovered
+    y0 = _bits(np.full((rows, N), 7.0))
+    y = oracle.grouped_gemm(_bits(xf), _bits(wf), groups, y0)
+    want = y0.copy()
+    for r0, n, wi in groups:
+        want[r0:r0 + n] = _bits(xf[r0:r0 + n].astype(np.float64) @ wf[wi].astype(np.float64).T)
+    assert np.array_equal(y, want)
+
+
+def test_grouped_gemm_random_within_one_rounding_of_numpy():
+    rng = np.random.default_rng(42)
+    K, N, rows = 256, 24, 50
+    x = _bits(rng.standard_normal((rows, K)))
+    w = _bits(rng.standard_normal((2, N, K)) * 0.05)
+    groups = np.array([[0, 25, 1], [25, 25, 0]], np.int32)
+    y = bf16_bits_to_f32(oracle.grouped_gemm(x, w, groups)).astype(np.float64)
+    xd, wd = bf16_bits_to_f32(x).astype(np.float64), bf16_bits_to_f32(w).astype(np.float64)
+    ref = np.concatenate([xd[:25] @ wd[1].T, xd[25:] @ wd[0].T])
+    assert np.all(np.abs(y - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)   # half a bf16 ulp
+
+
+def test_grouped_gemm_identity_weights_return_the_rows():
+    rng = np.random.default_rng(43)
+    K = 64
+    x = _bits(rng.standard_normal((33, K)))
+    eye = _bits(np.eye(K))[None]
+    y = oracle.grouped_gemm(x, eye, np.array([[0, 33, 0]], np.int32))
+    assert np.array_equal(same_sign_zero(y), same_sign_zero(x))
+
+
+def same_sign_zero(b: np.ndarray) -> np.ndarray:
+    b = b.copy()
+    b[b == 0x8000] = 0     # x * 1 + 0 * ... sums to +0 for a -0 input
+    return b
+
+
+@pytest.mark.parametrize("kind", ["ht", "ll", "static"])
+def test_expert_groups_cover_every_routed_row_once_with_its_expert(kind):
+    idx, w, _ = workloads.random_case(44, 300, 8, 16, 4, mask_frac=0.05, skew=1.5)
+    E, R, S, cap = 16, 4, 1, 40
+    L = oracle.layout(idx, E, kind, cap=cap, R=R, S=S, slot_mode=oracle.SLOTS_INFERENCE)
+    for use_slots in (False, True):
+        groups = oracle.expert_groups(L, kind, E, cap=cap, R=R, S=S, use_slots=use_slots)
+        owner = np.full(L.rows, -1, np.int64)
+        for r0, n, wi in groups:
+            assert np.all(owner[r0:r0 + n] == -1)            # no row in two groups
+            if wi < E:
+                owner[r0:r0 + n] = wi
+            else:                                           # a slot holds a copy of an expert
+                r, s = divmod(int(wi) - E, S)
+                owner[r0:r0 + n] = L.plan.replica[r, s]
+        _, ridx, _ = oracle.recv_meta(idx, w, L.dst, L.rows)
+        assert np.array_equal(owner, np.where(ridx >= 0, ridx, -1))   # exactly the used rows
+        if kind == "static" and use_slots:
+            assert np.any(groups[:, 2] >= E) and np.any(L.plan.seg_slot < 0)
