@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak), T=4096 H=7168 top-8"
 
 
@@ -49,6 +50,11 @@ def parse():
                    help="STATIC workloads: what the plan does past a rank's S-th replica slot")
     p.add_argument("--slots", type=int, default=None,
                    help="STATIC workloads: replica slots per rank (default: the workload's)")
+    p.add_argument("--gemm", type=int, default=0, metavar="N",
+                   help="add the grouped GEMM of the experts after dispatch: the received "
+                        "[rows, H] bf16 tokens times one [N, H] bf16 matrix per expert (through "
+                        "the prefetch slots with --prefetch); reported beside the step, its "
+                        "roofline against the bf16 MFMA peak")
     p.add_argument("--cold", action="store_true",
                    help="write a 512 MB buffer before every step (Infinity Cache flushed); "
                         "steps are then timed one by one")
@@ -62,7 +68,7 @@ def parse():
 PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
 
 
-def algorithmic_bytes(c, fp8=False, filled_slots=0):
+def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P):
     """Bytes each kernel must move by definition: x read once, every routed row
     written once and read once, outputs written once, int32/fp32 metadata."""
     N = c.T * c.k
@@ -78,7 +84,7 @@ def algorithmic_bytes(c, fp8=False, filled_slots=0):
         b["dispatch_bwd"] = N * row + N * 4 + c.T * row
         P = 4096 * 1536
         b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
-    b["prefetch"] = filled_slots * PREFETCH_P * 2 * 2            # each filled slot: owner row read, slot written
+    b["prefetch"] = filled_slots * slot_elems * 2 * 2            # each filled slot: owner row read, slot written
     return b
 
 
@@ -223,9 +229,16 @@ def main():
         idx, w = torch.empty_like(idx), torch.empty_like(w)
         ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, stream)))
     ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, stream)))
-    if a.prefetch:
+    slot_elems = a.gemm * c.H if a.gemm else PREFETCH_P
+    slots = None
+    if a.gemm:   # one [N, H] projection per expert, the GEMM's weights
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 * 5 + 7)
+        wts = (torch.randn((c.E, a.gemm, c.H), generator=gen, device=dev) * c.H ** -0.5).to(torch.bfloat16)
+    elif a.prefetch:
         wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
-        slots = torch.empty((c.R, S, PREFETCH_P), dtype=torch.bfloat16, device=dev)
+    if a.prefetch:
+        slots = torch.empty((c.R, S) + tuple(wts.shape[1:]), dtype=torch.bfloat16, device=dev)
         ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, stream)))
     if a.fp8:
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
@@ -234,6 +247,10 @@ def main():
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, stream)))
     else:
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)))
+    if a.gemm:
+        gy_out = torch.empty((h.recv_rows, a.gemm), dtype=torch.bfloat16, device=dev)
+        recv2d = recv.view(h.recv_rows, c.H)
+        ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, stream)))
     ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, stream)))
     if train:
         ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, stream)))
@@ -302,7 +319,22 @@ def main():
               for i, (nm, _) in enumerate(ops)}
 
     filled = int((h.tables()["replica"] >= 0).sum()) if c.layout == "static" and S > 0 else 0
-    ab = algorithmic_bytes(c, a.fp8, filled)
+    ab = algorithmic_bytes(c, a.fp8, filled, slot_elems)
+    gemm_info = None
+    if a.gemm:
+        tb = h.tables()
+        if c.layout == "ll":
+            grows = int(torch.clamp(tb["counts"], max=c.cap).sum())
+        else:
+            grows = int(tb["offsets"][-1])   # every routed entry is one row of some group
+        flops = 2.0 * grows * a.gemm * c.H
+        ab["gemm"] = grows * c.H * 2 + c.E * a.gemm * c.H * 2 + grows * a.gemm * 2   # X, W, Y once
+        tflops = flops / (per_us["gemm"] * 1e-6) / 1e12
+        gemm_info = {"N": a.gemm, "K": c.H, "rows": grows, "flops": flops,
+                     "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
     chain_bytes = sum(ab[nm] for nm, _ in ops)
     step_s = step_ms / 1000.0
     dom = max((nm for nm in ("dispatch", "combine", "combine_bwd") if nm in per_us),
@@ -335,7 +367,8 @@ def main():
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route},
-        **({"prefetch": {"filled_slots": filled, "slot_bytes": PREFETCH_P * 2}} if a.prefetch else {}),
+        **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
+        **({"gemm": gemm_info} if gemm_info else {}),
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": chain_bytes,

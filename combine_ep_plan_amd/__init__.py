@@ -27,7 +27,8 @@ __all__ = [
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
-    "ep_dup_grad_reduce", "ep_prefetch_replicas", "SLOTS_TRAINING", "SLOTS_INFERENCE",
+    "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "SLOTS_TRAINING",
+    "SLOTS_INFERENCE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -109,6 +110,7 @@ def load_library():
         "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_prefetch_replicas": (S, [c_void_p, _T, _T, c_void_p]),
+        "ep_expert_gemm": (S, [c_void_p, _T, _T, _T, _T, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -260,6 +262,14 @@ def ep_prefetch_replicas(h: int, expert_weights: torch.Tensor, slot_weights: tor
     _check(load_library().ep_prefetch_replicas(
         c_void_p(h), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
         _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _stream(stream)), "ep_prefetch_replicas")
+
+
+def ep_expert_gemm(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
+                   slot_weights: torch.Tensor | None, out: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_expert_gemm(
+        c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
+        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream)),
+        "ep_expert_gemm")
 
 
 # ---------------------------------------------------------------------------
@@ -447,6 +457,19 @@ class Buffer:
                                 dtype=expert_weights.dtype, device=expert_weights.device)
         ep_prefetch_replicas(handle.ptr, expert_weights, slots, stream)
         return slots
+
+    def expert_gemm(self, recv: torch.Tensor, expert_weights: torch.Tensor, handle: Handle,
+                    slots: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+        """Grouped GEMM of the experts over the received rows: ``recv``
+        [rows, K] (any leading shape) times each group's [N, K] weights."""
+        N = expert_weights.shape[1]
+        rows = handle.recv_rows
+        if out is None:
+            out = torch.empty((rows, N), dtype=torch.bfloat16, device=recv.device)
+        ep_expert_gemm(handle.ptr, recv.view(rows, expert_weights.shape[2]), expert_weights, slots,
+                       out, stream)
+        return out
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,
                         handle: Handle, replica_expert: torch.Tensor | None = None,

@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argum
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 SOURCES = ["route.hip", "plan.hip", "dispatch.hip", "combine.hip", "dup_reduce.hip", "prefetch.hip",
-           "ep_api.cpp"]
+           "gemm.hip", "ep_api.cpp"]
 
 
 def hipcc() -> str:

@@ -125,6 +125,8 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
     w.replica = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)g.R * g.S));
     w.seg_slot = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)(g.E + g.R)));
   }
+  w.gemm_tiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * 4 * (size_t)gemm_max_tiles(g)));
+  w.gemm_ntiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t)));
   if (ws) *ws = w;
   return off;
 }
@@ -475,6 +477,42 @@ ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weight
   return hip_status(epk::launch_prefetch(g, h->ws, static_cast<const uint8_t *>(w->data),
                                          row_bytes, static_cast<uint8_t *>(sl->data),
                                          as_stream(stream)));
+}
+
+ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                           const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
+                           ep_tensor_t *out, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(recv_tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  st = check_tensor(expert_weights, EP_TAG_EXPERT_WEIGHTS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  st = check_tensor(out, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  const ep_tensor_t *w = expert_weights;
+  if (w->ndim != 3 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
+  const int64_t N = w->sizes[1], K = w->sizes[2];
+  if (K <= 0 || K % 64 != 0 || K > INT32_MAX || N < 1 || N > INT32_MAX) return EP_ERR_BAD_SHAPE;
+  if (!is_rows(recv_tokens, g.rows, K) || !is_rows(out, g.rows, N)) return EP_ERR_BAD_SHAPE;
+  const uint16_t *wslot = nullptr;
+  if (slot_weights) {
+    st = check_tensor(slot_weights, EP_TAG_EXPERT_WEIGHTS, EP_DTYPE_BF16);
+    if (st != EP_OK) return st;
+    if (g.layout != EP_LAYOUT_STATIC) return EP_ERR_UNSUPPORTED;
+    const ep_tensor_t *sl = slot_weights;
+    const bool four = sl->ndim == 4 && sl->sizes[0] == g.R && sl->sizes[1] == g.S &&
+                      sl->sizes[2] == N && sl->sizes[3] == K;
+    const bool three = sl->ndim == 3 && sl->sizes[0] == (int64_t)g.R * g.S && sl->sizes[1] == N &&
+                       sl->sizes[2] == K;
+    if (!four && !three) return EP_ERR_BAD_SHAPE;
+    wslot = static_cast<const uint16_t *>(sl->data);
+  }
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return hip_status(epk::launch_grouped_gemm(g, h->ws, static_cast<const uint16_t *>(recv_tokens->data),
+                                             static_cast<const uint16_t *>(w->data), wslot,
+                                             (int32_t)K, (int32_t)N,
+                                             static_cast<uint16_t *>(out->data), as_stream(stream)));
 }
 
 }  // extern "C"

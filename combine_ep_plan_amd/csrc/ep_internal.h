@@ -15,6 +15,7 @@ constexpr int kTileEntries = kTileThreads * kTileChunks;  // 2048
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kLdsLimit = 65536;
+constexpr int kGemmBM = 128;  // rows of one grouped-GEMM tile
 
 constexpr uint32_t kFlagIndexRange = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
@@ -41,6 +42,9 @@ struct Workspace {
   int32_t *load;         // [R]
   int32_t *replica;      // [R*S]
   int32_t *seg_slot;     // [E+R] slot of each segment on its rank, -1 if none
+  // grouped GEMM
+  int32_t *gemm_tiles;   // [gemm_max_tiles][4] row0, rows, weight index, 0
+  int32_t *gemm_ntiles;  // [1]
 };
 
 struct Geometry {
@@ -76,6 +80,10 @@ hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, in
                         float *w, hipStream_t s);
 hipError_t launch_prefetch(const Geometry &g, const Workspace &ws, const uint8_t *weights,
                            int64_t row_bytes, uint8_t *slots, hipStream_t s);
+int32_t gemm_max_tiles(const Geometry &g);
+hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
+                               const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
+                               uint16_t *y, hipStream_t s);
 hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
                              int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
 

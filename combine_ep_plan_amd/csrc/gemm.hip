@@ -1,0 +1,255 @@
+// gemm.hip -- grouped GEMM of the experts on gfx950 MFMA ("Ultra-Large MoE
+// Models" article, section 3.1: the core of the expert computation, one
+// irregularly sized matrix product per expert over the tokens grouped by
+// expert; NCCL EP listing, Figure 2: the expert FFN sits between dispatch
+// and combine).
+//
+// For every group of consecutive receive rows that share one weight matrix
+// (an expert's rows, or a STATIC segment through its prefetch slot):
+//   Y[row][n] = bf16( sum_c X[row][c] * W[n][c] ),  fp32 accumulation.
+//
+// Two kernels:
+//  * k_gemm_tiles (one workgroup) cuts the groups of the current plan into
+//    row tiles of kBM rows -- (row0, rows, weight index) -- with a prefix sum
+//    over the groups, so the GEMM grid can have a fixed size;
+//  * k_grouped_gemm: one 256-thread workgroup per (row tile, kBN columns);
+//    four waves in a 2 x 2 arrangement, each owning a 64 x 64 block of the
+//    output as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.  The kBK = 64
+//    deep slabs of X and W go through LDS, double-buffered: the next slab's
+//    16-byte global loads are in flight while the current one feeds the
+//    MFMAs.  LDS rows are 128 bytes (eight 16-byte chunks) and chunk c of
+//    row r is stored at c ^ (r & 7), so the 32 rows one MFMA operand read
+//    touches fall on distinct banks.  Workgroup ids are remapped so that the
+//    workgroups of one XCD take consecutive tiles (the column tiles of one
+//    row tile share its X rows in that XCD's L2).
+#include "device.h"
+#include "ep_internal.h"
+
+namespace epk {
+
+constexpr int kGemmThreads = 256;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+constexpr int kChunks = kBK / 8;  // 16-byte chunks in one row of a slab
+constexpr int kXcds = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ (row & 7)); }
+
+// ---------------------------------------------------------------------------
+// tile table
+
+struct TileArgs {
+  Geometry g;
+  Workspace ws;
+  int32_t use_slots;  // STATIC segments with a slot read weights from the slot
+};
+
+// Group q of the current plan: first receive row, rows, weight index
+// (< E: owner expert; E + r*S + s: slot s of rank r).
+__device__ __forceinline__ void group_of(const TileArgs &a, int32_t q, int32_t &row0,
+                                         int32_t &rows, int32_t &widx) {
+  const Geometry &g = a.g;
+  const Workspace &ws = a.ws;
+  if (g.layout == kHT) {
+    row0 = ws.offsets[q];
+    rows = ws.offsets[q + 1] - row0;
+    widx = q;
+  } else if (g.layout == kLL) {
+    const int32_t c = ws.counts[q];
+    row0 = q * g.cap;
+    rows = c < g.cap ? c : g.cap;
+    widx = q;
+  } else if (q < g.E) {  // kept rows of expert q on its home rank
+    const int32_t m = g.E / g.R;
+    row0 = (q / m) * g.C + ws.native_row[q];
+    rows = ws.keep[q];
+    widx = q;
+  } else {  // segment q - E on its receiving rank
+    const int32_t *s = ws.segments + (int64_t)(q - g.E) * 5;
+    const int32_t slot = ws.seg_slot[q - g.E];
+    row0 = s[1] * g.C + s[4];
+    rows = s[3];
+    widx = (a.use_slots && slot >= 0) ? g.E + s[1] * g.S + slot : s[0];
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_tiles) {
+  __shared__ int32_t s_wave[16];
+  __shared__ int32_t s_base;
+  const Geometry &g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t ngroups = g.layout == kStatic ? g.E + *a.ws.n_segments : g.E;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int32_t q0 = 0; q0 < ngroups; q0 += 1024) {
+    const int32_t q = q0 + tid;
+    int32_t row0 = 0, rows = 0, widx = 0;
+    if (q < ngroups) group_of(a, q, row0, rows, widx);
+    const int32_t nt = rows > 0 ? (rows + kGemmBM - 1) / kGemmBM : 0;
+    // inclusive scan of nt over the workgroup: lanes, then waves
+    int32_t x = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int32_t before = s_base, total = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      before += v < w ? s_wave[v] : 0;
+      total += s_wave[v];
+    }
+    int32_t t = before + x - nt;
+    for (int32_t i = 0; i < nt && t < max_tiles; ++i, ++t) {
+      int32_t *e = a.ws.gemm_tiles + (int64_t)t * 4;
+      e[0] = row0 + i * kGemmBM;
+      e[1] = rows - i * kGemmBM < kGemmBM ? rows - i * kGemmBM : kGemmBM;
+      e[2] = widx;
+      e[3] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) s_base += total;
+    __syncthreads();
+  }
+  if (tid == 0) *a.ws.gemm_ntiles = s_base < max_tiles ? s_base : max_tiles;
+}
+
+// ---------------------------------------------------------------------------
+// grouped GEMM
+
+__global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
+    const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
+    int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
+  __shared__ u32x4 sa[2][kGemmBM * kChunks];
+  __shared__ u32x4 sb[2][kBN * kChunks];
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous range of logical tiles (column tile fastest)
+  const int32_t per_xcd = gridDim.x / kXcds;
+  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int32_t tile = lid / n_col_tiles;
+  if (tile >= *ntiles) return;
+  const int32_t n0 = (lid - tile * n_col_tiles) * kBN;
+  const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
+  const int64_t KV = K / 8;  // 16-byte vectors per row
+  const u32x4 *Wm = widx < E ? W + (int64_t)widx * N * KV : Wslot + (int64_t)(widx - E) * N * KV;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+
+  // loader: chunk q = tid + i * 256 of a slab is row q / 8, chunk q % 8
+  constexpr int kLoads = kGemmBM * kChunks / kGemmThreads;  // 4
+  const int c_ld = tid & (kChunks - 1);
+  const u32x4 *pa[kLoads];
+  const u32x4 *pb[kLoads];
+  bool va[kLoads], vb[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    va[i] = r < rows;
+    vb[i] = n0 + r < N;
+    pa[i] = X + (int64_t)(row0 + (va[i] ? r : 0)) * KV + c_ld;
+    pb[i] = Wm + (int64_t)(vb[i] ? n0 + r : 0) * KV + c_ld;
+  }
+  u32x4 ra[kLoads], rb[kLoads];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      ra[i] = va[i] ? pa[i][kt * kChunks] : zero;
+      rb[i] = vb[i] ? pb[i][kt * kChunks] : zero;
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int r = (tid + i * kGemmThreads) / kChunks;
+      sa[buf][swz(r, c_ld)] = ra[i];
+      sb[buf][swz(r, c_ld)] = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int KT = K / kBK;
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);  // this lane's 8 K-values of the 16
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + (lane & 31);
+        fa[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(row, c)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + j * 32 + (lane & 31);
+        fb[j] = __builtin_bit_cast(bf16x8, sb[buf][swz(n, c)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator r of a lane: row (r / 4) * 8 + (lane / 32) * 4 + r % 4, column lane % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);  // rows row, row + 1
+        if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
+        if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
+      }
+    }
+}
+
+int32_t gemm_max_tiles(const Geometry &g) {
+  const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
+  return (int32_t)((g.n + kGemmBM - 1) / kGemmBM + groups);
+}
+
+hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
+                               const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
+                               uint16_t *y, hipStream_t s) {
+  const int32_t max_tiles = gemm_max_tiles(g);
+  if (max_tiles == 0 || N == 0) return hipSuccess;
+  TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
+  hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  const int32_t ncol = (N + kBN - 1) / kBN;
+  int64_t blocks = (int64_t)max_tiles * ncol;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the XCD remap needs a multiple of 8
+  hipLaunchKernelGGL(k_grouped_gemm, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+                     reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
+                     reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
+                     g.E, ncol, y);
+  return hipGetLastError();
+}
+
+}  // namespace epk

@@ -316,6 +316,34 @@ ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
 ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weights,
                                  ep_tensor_t *slot_weights, void *stream);
 
+/* Grouped GEMM of the experts ("Ultra-Large MoE Models" article, section
+ * 3.1: the tokens grouped by expert are multiplied by their expert's
+ * weights, one irregularly sized product per expert; NCCL EP listing,
+ * Figure 2: the expert FFN between dispatch and combine).  After ep_plan,
+ * for every group of receive rows that share a weight matrix and every
+ * row i of it, column n < N:
+ *   out[i, n] = bf16( sum_c recv_tokens[i, c] * W[n, c] )  (fp32 MFMA
+ *   accumulation, rounded once to nearest even)
+ * Groups: HT -- expert e's rows [offsets[e], offsets[e+1]); LL -- rows
+ * [e*cap, e*cap + min(counts[e], cap)); STATIC -- e's kept rows on its home
+ * rank and each segment's rows on its receiving rank, with W the segment's
+ * prefetch slot when slot_weights is given and the segment has one, else
+ * the owner's matrix (the inference overflow reads the owner directly).
+ * recv_tokens:    bf16 [recv_rows, K] (e.g. the dispatch output), tag TOKENS;
+ *                 K % 64 == 0.
+ * expert_weights: bf16 [E, N, K] (each expert's [N, K] matrix, K
+ *                 contiguous), tag EXPERT_WEIGHTS.
+ * slot_weights:   NULL, or (STATIC only) bf16 [R, S, N, K] or [R*S, N, K],
+ *                 tag EXPERT_WEIGHTS (filled by ep_prefetch_replicas).
+ * out:            bf16 [recv_rows, N], tag TOKENS; rows no group covers are
+ *                 not written.
+ * Errors: EP_ERR_BAD_SHAPE, EP_ERR_UNSUPPORTED (slots for a non-STATIC
+ * handle), EP_ERR_NOT_PLANNED.  Enqueues two kernels (the tile table of the
+ * current plan, then the GEMM). */
+ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                           const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
+                           ep_tensor_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -297,3 +297,29 @@ def test_prefetch_argument_validation(lib):
     assert P(h, T(FP8, W, 8, 2, 16), T(FP8, W, 4, 2, 2, 16), None) == 5
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
+
+
+def test_expert_gemm_argument_validation(lib):
+    G = lib.ep_expert_gemm
+    W, TK = ep.TAG_EXPERT_WEIGHTS, ep.TAG_TOKENS
+    g, h, _ = make_handle(lib)                       # HT, T=64, k=2: 128 rows, E=8
+    x = T(BF16, TK, 128, 64)
+    w = T(BF16, W, 8, 32, 64)
+    y = T(BF16, TK, 128, 32)
+    assert G(None, x, w, None, y, None) == 1
+    assert G(h, T(BF16, W, 128, 64), w, None, y, None) == 2      # x must be TOKENS
+    assert G(h, x, T(F32, W, 8, 32, 64), None, y, None) == 3
+    assert G(h, x, T(BF16, W, 7, 32, 64), None, y, None) == 4    # not E matrices
+    assert G(h, T(BF16, TK, 128, 48), T(BF16, W, 8, 32, 48), None, T(BF16, TK, 128, 32), None) == 4  # K % 64
+    assert G(h, x, w, None, T(BF16, TK, 128, 33), None) == 4      # out columns != N
+    assert G(h, T(BF16, TK, 127, 64), w, None, y, None) == 4      # not recv_rows
+    assert G(h, x, w, T(BF16, W, 4, 1, 32, 64), y, None) == 7     # slots only for STATIC
+    assert G(h, x, w, None, y, None) == 5                         # not planned
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+    g, h, _ = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    assert G(h, x, w, T(BF16, W, 4, 3, 32, 64), y, None) == 4     # not [R, S, N, K]
+    assert G(h, x, w, T(BF16, W, 8, 32, 64), y, None) == 5        # [R*S, N, K] accepted; not planned
+    assert G(h, x, w, T(BF16, W, 4, 2, 32, 64), y, None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
