@@ -10,25 +10,37 @@
 //
 // Two kernels:
 //  * k_gemm_tiles (one workgroup) cuts the groups of the current plan into
-//    row tiles of kBM rows -- (row0, rows, weight index) -- with a prefix sum
-//    over the groups, so the GEMM grid can have a fixed size;
-//  * k_grouped_gemm: one 256-thread workgroup per (row tile, kBN columns);
-//    four waves in a 2 x 2 arrangement, each owning a 64 x 64 block of the
-//    output as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.  The kBK = 64
-//    deep slabs of X and W go through LDS, double-buffered: the next slab's
-//    16-byte global loads are in flight while the current one feeds the
-//    MFMAs.  LDS rows are 128 bytes (eight 16-byte chunks) and chunk c of
-//    row r is stored at c ^ (r & 7), so the 32 rows one MFMA operand read
-//    touches fall on distinct banks.  Workgroup ids are remapped so that the
-//    workgroups of one XCD take consecutive tiles (the column tiles of one
-//    row tile share its X rows in that XCD's L2).
+//    row tiles of kGemmBM rows -- (row0, rows, weight index) -- with a prefix
+//    sum over the groups, so the GEMM grid can have a fixed size;
+//  * k_grouped_gemm: one 256-thread workgroup per (row tile, 128 columns),
+//    two per CU; four waves in a 2 x 2 arrangement, each owning a 64 x 64
+//    block of the output as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.
+//    Slabs 64 deep of X and W go through LDS, double-buffered.  Pipelining:
+//    the global loads of slab kt+2 are in flight during slab kt+1; within a
+//    slab, the fragments of the next 16-deep step are read from LDS while
+//    the MFMAs of the current one run, and the first step of the next slab
+//    is read right after the barrier that publishes it.
+//    LDS: rows of a slab are 128 bytes (eight 16-byte chunks); with 64
+//    4-byte banks two rows share a 256-byte bank row, so chunk c of row r is
+//    stored at c ^ ((r / 2) % 8): the 16 rows one 16-lane phase of an MFMA
+//    operand read touches then cover all 64 banks once (no conflicts).
+//    Rows past a tile's end load a valid row instead of branching (their
+//    products land in outputs that are never stored).
+//    Workgroup order: workgroup b runs on XCD b % 8; each XCD takes an equal,
+//    contiguous share of the valid (row tile, column tile) pairs, column tile
+//    fastest, so the column tiles of one row tile share its X rows in that
+//    XCD's L2 and no XCD idles on the grid's unused tail.
 #include "device.h"
 #include "ep_internal.h"
 
 namespace epk {
 
-constexpr int kGemmThreads = 256;
+constexpr int kTileM = kGemmBM;
 constexpr int kBN = 128;
+constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kGemmThreads = 64 * kWavesM * kWavesN;
+constexpr int kWTM = kTileM / kWavesM, kWTN = kBN / kWavesN;  // one wave's output block
+constexpr int kFM = kWTM / 32, kFN = kWTN / 32;                // 32 x 32 MFMA blocks per wave
 constexpr int kBK = 64;
 constexpr int kChunks = kBK / 8;  // 16-byte chunks in one row of a slab
 constexpr int kXcds = 8;
@@ -36,7 +48,8 @@ constexpr int kXcds = 8;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ ((row >> 1) & 7)); }
+static_assert(kChunks == 8, "the swizzle assumes 128-byte slab rows");
 
 // ---------------------------------------------------------------------------
 // tile table
@@ -88,7 +101,7 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
     const int32_t q = q0 + tid;
     int32_t row0 = 0, rows = 0, widx = 0;
     if (q < ngroups) group_of(a, q, row0, rows, widx);
-    const int32_t nt = rows > 0 ? (rows + kGemmBM - 1) / kGemmBM : 0;
+    const int32_t nt = rows > 0 ? (rows + kTileM - 1) / kTileM : 0;
     // inclusive scan of nt over the workgroup: lanes, then waves
     int32_t x = nt;
 #pragma unroll
@@ -107,8 +120,8 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
     int32_t t = before + x - nt;
     for (int32_t i = 0; i < nt && t < max_tiles; ++i, ++t) {
       int32_t *e = a.ws.gemm_tiles + (int64_t)t * 4;
-      e[0] = row0 + i * kGemmBM;
-      e[1] = rows - i * kGemmBM < kGemmBM ? rows - i * kGemmBM : kGemmBM;
+      e[0] = row0 + i * kTileM;
+      e[1] = rows - i * kTileM < kTileM ? rows - i * kTileM : kTileM;
       e[2] = widx;
       e[3] = 0;
     }
@@ -126,103 +139,119 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
     int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
-  __shared__ u32x4 sa[2][kGemmBM * kChunks];
+  __shared__ u32x4 sa[2][kTileM * kChunks];
+  static_assert(kTileM * kChunks % kGemmThreads == 0 && kBN * kChunks % kGemmThreads == 0, "loader");
   __shared__ u32x4 sb[2][kBN * kChunks];
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of logical tiles (column tile fastest)
-  const int32_t per_xcd = gridDim.x / kXcds;
-  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  // XCD-aware order over the valid work only (the grid is sized for the
+  // largest possible tile count)
+  const int32_t valid = *ntiles * n_col_tiles;
+  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
+  const int32_t slot = blockIdx.x / kXcds;
+  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || lid >= valid) return;
   const int32_t tile = lid / n_col_tiles;
-  if (tile >= *ntiles) return;
   const int32_t n0 = (lid - tile * n_col_tiles) * kBN;
   const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
   const int64_t KV = K / 8;  // 16-byte vectors per row
   const u32x4 *Wm = widx < E ? W + (int64_t)widx * N * KV : Wslot + (int64_t)(widx - E) * N * KV;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / kWavesN, wn = wv % kWavesN;
 
-  // loader: chunk q = tid + i * 256 of a slab is row q / 8, chunk q % 8
-  constexpr int kLoads = kGemmBM * kChunks / kGemmThreads;  // 4
+  // loader: chunk q = tid + i * 256 of a slab is row q / 8, chunk q % 8.
+  // Rows past the tile's end read a valid row instead (their products land
+  // in outputs that are never stored), so every load is unconditional.
+  constexpr int kLoads = kTileM * kChunks / kGemmThreads;
+  constexpr int kLoadsB = kBN * kChunks / kGemmThreads;
   const int c_ld = tid & (kChunks - 1);
   const u32x4 *pa[kLoads];
-  const u32x4 *pb[kLoads];
-  bool va[kLoads], vb[kLoads];
+  const u32x4 *pb[kLoadsB];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = (tid + i * kGemmThreads) / kChunks;
-    va[i] = r < rows;
-    vb[i] = n0 + r < N;
-    pa[i] = X + (int64_t)(row0 + (va[i] ? r : 0)) * KV + c_ld;
-    pb[i] = Wm + (int64_t)(vb[i] ? n0 + r : 0) * KV + c_ld;
+    pa[i] = X + (int64_t)(row0 + (r < rows ? r : rows - 1)) * KV + c_ld;
   }
-  u32x4 ra[kLoads], rb[kLoads];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      ra[i] = va[i] ? pa[i][kt * kChunks] : zero;
-      rb[i] = vb[i] ? pb[i][kt * kChunks] : zero;
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int r = (tid + i * kGemmThreads) / kChunks;
-      sa[buf][swz(r, c_ld)] = ra[i];
-      sb[buf][swz(r, c_ld)] = rb[i];
-    }
-  };
+  for (int i = 0; i < kLoadsB; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    pb[i] = Wm + (int64_t)(n0 + r < N ? n0 + r : N - 1) * KV + c_ld;
+  }
+  u32x4 ra0[kLoads], rb0[kLoadsB];
 
-  f32x16 acc[2][2];
+#define GLOAD(RA, RB, kt)                                                              \
+  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) RA[i] = pa[i][(kt) * kChunks];    \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i) RB[i] = pb[i][(kt) * kChunks];
+#define SWRITE(RA, RB, buf)                                                                 \
+  _Pragma("unroll") for (int i = 0; i < kLoads; ++i)                                        \
+      sa[buf][swz((tid + i * kGemmThreads) / kChunks, c_ld)] = RA[i];                       \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i)                                       \
+      sb[buf][swz((tid + i * kGemmThreads) / kChunks, c_ld)] = RB[i];
+
+  f32x16 acc[kFM][kFN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kFN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // One 16-deep step of fragments is read from LDS while the MFMAs of the
+  // previous step run (two small register sets); the first step of slab
+  // kt+1 is read right after the barrier that publishes it, under the last
+  // MFMAs of slab kt.  The global loads of slab kt+2 are in flight during
+  // all of slab kt+1.
+#define READK(FA, FB, buf, kk)                                                                      \
+  {                                                                                                 \
+    const int c_ = (kk) * 2 + (lane >> 5);                                                          \
+    _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                                 \
+        FA[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(wm * kWTM + i * 32 + (lane & 31), c_)]);     \
+    _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                                 \
+        FB[j] = __builtin_bit_cast(bf16x8, sb[buf][swz(wn * kWTN + j * 32 + (lane & 31), c_)]);     \
+  }
+#define MFMAK(FA, FB)                                                                               \
+  _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                                   \
+  _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                                   \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
+
+  static_assert(kBK == 64, "four 16-deep steps per slab");
   const int KT = K / kBK;
-  gload(0);
-  swrite(0);
+  bf16x8 fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
+  GLOAD(ra0, rb0, 0);
+  SWRITE(ra0, rb0, 0);
+  if (KT > 1) { GLOAD(ra0, rb0, 1); }
   __syncthreads();
+  READK(fa0, fb0, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);  // this lane's 8 K-values of the 16
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + (lane & 31);
-        fa[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(row, c)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wn * 64 + j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8, sb[buf][swz(n, c)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    READK(fa1, fb1, buf, 1);
+    MFMAK(fa0, fb0);
+    READK(fa0, fb0, buf, 2);
+    MFMAK(fa1, fb1);
+    READK(fa1, fb1, buf, 3);
+    MFMAK(fa0, fb0);
+    if (kt + 1 < KT) {
+      SWRITE(ra0, rb0, buf ^ 1);
+      if (kt + 2 < KT) { GLOAD(ra0, rb0, kt + 2); }
+      __syncthreads();
+      READK(fa0, fb0, buf ^ 1, 0);
     }
-    if (kt + 1 < KT) swrite(buf ^ 1);
-    __syncthreads();
+    MFMAK(fa1, fb1);
   }
+#undef READK
+#undef MFMAK
+#undef GLOAD
+#undef SWRITE
 
   // accumulator r of a lane: row (r / 4) * 8 + (lane / 32) * 4 + r % 4, column lane % 32
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < kFN; ++j) {
+      const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);  // rows row, row + 1
         if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
         if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
@@ -232,7 +261,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
 
 int32_t gemm_max_tiles(const Geometry &g) {
   const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
-  return (int32_t)((g.n + kGemmBM - 1) / kGemmBM + groups);
+  return (int32_t)((g.n + kTileM - 1) / kTileM + groups);
 }
 
 hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
