@@ -56,8 +56,10 @@ def test_route_workloads(name, rho):
     assert np.array_equal(gi, inp.topk_idx)          # the routing the workloads were drawn with
 
 
+# up to 1024 tokens a token takes a whole wave, above that a 16-lane row
 @pytest.mark.parametrize("T,E,k", [(777, 1024, 16), (300, 384, 8), (129, 65, 3), (50, 5, 7),
-                                   (33, 1, 1), (0, 16, 4), (1000, 64, 1)])
+                                   (33, 1, 1), (0, 16, 4), (1000, 64, 1), (1024, 256, 8),
+                                   (1025, 65, 3), (2000, 1024, 16), (1500, 5, 7), (3001, 1, 1)])
 def test_route_shapes_and_ties(T, E, k):
     rng = np.random.default_rng(T * 7 + E)
     lg = rng.standard_normal((T, E)).astype(np.float32)
