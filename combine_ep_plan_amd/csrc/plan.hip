@@ -67,6 +67,12 @@ __device__ __forceinline__ int32_t last_le(const int32_t *a, int32_t n, int32_t 
   return lo;
 }
 
+// Wait until this wave's global stores have reached L2 (s_waitcnt vmcnt(0);
+// lgkmcnt and expcnt fields left at their no-wait maxima).  A workgroup
+// barrier on gfx950 does not wait for them, so every wave does this before
+// the barrier that precedes a release by one wave of the workgroup.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Receive row of an entry of expert e at position pos among e's entries.
 __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace &ws,
                                              const int32_t *offs, int32_t e, int32_t pos) {
@@ -330,12 +336,14 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   }
 
   if (!single) {
-    // Publish this tile; the last one to arrive finishes the layout.  The
-    // barrier waits for every wave's stores; then a single wave makes them
-    // visible to the other XCDs (agent-scope release: one L2 write-back per
-    // workgroup, not one per wave) and takes a ticket.  The last workgroup's
-    // agent-scope acquire (one invalidate) lets all its waves see every tile.
+    // Publish this tile; the last one to arrive finishes the layout.  Every
+    // wave waits for its own stores to reach L2, the barrier joins them, then
+    // a single wave makes them visible to the other XCDs (agent-scope release:
+    // one L2 write-back per workgroup, not one per wave) and takes a ticket.
+    // The last workgroup's agent-scope acquire (one invalidate) lets all its
+    // waves see every tile.
     if (tid == 0) ws.tile_flags[blockIdx.x] = s_flags;
+    wait_stores();
     __syncthreads();
     if (tid == 0) {
       __threadfence();

@@ -186,8 +186,9 @@ ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
 
 /* Create a per-pass handle (NCCL EP listing, Table II: handles) over a
  * caller-owned device workspace of `workspace_bytes` bytes, 256-byte
- * aligned, whose first 256 bytes are zero when the handle is created (every
- * ep_plan leaves them zero again).  Host bookkeeping only: nothing is
+ * aligned, whose first 256 bytes are zero when the handle is created (the
+ * status word then holds the EP_FLAG_* bits of each call; ep_plan returns
+ * its workgroup ticket to zero).  Host bookkeeping only: nothing is
  * enqueued.  Errors: EP_ERR_INVALID_ARG (NULL, misaligned, num_tokens < 0 or
  * > max_tokens), EP_ERR_WORKSPACE_TOO_SMALL. */
 ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,

@@ -54,6 +54,9 @@ CASES = [
     ("exact_tile", 512, 32, 256, 8, "static", 0, 32, 8, 0.0, 0.0, 0.0, 1.1, 14),
     ("one_full_tile", 256, 40, 64, 8, "ht", 0, 8, 0, 0.0, 0.0, 0.0, 1.0, 15),
     ("ll_multi_tile_masked", 700, 48, 96, 8, "ll", 90, 8, 0, 0.08, 0.01, 0.0, 1.3, 16),
+    # 274 layout tiles: the finishing workgroup scans hundreds of tile histograms
+    ("many_tiles_ht", 70000, 8, 64, 8, "ht", 0, 8, 0, 0.02, 0.0, 0.0, 1.0, 17),
+    ("many_tiles_static", 70000, 8, 64, 8, "static", 0, 8, 4, 0.0, 0.0, 0.0, 1.5, 18),
 ]
 
 
