@@ -3,7 +3,9 @@
 // (the backward of dispatch) and the backward of combine (NCCL EP listing,
 // Figure 5: the forward pass's routing state is reused), on gfx950.
 //
-// One workgroup per token.  Each lane owns 8 channels (one 16-byte vector)
+// One workgroup per token (per piece of the row for small batches, as in
+// dispatch; combine backward keeps whole rows for its grad_w reduction).
+// Each lane owns 8 channels (one 16-byte vector)
 // and keeps all k gathers of its vector in flight before reducing them in
 // fp32 in ascending j, so the k rows of a token cost one HBM read each and
 // the output one HBM write.
@@ -19,7 +21,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
                                                          const int32_t *__restrict__ dst,
                                                          const float *__restrict__ w,
                                                          void *__restrict__ out, int64_t nrows,
-                                                         int32_t V, int32_t kr) {
+                                                         int32_t V, int32_t kr, int32_t chunk) {
   constexpr int KN = K > 0 ? K : kMaxTopK;
   const int64_t t = blockIdx.x;
   const int32_t k = K > 0 ? K : kr;
@@ -32,7 +34,9 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
     if (d[j] >= nrows) d[j] = -1;
     wj[j] = (WEIGHTED && on) ? w[t * k + j] : 1.0f;
   }
-  for (int32_t v = threadIdx.x; v < V; v += kRowThreads) {
+  const int32_t lo = blockIdx.y * chunk;
+  const int32_t hi = lo + chunk < V ? lo + chunk : V;
+  for (int32_t v = lo + threadIdx.x; v < hi; v += kRowThreads) {
     u32x4 r[KN];
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
@@ -130,9 +134,11 @@ hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t
   if (g.T == 0) return hipSuccess;
   const int32_t V = H / 8;
   const u32x4 *r = reinterpret_cast<const u32x4 *>(rows);
-#define L4(KK, WT, OF)                                                                  \
-  hipLaunchKernelGGL((k_combine<KK, WT, OF>), dim3(g.T), dim3(kRowThreads), 0, s, r,   \
-                     ws.dst, topk_w, out, g.rows, V, g.k)
+  int32_t chunk = V;
+  const int32_t pieces = row_pieces(g.T, V, &chunk);
+#define L4(KK, WT, OF)                                                                        \
+  hipLaunchKernelGGL((k_combine<KK, WT, OF>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, r, \
+                     ws.dst, topk_w, out, g.rows, V, g.k, chunk)
 #define L(KK)                           \
   do {                                  \
     if (topk_w) {                       \

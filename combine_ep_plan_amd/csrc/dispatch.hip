@@ -4,7 +4,8 @@
 // quantised to FP8 e4m3 with one fp32 scale per 128 channels (NCCL EP
 // listing, Table IV: FP8 scales travel with the tokens).
 //
-// One workgroup per token: the row is read once with 16-byte loads and
+// One workgroup per token (per piece of a token's row when there are too
+// few tokens to fill the GPU): the row is read once with 16-byte loads and
 // written to each of its k destinations with 16-byte streaming stores, so
 // x costs one HBM read and every receive row one HBM write.
 #include "device.h"
@@ -15,22 +16,40 @@ namespace epk {
 constexpr int kRowThreads = 512;
 constexpr int kUnroll = 2;
 
+// Pieces per row: small batches (decode) split each row over several
+// workgroups, so the grid reaches about kSplitTarget workgroups; pieces are
+// whole 128-channel blocks (16 vectors), as FP8 scales need.
+constexpr int64_t kSplitTarget = 1024;
+
+int32_t row_pieces(int32_t T, int32_t V, int32_t *chunk) {
+  int64_t want = T > 0 ? (kSplitTarget + T - 1) / T : 1;
+  const int64_t most = (V + 15) / 16;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  int32_t c = (int32_t)((V + want - 1) / want);
+  c = (c + 15) / 16 * 16;
+  *chunk = c;
+  return (V + c - 1) / c;
+}
+
 template <int K>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__restrict__ x,
                                                                const int32_t *__restrict__ dst,
                                                                u32x4 *__restrict__ recv,
                                                                int64_t rows, int32_t V,
-                                                               int32_t kr) {
+                                                               int32_t kr, int32_t chunk) {
   const int64_t t = blockIdx.x;
   const int32_t k = K > 0 ? K : kr;
   const int32_t *dt = dst + t * k;
   const u32x4 *xr = x + t * V;
-  for (int32_t v0 = threadIdx.x; v0 < V; v0 += kRowThreads * kUnroll) {
+  const int32_t lo = blockIdx.y * chunk;
+  const int32_t hi = lo + chunk < V ? lo + chunk : V;
+  for (int32_t v0 = lo + threadIdx.x; v0 < hi; v0 += kRowThreads * kUnroll) {
     u32x4 val[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int32_t v = v0 + u * kRowThreads;
-      if (v < V) val[u] = xr[v];
+      if (v < hi) val[u] = xr[v];
     }
 #pragma unroll
     for (int j = 0; j < (K > 0 ? K : kMaxTopK); ++j) {
@@ -41,7 +60,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__re
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int32_t v = v0 + u * kRowThreads;
-        if (v < V) store_stream(o + v, val[u]);
+        if (v < hi) store_stream(o + v, val[u]);
       }
     }
   }
@@ -57,12 +76,15 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
                                                               u32x2 *__restrict__ recv_q,
                                                               float *__restrict__ recv_s,
                                                               int64_t rows, int32_t V,
-                                                              int32_t kr) {
+                                                              int32_t kr, int32_t chunk) {
   const int64_t t = blockIdx.x;
   const int32_t k = K > 0 ? K : kr;
   const int32_t *dt = dst + t * k;
   const int32_t nb = V >> 4;
-  for (int32_t v = threadIdx.x; v < V; v += kRowThreads) {
+  // pieces are whole 16-vector blocks, so a block's 16 lanes are all in or all out
+  const int32_t lo = blockIdx.y * chunk;
+  const int32_t hi = lo + chunk < V ? lo + chunk : V;
+  for (int32_t v = lo + threadIdx.x; v < hi; v += kRowThreads) {
     float f[8];
     unpack8(x[t * V + v], f);
     float amax = 0.0f;
@@ -118,10 +140,12 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
                                 int32_t H, uint16_t *recv, hipStream_t s) {
   if (g.T == 0) return hipSuccess;
   const int32_t V = H / 8;
+  int32_t chunk = V;
+  const int32_t pieces = row_pieces(g.T, V, &chunk);
 #define L(KK)                                                                          \
-  hipLaunchKernelGGL(k_dispatch_bf16<KK>, dim3(g.T), dim3(kRowThreads), 0, s,         \
+  hipLaunchKernelGGL(k_dispatch_bf16<KK>, dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
-                     reinterpret_cast<u32x4 *>(recv), g.rows, V, g.k)
+                     reinterpret_cast<u32x4 *>(recv), g.rows, V, g.k, chunk)
   EP_K_SWITCH(g.k, L)
 #undef L
   return hipGetLastError();
@@ -131,11 +155,13 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
                                int32_t H, uint8_t *recv_q, float *recv_scale, hipStream_t s) {
   if (g.T == 0) return hipSuccess;
   const int32_t V = H / 8;
+  int32_t chunk = V;
+  const int32_t pieces = row_pieces(g.T, V, &chunk);
 #define L(KK)                                                                          \
-  hipLaunchKernelGGL(k_dispatch_fp8<KK>, dim3(g.T), dim3(kRowThreads), 0, s,          \
+  hipLaunchKernelGGL(k_dispatch_fp8<KK>, dim3(g.T, pieces), dim3(kRowThreads), 0, s,  \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
-                     reinterpret_cast<u32x2 *>(recv_q), recv_scale, g.rows, V,   \
-                     g.k)
+                     reinterpret_cast<u32x2 *>(recv_q), recv_scale, g.rows, V,        \
+                     g.k, chunk)
   EP_K_SWITCH(g.k, L)
 #undef L
   return hipGetLastError();

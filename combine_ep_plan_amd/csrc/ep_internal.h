@@ -57,6 +57,10 @@ struct Geometry {
   int64_t rows;     // receive rows
 };
 
+// Pieces each token row is split into by dispatch and combine (small batches
+// spread one row over several workgroups); *chunk = 16-byte vectors per piece.
+int32_t row_pieces(int32_t T, int32_t V, int32_t *chunk);
+
 // Byte size of the workspace for `g` (base == nullptr) or carve it (base != nullptr).
 size_t carve_workspace(const Geometry &g, char *base, Workspace *ws);
 size_t plan_lds_bytes(int32_t E, int32_t R);
