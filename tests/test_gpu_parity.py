@@ -263,3 +263,31 @@ def test_identity_experts_roundtrip_small():
     recv, _, _, _, _ = buf.dispatch(x, dev_i32(c["idx"]), dev_f32(c["w"]), handle=h)
     y = buf.combine(recv, h, dev_f32(c["w"]))
     assert same_up_to_zero_sign_np(host_bits(y), c["x"])
+
+
+def test_deterministic_on_two_streams():
+    # the whole chain on two streams at once, each with its own handle: every
+    # output bit-identical (no atomics order any result)
+    c = _case(CASES[5])
+    g = make_group(c["E"], c["R"], c["H"], c["k"], c["T"], c["kind"], c["cap"], c["S"])
+    buf = ep.Buffer(g)
+    x, idx, w = dev_bf16(c["x"]), dev_i32(c["idx"]), dev_f32(c["w"])
+    gy = dev_bf16(workloads.f32_to_bf16_bits(
+        np.random.default_rng(3).standard_normal((c["T"], c["H"])).astype(np.float32)))
+    torch.cuda.synchronize()
+    outs = []
+    for st in (torch.cuda.Stream(), torch.cuda.Stream()):
+        with torch.cuda.stream(st):
+            h = ep.Handle(g, c["T"])
+            h.plan(idx, st)
+            recv, _, _, _, _ = buf.dispatch(x, idx, w, handle=h, recv_meta=False, stream=st)
+            y = buf.combine(recv, h, w, stream=st)
+            gout, gw = buf.combine_bwd(gy, recv, w, h, stream=st)
+            gx = buf.dispatch_bwd(gout, h, stream=st)
+            outs.append((h, recv, y, gout, gw, gx))
+    torch.cuda.synchronize()
+    a, b = outs
+    assert np.array_equal(host(a[0].tables()["dst"]), host(b[0].tables()["dst"]))
+    for u, v in zip(a[1:], b[1:]):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)

@@ -200,3 +200,17 @@ def test_training_fwd_bwd_and_dup_reduce():
     assert np.array_equal(host(owner[hot]).reshape(1, -1), want)
     assert float(owner[(hot + 1) % c.E].abs().max()) == 0.0
     assert h.status() == 0
+
+
+@pytest.mark.parametrize("name,s", [(n, s) for n in ("tiny", "decode", "prefill", "sweep", "training")
+                                    for s in (1, 2)])
+def test_workload_other_seeds(name, s):
+    # seeds 1 and 2 of every workload: layout and plan in full, dispatch in
+    # full, combine on sampled tokens
+    inp = workloads.make_inputs(name, s, 8.0) if name == "sweep" else workloads.make_inputs(name, s)
+    c = inp.cfg
+    g, h, buf, x, idx, w, recv, L = _run_forward(inp)
+    check_layout(h, L, c.layout, inp.topk_idx, inp.topk_w)
+    _check_dispatch_full(inp, recv, L, x)
+    y = buf.combine(recv, h, w, out_dtype=torch.float32 if c.out_fp32 else torch.bfloat16)
+    _check_combine_sampled(inp, L, recv, y, inp.topk_w, n=256, out_fp32=c.out_fp32)
