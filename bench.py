@@ -55,6 +55,9 @@ def parse():
                         "[rows, H] bf16 tokens times one [N, H] bf16 matrix per expert (through "
                         "the prefetch slots with --prefetch); reported beside the step, its "
                         "roofline against the bf16 MFMA peak")
+    p.add_argument("--graph", action="store_true",
+                   help="time the step as one captured HIP graph (replayed K times) instead of "
+                        "K eager launches of each call; per-kernel times stay eager")
     p.add_argument("--cold", action="store_true",
                    help="write a 512 MB buffer before every step (Infinity Cache flushed); "
                         "steps are then timed one by one")
@@ -223,12 +226,13 @@ def main():
         rep_e = torch.zeros(2, dtype=torch.int32, device=dev)   # replicas of expert 0, same owner
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if a.cold else None
 
+    LS = {"s": stream}   # the stream the library calls launch on (a capture stream under --graph)
     ops = []
     if a.route:   # the pass starts from router logits: plan and combine use the routed outputs
         logits = torch.from_numpy(inp.logits).to(dev)
         idx, w = torch.empty_like(idx), torch.empty_like(w)
-        ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, stream)))
-    ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, stream)))
+        ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, LS["s"])))
+    ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, LS["s"])))
     slot_elems = a.gemm * c.H if a.gemm else PREFETCH_P
     slots = None
     if a.gemm:   # one [N, H] projection per expert, the GEMM's weights
@@ -239,23 +243,23 @@ def main():
         wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
     if a.prefetch:
         slots = torch.empty((c.R, S) + tuple(wts.shape[1:]), dtype=torch.bfloat16, device=dev)
-        ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, stream)))
+        ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, LS["s"])))
     if a.fp8:
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
         ep.ep_plan(h.ptr, idx, stream)
         ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)
-        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, stream)))
+        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, LS["s"])))
     else:
-        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)))
+        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, LS["s"])))
     if a.gemm:
         gy_out = torch.empty((h.recv_rows, a.gemm), dtype=torch.bfloat16, device=dev)
         recv2d = recv.view(h.recv_rows, c.H)
-        ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, stream)))
-    ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, stream)))
+        ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"])))
+    ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, LS["s"])))
     if train:
-        ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, stream)))
-        ops.append(("dispatch_bwd", lambda: ep.ep_combine(h.ptr, gout, None, gx, stream)))
-        ops.append(("dup_reduce", lambda: ep.ep_dup_grad_reduce(h.ptr, rep, rep_e, owner, stream)))
+        ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, LS["s"])))
+        ops.append(("dispatch_bwd", lambda: ep.ep_combine(h.ptr, gout, None, gx, LS["s"])))
+        ops.append(("dup_reduce", lambda: ep.ep_dup_grad_reduce(h.ptr, rep, rep_e, owner, LS["s"])))
 
     def step():
         for _, f in ops:
@@ -266,6 +270,24 @@ def main():
     torch.cuda.synchronize()
     assert h.status() == 0, "device flags raised on the benchmark input"
 
+    graph = None
+    if a.graph:   # the whole step as one HIP graph, replayed (no host launch cost per kernel)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            LS["s"] = torch.cuda.current_stream()
+            step()
+        LS["s"] = stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert h.status() == 0, "device flags raised on the benchmark input (graph replay)"
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
     # timed region 1: the whole step, back to back (or one by one when --cold)
     K = a.steps
     if not a.cold:
@@ -275,7 +297,7 @@ def main():
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]
         e0.record(stream)
         for i in range(K):
-            step()
+            run_step()
             if i < K - 1:
                 marks[i].record(stream)
         e1.record(stream)
@@ -293,7 +315,7 @@ def main():
             flush.fill_(1)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            step()
+            run_step()
             e1.record(stream)
             torch.cuda.synchronize()
             tot += e0.elapsed_time(e1)
@@ -366,7 +388,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
-                   "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route},
+                   "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route,
+                   "hip_graph": a.graph},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
         **({"gemm": gemm_info} if gemm_info else {}),
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
