@@ -350,13 +350,23 @@ def main():
         else:
             grows = int(tb["offsets"][-1])   # every routed entry is one row of some group
         flops = 2.0 * grows * a.gemm * c.H
-        ab["gemm"] = grows * c.H * 2 + c.E * a.gemm * c.H * 2 + grows * a.gemm * 2   # X, W, Y once
+        # X, every weight matrix some row uses (experts with rows, plus the
+        # prefetch slots the segments read) and Y, once each
+        mats = int((tb["counts"] > 0).sum()) + (filled if a.prefetch else 0)
+        ab["gemm"] = grows * c.H * 2 + mats * a.gemm * c.H * 2 + grows * a.gemm * 2
         tflops = flops / (per_us["gemm"] * 1e-6) / 1e12
-        gemm_info = {"N": a.gemm, "K": c.H, "rows": grows, "flops": flops,
-                     "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1),
-                     "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
-                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+        gemm_info = {"N": a.gemm, "K": c.H, "rows": grows, "weight_matrices": mats, "flops": flops,
+                     "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1)}
+        # the binding resource: MFMA time of the flops or HBM time of the bytes
+        if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) >= ab["gemm"] / (HBM_PEAK_GBPS * 1e9):
+            gemm_info["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
+                                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            gbps = ab["gemm"] / (per_us["gemm"] * 1e-6) / 1e9
+            gemm_info["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),
+                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     chain_bytes = sum(ab[nm] for nm, _ in ops)
     step_s = step_ms / 1000.0
     dom = max((nm for nm in ("dispatch", "combine", "combine_bwd") if nm in per_us),
