@@ -76,6 +76,7 @@ def _L():
             "orc_dup_reduce": (None, [i32, i64, P, P, i32, P]),
             "orc_route": (None, [i32, i32, i32, P, P, P]),
             "orc_grouped_gemm": (None, [i32, P, i32, i32, P, P, P]),
+            "orc_grouped_gemm_fp8": (None, [i32, P, i32, i32, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -371,6 +372,41 @@ def grouped_gemm(x_bits: np.ndarray, w_bits: np.ndarray, groups: np.ndarray,
         raise ValueError("grouped_gemm: a group is outside X or names no weight matrix")
     y = np.zeros((x.shape[0], N), np.uint16) if y_bits is None else np.array(y_bits, np.uint16, copy=True, order="C")
     _L().orc_grouped_gemm(gr.shape[0], _p(gr), K, N, _p(x), _p(w), _p(y))
+    return y
+
+
+def quantize_rows_fp8(bits: np.ndarray):
+    """Every row of a bf16 matrix (last axis a multiple of 128) quantised as
+    ep_dispatch's FP8 path does: e4m3 codes and one fp32 scale per 128."""
+    b = _c(bits, np.uint16)
+    H = b.shape[-1]
+    flat = b.reshape(-1, H)
+    q = np.zeros(flat.shape, np.uint8)
+    s = np.zeros((flat.shape[0], H // 128), np.float32)
+    for r in range(flat.shape[0]):
+        q[r], s[r] = quantize_row_fp8(flat[r])
+    return q.reshape(b.shape), s.reshape(b.shape[:-1] + (H // 128,))
+
+
+def grouped_gemm_fp8(x_codes: np.ndarray, x_scales: np.ndarray, w_codes: np.ndarray,
+                     w_scales: np.ndarray, groups: np.ndarray,
+                     y_bits: np.ndarray | None = None) -> np.ndarray:
+    """The grouped GEMM on FP8 operands: codes (e4m3) with one fp32 scale per
+    128 of K, for the rows ([rows, K], [rows, K/128]) and for every output row
+    of every weight matrix ([nW, N, K], [nW, N, K/128])."""
+    x = _c(x_codes, np.uint8)
+    sx = _c(x_scales, np.float32)
+    w = _c(w_codes, np.uint8)
+    sw = _c(w_scales, np.float32)
+    nW, N, K = w.shape
+    if K % 128 or x.shape[1] != K or sx.shape != (x.shape[0], K // 128) or sw.shape != (nW, N, K // 128):
+        raise ValueError("grouped_gemm_fp8: inconsistent shapes")
+    gr = _c(groups, np.int32).reshape(-1, 3)
+    if gr.size and (gr[:, 0].min() < 0 or (gr[:, 0] + gr[:, 1]).max() > x.shape[0]
+                    or gr[:, 2].min() < 0 or gr[:, 2].max() >= nW):
+        raise ValueError("grouped_gemm_fp8: a group is outside X or names no weight matrix")
+    y = np.zeros((x.shape[0], N), np.uint16) if y_bits is None else np.array(y_bits, np.uint16, copy=True, order="C")
+    _L().orc_grouped_gemm_fp8(gr.shape[0], _p(gr), K, N, _p(x), _p(sx), _p(w), _p(sw), _p(y))
     return y
 
 

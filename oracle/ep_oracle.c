@@ -652,6 +652,45 @@ void orc_grouped_gemm(int32_t ngroups, const int32_t *groups, int32_t K, int32_t
   }
 }
 
+/*
+ * The same grouped GEMM on FP8 operands: the receive rows as ep_dispatch's
+ * FP8 path leaves them ([NCCLEP] Table IV: e4m3 codes with one fp32 scale
+ * per 128 channels) and weights in the same format, one scale per output
+ * row n and 128-wide block of K.  READING: a code stands for code * scale,
+ * so, for every group g = (row0, rows, widx), row i and column n,
+ *   Y[row0 + i][n] = bf16( sum_b SX[row0 + i][b] * SW[widx][n][b] *
+ *                          sum_{c in block b} X[row0 + i][c] * W[widx][n][c] )
+ * with the codes decoded exactly (OCP e4m3), all sums in double and one
+ * rounding to bf16.
+ *   X  [.][K] e4m3, SX [.][K/128] fp32; W [.][N][K] e4m3, SW [.][N][K/128] fp32
+ */
+void orc_grouped_gemm_fp8(int32_t ngroups, const int32_t *groups, int32_t K, int32_t N,
+                          const uint8_t *X, const float *SX, const uint8_t *W, const float *SW,
+                          uint16_t *Y) {
+  const int32_t nb = K / 128;
+  for (int32_t g = 0; g < ngroups; ++g) {
+    const int64_t row0 = groups[g * 3 + 0], rows = groups[g * 3 + 1], widx = groups[g * 3 + 2];
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < rows; ++i) {
+      const uint8_t *x = X + (row0 + i) * K;
+      const float *sx = SX + (row0 + i) * nb;
+      for (int32_t n = 0; n < N; ++n) {
+        const uint8_t *w = W + (widx * N + n) * (int64_t)K;
+        const float *sw = SW + (widx * N + n) * (int64_t)nb;
+        double acc = 0.0;
+        for (int32_t b = 0; b < nb; ++b) {
+          double part = 0.0;
+          for (int32_t c = b * 128; c < (b + 1) * 128; ++c)
+            part += orc_e4m3_to_double(x[c]) * orc_e4m3_to_double(w[c]);
+          acc += (double)sx[b] * (double)sw[b] * part;
+        }
+        Y[(row0 + i) * N + n] = orc_bf16_from_double(acc);
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* top-k routing                                                             */
 /* ------------------------------------------------------------------------ */

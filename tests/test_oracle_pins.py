@@ -729,3 +729,116 @@ def test_expert_groups_cover_every_routed_row_once_with_its_expert(kind):
         assert np.array_equal(owner, np.where(ridx >= 0, ridx, -1))   # exactly the used rows
         if kind == "static" and use_slots:
             assert np.any(groups[:, 2] >= E) and np.any(L.plan.seg_slot < 0)
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM on FP8 operands
+# ---------------------------------------------------------------------------
+
+def _runs(tokens: list[str]) -> np.ndarray:
+    out = []
+    for t in tokens:
+        n, c = t.split("*")
+        out += [int(c, 0)] * int(n)
+    return np.array(out, np.uint8)
+
+
+def _numbered(g: dict, key: str) -> np.ndarray:
+    rows, i = [], 0
+    while f"{key}{i}" in g:
+        rows.append(_runs(g[f"{key}{i}"]))
+        i += 1
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("case", ["A", "B", "C"])
+def test_grouped_gemm_fp8_golden(case):
+    g = read_golden("gemm_fp8_small.txt")[case]
+    K, N = int(g["K"][0]), int(g["N"][0])
+    x = _numbered(g, "X")
+    w = _numbered(g, "W").reshape(-1, N, K)
+    assert x.shape[1] == K
+    sx = floats(g["SX"]).astype(np.float32).reshape(x.shape[0], K // 128)
+    sw = floats(g["SW"]).astype(np.float32).reshape(w.shape[0], N, K // 128)
+    groups = ints(g["groups"]).reshape(-1, 3)
+    y0 = None
+    if "Yinit" in g:
+        y0 = _bits(np.full((x.shape[0], N), float(g["Yinit"][0])))
+    y = oracle.grouped_gemm_fp8(x, sx, w, sw, groups, y0)
+    assert bf16_bits_to_f32(y).ravel().tolist() == floats(g["Y"]).tolist()
+
+
+def _torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _finite_codes(rng, shape) -> np.ndarray:
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3F     # 0x7F / 0xFF are NaN in e4m3; the quantiser never makes them
+    return c
+
+
+def test_grouped_gemm_fp8_random_is_the_exact_sum_rounded_once():
+    # power-of-two scales: every product and every partial sum is exact in
+    # float64 (8-bit products over 2^-18 .. 2^25), so numpy's matmul over the
+    # codes decoded by torch gives the exact value; round it once, exactly
+    rng = np.random.default_rng(51)
+    K, N, rows, nW = 384, 20, 45, 3
+    x = _finite_codes(rng, (rows, K))
+    w = _finite_codes(rng, (nW, N, K))
+    sx = np.ldexp(1.0, rng.integers(-6, 7, (rows, K // 128))).astype(np.float32)
+    sw = np.ldexp(1.0, rng.integers(-6, 7, (nW, N, K // 128))).astype(np.float32)
+    groups = np.array([[0, 17, 2], [17, 3, 0], [25, 20, 1]], np.int32)   # rows 20..24 uncovered
+    y0 = _bits(np.full((rows, N), -3.0))
+    y = oracle.grouped_gemm_fp8(x, sx, w, sw, groups, y0)
+    xd, wd = _torch_e4m3(x), _torch_e4m3(w)
+    want = y0.copy()
+    for r0, n, wi in groups:
+        acc = np.zeros((n, N))
+        for b in range(K // 128):
+            cs = slice(b * 128, (b + 1) * 128)
+            acc += (xd[r0:r0 + n, cs] @ wd[wi][:, cs].T) * sx[r0:r0 + n, b][:, None] * sw[wi][:, b][None, :]
+        want[r0:r0 + n] = [[exact_round_bf16(Fraction(float(v))) for v in row] for row in acc]
+    assert np.array_equal(y, want)
+
+
+def test_grouped_gemm_fp8_unit_scales_is_the_bf16_gemm_of_the_decoded_codes():
+    # every e4m3 value is exact in bf16, so with all scales 1 the FP8 GEMM is
+    # the bf16 GEMM of the decoded values
+    rng = np.random.default_rng(52)
+    K, N, rows = 256, 16, 30
+    x = _finite_codes(rng, (rows, K))
+    w = _finite_codes(rng, (2, N, K))
+    groups = np.array([[0, 10, 1], [10, 20, 0]], np.int32)
+    y = oracle.grouped_gemm_fp8(x, np.ones((rows, 2), np.float32), w, np.ones((2, N, 2), np.float32), groups)
+    xb = _bits(_torch_e4m3(x).astype(np.float32))
+    wb = _bits(_torch_e4m3(w).astype(np.float32))
+    assert np.array_equal(same_sign_zero(y), same_sign_zero(oracle.grouped_gemm(xb, wb, groups)))
+
+
+def test_grouped_gemm_fp8_of_quantised_operands_tracks_the_bf16_gemm():
+    # rows and weights quantised the way the FP8 dispatch does it: the result
+    # stays within e4m3's relative precision (3 mantissa bits) of the bf16 GEMM
+    rng = np.random.default_rng(53)
+    K, N, rows = 512, 32, 64
+    xb = _bits(rng.standard_normal((rows, K)) * np.exp(rng.standard_normal((rows, 1))))
+    wb = _bits(rng.standard_normal((2, N, K)) / np.sqrt(K))
+    qx, sx = oracle.quantize_rows_fp8(xb)
+    qw, sw = oracle.quantize_rows_fp8(wb)
+    assert qx.shape == (rows, K) and sx.shape == (rows, K // 128) and sw.shape == (2, N, K // 128)
+    groups = np.array([[0, 40, 0], [40, 24, 1]], np.int32)
+    y = bf16_bits_to_f32(oracle.grouped_gemm_fp8(qx, sx, qw, sw, groups)).astype(np.float64)
+    ref = bf16_bits_to_f32(oracle.grouped_gemm(xb, wb, groups)).astype(np.float64)
+    assert rel_err(y, ref) < 0.06
+    assert float(y.ravel() @ ref.ravel()) / (np.linalg.norm(y) * np.linalg.norm(ref)) > 0.995
+
+
+def test_grouped_gemm_fp8_rejects_bad_shapes():
+    x = np.zeros((4, 192), np.uint8)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_fp8(x, np.ones((4, 1), np.float32), np.zeros((1, 2, 192), np.uint8),
+                                np.ones((1, 2, 1), np.float32), np.array([[0, 4, 0]], np.int32))
+    x = np.zeros((4, 128), np.uint8)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_fp8(x, np.ones((4, 1), np.float32), np.zeros((1, 2, 128), np.uint8),
+                                np.ones((1, 2, 1), np.float32), np.array([[2, 4, 0]], np.int32))
