@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak), T=4096 H=7168 top-8"
 
 
@@ -40,7 +41,10 @@ def parse():
     p.add_argument("--workload", default="prefill",
                    choices=["prefill", "decode", "tiny", "sweep", "training"])
     p.add_argument("--rho", type=float, default=8.0, help="sweep: max/mean expert load")
-    p.add_argument("--fp8", action="store_true", help="decode: FP8 e4m3 dispatch")
+    p.add_argument("--fp8", action="store_true",
+                   help="FP8 e4m3 dispatch (one fp32 scale per 128 channels); with --gemm the "
+                        "grouped GEMM takes the FP8 rows and FP8 weights (roofline against the "
+                        "fp8 MFMA peak)")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
     p.add_argument("--prefetch", action="store_true",
@@ -71,7 +75,7 @@ def parse():
 PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
 
 
-def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P):
+def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P, slot_elem_bytes=2):
     """Bytes each kernel must move by definition: x read once, every routed row
     written once and read once, outputs written once, int32/fp32 metadata."""
     N = c.T * c.k
@@ -87,7 +91,8 @@ def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P):
         b["dispatch_bwd"] = N * row + N * 4 + c.T * row
         P = 4096 * 1536
         b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
-    b["prefetch"] = filled_slots * slot_elems * 2 * 2            # each filled slot: owner row read, slot written
+    b["prefetch"] = filled_slots * slot_elems * slot_elem_bytes * 2   # each filled slot: owner row read, slot written
+    b["prefetch_scales"] = filled_slots * (slot_elems // 128) * 4 * 2  # FP8 weights: their fp32 scales
     return b
 
 
@@ -241,9 +246,21 @@ def main():
         wts = (torch.randn((c.E, a.gemm, c.H), generator=gen, device=dev) * c.H ** -0.5).to(torch.bfloat16)
     elif a.prefetch:
         wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
+    gemm_fp8 = bool(a.gemm and a.fp8)
+    if gemm_fp8:   # the weights quantised like the rows: e4m3 codes, one scale per 128 of K
+        wf = wts.float().view(c.E, a.gemm, c.H // 128, 128)
+        amax = wf.abs().amax(-1)
+        wsc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).contiguous()
+        wts = (wf / wsc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(c.E, a.gemm, c.H)
+        del wf, amax
     if a.prefetch:
-        slots = torch.empty((c.R, S) + tuple(wts.shape[1:]), dtype=torch.bfloat16, device=dev)
+        slots = torch.empty((c.R, S) + tuple(wts.shape[1:]), dtype=wts.dtype, device=dev)
         ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, LS["s"])))
+        slot_sc = None
+        if gemm_fp8:
+            slot_sc = torch.empty((c.R, S) + tuple(wsc.shape[1:]), dtype=torch.float32, device=dev)
+            ops.append(("prefetch_scales",
+                        lambda: ep.ep_prefetch_replicas(h.ptr, wsc, slot_sc, LS["s"], scales=True)))
     if a.fp8:
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
         ep.ep_plan(h.ptr, idx, stream)
@@ -253,8 +270,13 @@ def main():
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, LS["s"])))
     if a.gemm:
         gy_out = torch.empty((h.recv_rows, a.gemm), dtype=torch.bfloat16, device=dev)
-        recv2d = recv.view(h.recv_rows, c.H)
-        ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"])))
+        if gemm_fp8:   # straight from the FP8 dispatch output
+            rq2d = rq.view(h.recv_rows, c.H)
+            ops.append(("gemm", lambda: ep.ep_expert_gemm_fp8(
+                h.ptr, rq2d, rs, wts, wsc, slots, slot_sc if a.prefetch else None, gy_out, LS["s"])))
+        else:
+            recv2d = recv.view(h.recv_rows, c.H)
+            ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"])))
     ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, LS["s"])))
     if train:
         ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, LS["s"])))
@@ -341,7 +363,7 @@ def main():
               for i, (nm, _) in enumerate(ops)}
 
     filled = int((h.tables()["replica"] >= 0).sum()) if c.layout == "static" and S > 0 else 0
-    ab = algorithmic_bytes(c, a.fp8, filled, slot_elems)
+    ab = algorithmic_bytes(c, a.fp8, filled, slot_elems, 1 if gemm_fp8 else 2)
     gemm_info = None
     if a.gemm:
         tb = h.tables()
@@ -353,15 +375,22 @@ def main():
         # X, every weight matrix some row uses (experts with rows, plus the
         # prefetch slots the segments read) and Y, once each
         mats = int((tb["counts"] > 0).sum()) + (filled if a.prefetch else 0)
-        ab["gemm"] = grows * c.H * 2 + mats * a.gemm * c.H * 2 + grows * a.gemm * 2
+        if gemm_fp8:   # codes (1 byte) plus one fp32 scale per 128 of K, for rows and weights
+            el, sc = 1, 4.0 / 128
+            peak = MFMA_FP8_PEAK_TFLOPS
+        else:
+            el, sc = 2, 0.0
+            peak = MFMA_BF16_PEAK_TFLOPS
+        ab["gemm"] = int(grows * c.H * (el + sc) + mats * a.gemm * c.H * (el + sc) + grows * a.gemm * 2)
         tflops = flops / (per_us["gemm"] * 1e-6) / 1e12
-        gemm_info = {"N": a.gemm, "K": c.H, "rows": grows, "weight_matrices": mats, "flops": flops,
+        gemm_info = {"N": a.gemm, "K": c.H, "dtype": "fp8-e4m3" if gemm_fp8 else "bf16",
+                     "rows": grows, "weight_matrices": mats, "flops": flops,
                      "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1)}
         # the binding resource: MFMA time of the flops or HBM time of the bytes
-        if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) >= ab["gemm"] / (HBM_PEAK_GBPS * 1e9):
+        if flops / (peak * 1e12) >= ab["gemm"] / (HBM_PEAK_GBPS * 1e9):
             gemm_info["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
-                                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+                                     "peak": peak, "unit": "TFLOP/s",
+                                     "frac": round(tflops / peak, 4)}
         else:
             gbps = ab["gemm"] / (per_us["gemm"] * 1e-6) / 1e9
             gemm_info["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),

@@ -27,7 +27,8 @@ __all__ = [
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
-    "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "SLOTS_TRAINING",
+    "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
+    "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
 ]
 
@@ -111,6 +112,7 @@ def load_library():
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_prefetch_replicas": (S, [c_void_p, _T, _T, c_void_p]),
         "ep_expert_gemm": (S, [c_void_p, _T, _T, _T, _T, c_void_p]),
+        "ep_expert_gemm_fp8": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -258,10 +260,12 @@ def ep_dup_grad_reduce(h: int, replica_grads: torch.Tensor, replica_expert: torc
 
 
 def ep_prefetch_replicas(h: int, expert_weights: torch.Tensor, slot_weights: torch.Tensor,
-                         stream=None) -> None:
+                         stream=None, scales: bool = False) -> None:
+    """``scales``: the tensors are the fp32 scales of FP8 weights (tag FP8_SCALES)."""
+    tag = TAG_FP8_SCALES if scales else TAG_EXPERT_WEIGHTS
     _check(load_library().ep_prefetch_replicas(
-        c_void_p(h), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
-        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _stream(stream)), "ep_prefetch_replicas")
+        c_void_p(h), _tensor(expert_weights, tag), _tensor(slot_weights, tag), _stream(stream)),
+        "ep_prefetch_replicas")
 
 
 def ep_expert_gemm(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
@@ -270,6 +274,17 @@ def ep_expert_gemm(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tens
         c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
         _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream)),
         "ep_expert_gemm")
+
+
+def ep_expert_gemm_fp8(h: int, recv_tokens: torch.Tensor, recv_scales: torch.Tensor,
+                       expert_weights: torch.Tensor, expert_scales: torch.Tensor,
+                       slot_weights: torch.Tensor | None, slot_scales: torch.Tensor | None,
+                       out: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_expert_gemm_fp8(
+        c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
+        _tensor(expert_weights, TAG_EXPERT_WEIGHTS), _tensor(expert_scales, TAG_FP8_SCALES),
+        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(slot_scales, TAG_FP8_SCALES),
+        _tensor(out, TAG_TOKENS), _stream(stream)), "ep_expert_gemm_fp8")
 
 
 # ---------------------------------------------------------------------------
@@ -447,15 +462,17 @@ class Buffer:
         return grad_out, grad_w
 
     def prefetch_replicas(self, expert_weights: torch.Tensor, handle: Handle,
-                          slots: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                          slots: torch.Tensor | None = None, stream=None,
+                          scales: bool = False) -> torch.Tensor:
         """Copy the plan's replica experts' weights ([E, P...]) into their
         prefetch slots ([R, S, P...]); slots the plan leaves empty keep their
-        contents (uninitialised if ``slots`` is None)."""
+        contents (uninitialised if ``slots`` is None).  ``scales``: the
+        tensor is the fp32 scales of FP8 weights."""
         c = self.group.cfg
         if slots is None:
             slots = torch.empty((c.num_ranks, c.slots_per_rank) + tuple(expert_weights.shape[1:]),
                                 dtype=expert_weights.dtype, device=expert_weights.device)
-        ep_prefetch_replicas(handle.ptr, expert_weights, slots, stream)
+        ep_prefetch_replicas(handle.ptr, expert_weights, slots, stream, scales=scales)
         return slots
 
     def expert_gemm(self, recv: torch.Tensor, expert_weights: torch.Tensor, handle: Handle,
@@ -469,6 +486,21 @@ class Buffer:
             out = torch.empty((rows, N), dtype=torch.bfloat16, device=recv.device)
         ep_expert_gemm(handle.ptr, recv.view(rows, expert_weights.shape[2]), expert_weights, slots,
                        out, stream)
+        return out
+
+    def expert_gemm_fp8(self, recv: torch.Tensor, recv_scales: torch.Tensor,
+                        expert_weights: torch.Tensor, expert_scales: torch.Tensor, handle: Handle,
+                        slots: torch.Tensor | None = None, slot_scales: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """The grouped GEMM on FP8 operands: ``recv`` e4m3 [rows, K] with fp32
+        ``recv_scales`` [rows, K/128] (the FP8 dispatch output), weights e4m3
+        [E, N, K] with fp32 scales [E, N, K/128]."""
+        N, K = expert_weights.shape[1], expert_weights.shape[2]
+        rows = handle.recv_rows
+        if out is None:
+            out = torch.empty((rows, N), dtype=torch.bfloat16, device=recv.device)
+        ep_expert_gemm_fp8(handle.ptr, recv.view(rows, K), recv_scales.view(rows, K // 128),
+                           expert_weights, expert_scales, slots, slot_scales, out, stream)
         return out
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,

@@ -448,11 +448,15 @@ ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weight
   if (!h || !expert_weights || !slot_weights) return EP_ERR_INVALID_ARG;
   const epk::Geometry &g = h->geo;
   const int32_t dt = expert_weights->dtype;
-  if (dt != EP_DTYPE_BF16 && dt != EP_DTYPE_FP32 && dt != EP_DTYPE_FP8_E4M3)
+  // the weights themselves, or the fp32 scales of FP8 weights
+  const int32_t tag = expert_weights->tag == EP_TAG_FP8_SCALES ? EP_TAG_FP8_SCALES
+                                                                : EP_TAG_EXPERT_WEIGHTS;
+  if (tag == EP_TAG_FP8_SCALES ? dt != EP_DTYPE_FP32
+                               : dt != EP_DTYPE_BF16 && dt != EP_DTYPE_FP32 && dt != EP_DTYPE_FP8_E4M3)
     return EP_ERR_BAD_DTYPE;
-  ep_status_t st = check_tensor(expert_weights, EP_TAG_EXPERT_WEIGHTS, dt);
+  ep_status_t st = check_tensor(expert_weights, tag, dt);
   if (st != EP_OK) return st;
-  st = check_tensor(slot_weights, EP_TAG_EXPERT_WEIGHTS, dt);
+  st = check_tensor(slot_weights, tag, dt);
   if (st != EP_OK) return st;
   if (g.layout != EP_LAYOUT_STATIC) return EP_ERR_UNSUPPORTED;
   // expert_weights [E, P...]; slot_weights [R, S, P...] or [R*S, P...]
@@ -513,6 +517,59 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
                                              static_cast<const uint16_t *>(w->data), wslot,
                                              (int32_t)K, (int32_t)N,
                                              static_cast<uint16_t *>(out->data), as_stream(stream)));
+}
+
+ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                               const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,
+                               const ep_tensor_t *expert_scales, const ep_tensor_t *slot_weights,
+                               const ep_tensor_t *slot_scales, ep_tensor_t *out, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(recv_tokens, EP_TAG_TOKENS, EP_DTYPE_FP8_E4M3);
+  if (st != EP_OK) return st;
+  st = check_tensor(recv_scales, EP_TAG_FP8_SCALES, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  st = check_tensor(expert_weights, EP_TAG_EXPERT_WEIGHTS, EP_DTYPE_FP8_E4M3);
+  if (st != EP_OK) return st;
+  st = check_tensor(expert_scales, EP_TAG_FP8_SCALES, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  st = check_tensor(out, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  const ep_tensor_t *w = expert_weights, *ws = expert_scales;
+  if (w->ndim != 3 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
+  const int64_t N = w->sizes[1], K = w->sizes[2];
+  if (K <= 0 || K % 128 != 0 || K > INT32_MAX || N < 1 || N > INT32_MAX) return EP_ERR_BAD_SHAPE;
+  const int64_t NB = K / 128;
+  if (!(ws->ndim == 3 && ws->sizes[0] == g.E && ws->sizes[1] == N && ws->sizes[2] == NB))
+    return EP_ERR_BAD_SHAPE;
+  if (!is_rows(recv_tokens, g.rows, K) || !is_rows(recv_scales, g.rows, NB) ||
+      !is_rows(out, g.rows, N))
+    return EP_ERR_BAD_SHAPE;
+  if ((slot_weights == nullptr) != (slot_scales == nullptr)) return EP_ERR_INVALID_ARG;
+  const uint8_t *wslot = nullptr;
+  const float *swslot = nullptr;
+  if (slot_weights) {
+    st = check_tensor(slot_weights, EP_TAG_EXPERT_WEIGHTS, EP_DTYPE_FP8_E4M3);
+    if (st != EP_OK) return st;
+    st = check_tensor(slot_scales, EP_TAG_FP8_SCALES, EP_DTYPE_FP32);
+    if (st != EP_OK) return st;
+    if (g.layout != EP_LAYOUT_STATIC) return EP_ERR_UNSUPPORTED;
+    const int64_t RS = (int64_t)g.R * g.S;
+    auto slots_of = [&](const ep_tensor_t *t, int64_t last) {
+      return (t->ndim == 4 && t->sizes[0] == g.R && t->sizes[1] == g.S && t->sizes[2] == N &&
+              t->sizes[3] == last) ||
+             (t->ndim == 3 && t->sizes[0] == RS && t->sizes[1] == N && t->sizes[2] == last);
+    };
+    if (!slots_of(slot_weights, K) || !slots_of(slot_scales, NB)) return EP_ERR_BAD_SHAPE;
+    wslot = static_cast<const uint8_t *>(slot_weights->data);
+    swslot = static_cast<const float *>(slot_scales->data);
+  }
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return hip_status(epk::launch_grouped_gemm_fp8(
+      g, h->ws, static_cast<const uint8_t *>(recv_tokens->data),
+      static_cast<const float *>(recv_scales->data), static_cast<const uint8_t *>(w->data),
+      static_cast<const float *>(ws->data), wslot, swslot, (int32_t)K, (int32_t)N,
+      static_cast<uint16_t *>(out->data), as_stream(stream)));
 }
 
 }  // extern "C"

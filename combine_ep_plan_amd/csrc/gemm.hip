@@ -259,6 +259,188 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
     }
 }
 
+// ---------------------------------------------------------------------------
+// grouped GEMM on FP8 operands
+//
+// The rows come as the FP8 dispatch leaves them and the weights in the same
+// format: OCP e4m3 codes, one fp32 scale per 128 of K (for a row of X, and
+// for a row n of a weight matrix).  A code stands for code * scale, so
+//   Y[row][n] = bf16( sum_b SX[row][b] * SW[n][b] * sum_{c in block b} X[row][c] * W[n][c] ).
+// Same tiles, waves, XCD order and LDS geometry as k_grouped_gemm: a slab
+// is 128 K-bytes, which is one scale block.  Per slab each wave runs two
+// 64-deep steps of v_mfma_scale_f32_32x32x64_f8f6f4 (unit hardware scales)
+// into a partial accumulator that starts at zero, then folds it into the
+// running sum with the block's row and column scales:
+//   acc += part * (SX[row][b] * SW[col][b])
+// (the hardware block scales are powers of two, the format's are not, so the
+// scales are applied on the vector ALU).  The slab's 128 row scales and 128
+// column scales go through LDS beside the codes, in four rotating buffers
+// so the fold can run after the barrier that publishes the next slab.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kScaleBufs = 4;
+constexpr int kF8Block = 128;  // K per scale; also the slab depth in bytes
+
+__global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
+    const u32x4 *__restrict__ X, const float *__restrict__ SX, const u32x4 *__restrict__ W,
+    const float *__restrict__ SW, const u32x4 *__restrict__ Wslot,
+    const float *__restrict__ SWslot, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, int32_t K, int32_t N, int32_t E, int32_t n_col_tiles,
+    uint16_t *__restrict__ Y) {
+  __shared__ u32x4 sa[2][kTileM * kChunks];
+  __shared__ u32x4 sb[2][kBN * kChunks];
+  __shared__ __attribute__((aligned(16))) float ssc[kScaleBufs][kTileM + kBN];  // row, then column scales
+  static_assert(kTileM + kBN == kGemmThreads, "one scale per thread per slab");
+  const int32_t valid = *ntiles * n_col_tiles;
+  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
+  const int32_t slot = blockIdx.x / kXcds;
+  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || lid >= valid) return;
+  const int32_t tile = lid / n_col_tiles;
+  const int32_t n0 = (lid - tile * n_col_tiles) * kBN;
+  const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
+  const int64_t KV = K / 16;        // 16-byte vectors per row
+  const int32_t NB = K / kF8Block;  // scales per row
+  const bool own = widx < E;
+  const int64_t wsel = own ? widx : widx - E;
+  const u32x4 *Wm = (own ? W : Wslot) + wsel * N * KV;
+  const float *SWm = (own ? SW : SWslot) + wsel * N * NB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / kWavesN, wn = wv % kWavesN;
+
+  constexpr int kLoads = kTileM * kChunks / kGemmThreads;
+  constexpr int kLoadsB = kBN * kChunks / kGemmThreads;
+  const int c_ld = tid & (kChunks - 1);
+  // Uniform tile bases and 32-bit lane offsets (a tile spans at most 128
+  // rows of K bytes), so the loads take a scalar base.
+  const u32x4 *Xt = X + (int64_t)row0 * KV;
+  const u32x4 *Wt = Wm + (int64_t)n0 * KV;
+  uint32_t oa[kLoads], ob[kLoadsB];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    oa[i] = (uint32_t)((r < rows ? r : rows - 1) * KV + c_ld);
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsB; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    ob[i] = (uint32_t)((n0 + r < N ? r : N - 1 - n0) * KV + c_ld);
+  }
+  // thread t < 128 stages the scale of tile row t, thread 128 + c that of column c
+  const float *ps = tid < kTileM
+                        ? SX + (int64_t)(row0 + (tid < rows ? tid : rows - 1)) * NB
+                        : SWm + (int64_t)(n0 + tid - kTileM < N ? n0 + tid - kTileM : N - 1) * NB;
+  u32x4 ra0[kLoads], rb0[kLoadsB];
+  float rs;
+
+#define GLOAD(kt)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) ra0[i] = (Xt + (kt) * kChunks)[oa[i]]; \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i) rb0[i] = (Wt + (kt) * kChunks)[ob[i]]; \
+  rs = ps[kt];
+#define SWRITE(kt)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < kLoads; ++i)                                          \
+      sa[(kt) & 1][swz((tid + i * kGemmThreads) / kChunks, c_ld)] = ra0[i];                   \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i)                                         \
+      sb[(kt) & 1][swz((tid + i * kGemmThreads) / kChunks, c_ld)] = rb0[i];                   \
+  ssc[(kt) % kScaleBufs][tid] = rs;
+
+  f32x16 acc[kFM][kFN], part[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Step h (0, 1) of a slab: a lane of the upper half-wave takes chunks
+  // 4h + 2, 4h + 3 of its row, the lower half chunks 4h, 4h + 1 (the same
+  // K positions for A and B, which is all the product needs).
+#define READK(FA, FB, buf, h)                                                                  \
+  {                                                                                            \
+    const int c_ = (h) * 4 + (lane >> 5) * 2;                                                  \
+    _Pragma("unroll") for (int i = 0; i < kFM; ++i) {                                          \
+      const int r_ = wm * kWTM + i * 32 + (lane & 31);                                         \
+      const u32x4 lo = sa[buf][swz(r_, c_)], hi = sa[buf][swz(r_, c_ + 1)];                    \
+      FA[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,                                \
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};                               \
+    }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < kFN; ++j) {                                          \
+      const int r_ = wn * kWTN + j * 32 + (lane & 31);                                         \
+      const u32x4 lo = sb[buf][swz(r_, c_)], hi = sb[buf][swz(r_, c_ + 1)];                    \
+      FB[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,                                \
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};                               \
+    }                                                                                          \
+  }
+  // cbsz = blgp = 0: both operands e4m3; scale exponents 127: 2^0
+#define MFMAK(FA, FB, FIRST)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                              \
+  _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                              \
+      part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                            \
+          FA[i], FB[j], (FIRST) ? f32x16{} : part[i][j], 0, 0, 0, 127, 0, 127);
+
+  static_assert(kChunks * 16 == kF8Block, "a slab is one scale block");
+  const int KT = K / kF8Block;
+  // One set of fragments: the second step's LDS reads are issued behind the
+  // first step's MFMAs (the registers of the partial sums and of the slab in
+  // flight leave no room for a second set at two waves per SIMD).
+  i32x8 fa[kFM], fb[kFN];
+  GLOAD(0);
+  SWRITE(0);
+  if (KT > 1) { GLOAD(1); }
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    READK(fa, fb, buf, 0);
+    MFMAK(fa, fb, true);
+    READK(fa, fb, buf, 1);
+    MFMAK(fa, fb, false);
+    if (kt + 1 < KT) {
+      SWRITE(kt + 1);
+      if (kt + 2 < KT) { GLOAD(kt + 2); }
+      __syncthreads();
+    }
+    // fold: accumulator r of a lane is tile row wm*64 + i*32 + (r/4)*8 +
+    // (lane/32)*4 + r%4, column wn*64 + j*32 + lane%32
+    const float *sc = ssc[kt % kScaleBufs];
+    float scol[kFN];
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 srow =
+            *reinterpret_cast<const f32x4 *>(sc + wm * kWTM + i * 32 + g4 * 8 + (lane >> 5) * 4);
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][j][g4 * 4 + q] += part[i][j][g4 * 4 + q] * (srow[q] * scol[j]);
+      }
+  }
+#undef READK
+#undef MFMAK
+#undef GLOAD
+#undef SWRITE
+
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) {
+      const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+        if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
+        if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
+      }
+    }
+}
+
 int32_t gemm_max_tiles(const Geometry &g) {
   const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
   return (int32_t)((g.n + kTileM - 1) / kTileM + groups);
@@ -278,6 +460,24 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
                      reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
                      reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
                      g.E, ncol, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const uint8_t *x,
+                                   const float *sx, const uint8_t *w, const float *sw,
+                                   const uint8_t *wslot, const float *swslot, int32_t K, int32_t N,
+                                   uint16_t *y, hipStream_t s) {
+  const int32_t max_tiles = gemm_max_tiles(g);
+  if (max_tiles == 0 || N == 0) return hipSuccess;
+  TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
+  hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  const int32_t ncol = (N + kBN - 1) / kBN;
+  int64_t blocks = (int64_t)max_tiles * ncol;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+                     reinterpret_cast<const u32x4 *>(x), sx, reinterpret_cast<const u32x4 *>(w), sw,
+                     reinterpret_cast<const u32x4 *>(wslot), swslot, ws.gemm_tiles,
+                     ws.gemm_ntiles, K, N, g.E, ncol, y);
   return hipGetLastError();
 }
 

@@ -306,10 +306,12 @@ ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
  * r = segments[i][1], slot (r, s) becomes a byte copy of expert
  * segments[i][0]'s row of expert_weights.  Slots the plan leaves empty, and
  * segments without a slot, are not touched (the overflow of the inference
- * slot mode reads the owner's row directly).  Call it once per projection.
- * expert_weights: [E, P...], tag EXPERT_WEIGHTS, dtype bf16, fp32 or FP8.
- * slot_weights:   [R, S, P...] output, tag EXPERT_WEIGHTS, same dtype; the
- *                 2-D form [R*S, P] is accepted too.
+ * slot mode reads the owner's row directly).  Call it once per projection
+ * (for FP8 weights, once for the codes and once for their scales).
+ * expert_weights: [E, P...], tag EXPERT_WEIGHTS, dtype bf16, fp32 or FP8;
+ *                 or the scales of FP8 weights: tag FP8_SCALES, fp32.
+ * slot_weights:   [R, S, P...] output, same tag and dtype; the 2-D form
+ *                 [R*S, P] is accepted too.
  * A row (P elements) must be a multiple of 16 bytes.  Errors:
  * EP_ERR_UNSUPPORTED for a non-STATIC handle, EP_ERR_NOT_PLANNED before
  * ep_plan, EP_ERR_BAD_SHAPE for mismatched sizes.  Reads only the plan
@@ -344,6 +346,32 @@ ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weight
 ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
                            const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
                            ep_tensor_t *out, void *stream);
+
+/* The same grouped GEMM on FP8 operands ("Ultra-Large MoE Models" article,
+ * section 3.1, over the receive rows the FP8 dispatch delivers: e4m3 codes
+ * with one fp32 scale per 128 channels, NCCL EP listing, Table IV).  The
+ * weights come in the same format: one scale per output row n and 128-wide
+ * block of K.  A code stands for code * scale, so for every group (as in
+ * ep_expert_gemm), row i and column n < N:
+ *   out[i, n] = bf16( sum_b recv_scales[i, b] * W_scales[n, b] *
+ *                     sum_{c in block b} recv_tokens[i, c] * W[n, c] )
+ * (exact e4m3 products, fp32 accumulation, one rounding to nearest even).
+ * recv_tokens:   e4m3 [recv_rows, K], tag TOKENS; K % 128 == 0.
+ * recv_scales:   fp32 [recv_rows, K/128], tag FP8_SCALES.
+ * expert_weights: e4m3 [E, N, K], tag EXPERT_WEIGHTS.
+ * expert_scales: fp32 [E, N, K/128], tag FP8_SCALES.
+ * slot_weights, slot_scales: both NULL, or (STATIC only) e4m3 [R, S, N, K]
+ *                and fp32 [R, S, N, K/128] (or [R*S, ...]) filled by
+ *                ep_prefetch_replicas, tags EXPERT_WEIGHTS and FP8_SCALES.
+ * out:           bf16 [recv_rows, N], tag TOKENS; rows no group covers are
+ *                not written.
+ * Errors: EP_ERR_BAD_SHAPE, EP_ERR_INVALID_ARG (only one of the slot
+ * tensors given), EP_ERR_UNSUPPORTED (slots for a non-STATIC handle),
+ * EP_ERR_NOT_PLANNED.  Enqueues two kernels (tile table, GEMM). */
+ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                               const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,
+                               const ep_tensor_t *expert_scales, const ep_tensor_t *slot_weights,
+                               const ep_tensor_t *slot_scales, ep_tensor_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -323,3 +323,50 @@ def test_expert_gemm_argument_validation(lib):
     assert G(h, x, w, T(BF16, W, 4, 2, 32, 64), y, None) == 5
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
+
+
+def test_prefetch_accepts_fp8_weight_scales(lib):
+    P = lib.ep_prefetch_replicas
+    W, SC = ep.TAG_EXPERT_WEIGHTS, ep.TAG_FP8_SCALES
+    g, h, _ = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    assert P(h, T(F32, SC, 8, 4, 2), T(F32, SC, 4, 2, 4, 2), None) == 5   # scales: accepted, not planned
+    assert P(h, T(F32, SC, 8, 4, 2), T(F32, W, 4, 2, 4, 2), None) == 2    # tags differ
+    assert P(h, T(BF16, SC, 8, 4, 8), T(BF16, SC, 4, 2, 4, 8), None) == 3  # scales are fp32
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
+def test_expert_gemm_fp8_argument_validation(lib):
+    G = lib.ep_expert_gemm_fp8
+    W, TK, SC = ep.TAG_EXPERT_WEIGHTS, ep.TAG_TOKENS, ep.TAG_FP8_SCALES
+    g, h, _ = make_handle(lib)                       # HT, T=64, k=2: 128 rows, E=8
+    x, sx = T(FP8, TK, 128, 256), T(F32, SC, 128, 2)
+    w, sw = T(FP8, W, 8, 32, 256), T(F32, SC, 8, 32, 2)
+    y = T(BF16, TK, 128, 32)
+    assert G(None, x, sx, w, sw, None, None, y, None) == 1
+    assert G(h, T(BF16, TK, 128, 256), sx, w, sw, None, None, y, None) == 3   # codes must be FP8
+    assert G(h, x, T(F32, TK, 128, 2), w, sw, None, None, y, None) == 2       # scales tag
+    assert G(h, x, sx, T(BF16, W, 8, 32, 256), sw, None, None, y, None) == 3
+    assert G(h, x, sx, w, sw, None, None, T(F32, TK, 128, 32), None) == 3     # out is bf16
+    assert G(h, T(FP8, TK, 128, 192), T(F32, SC, 128, 1), T(FP8, W, 8, 32, 192),
+             T(F32, SC, 8, 32, 1), None, None, y, None) == 4                  # K % 128
+    assert G(h, x, T(F32, SC, 128, 1), w, sw, None, None, y, None) == 4       # row scales K/128
+    assert G(h, x, sx, w, T(F32, SC, 8, 32, 1), None, None, y, None) == 4     # weight scales K/128
+    assert G(h, x, sx, w, T(F32, SC, 7, 32, 2), None, None, y, None) == 4
+    assert G(h, x, sx, T(FP8, W, 7, 32, 256), sw, None, None, y, None) == 4   # not E matrices
+    assert G(h, T(FP8, TK, 127, 256), sx, w, sw, None, None, y, None) == 4    # not recv_rows
+    assert G(h, x, sx, w, sw, None, None, T(BF16, TK, 128, 33), None) == 4    # out columns != N
+    assert G(h, x, sx, w, sw, T(FP8, W, 4, 1, 32, 256), None, y, None) == 1   # slot scales missing
+    assert G(h, x, sx, w, sw, T(FP8, W, 4, 1, 32, 256), T(F32, SC, 4, 1, 32, 2), y, None) == 7
+    assert G(h, x, sx, w, sw, None, None, y, None) == 5                       # not planned
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+    g, h, _ = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
+    sl, ssl = T(FP8, W, 4, 2, 32, 256), T(F32, SC, 4, 2, 32, 2)
+    assert G(h, x, sx, w, sw, T(FP8, W, 4, 3, 32, 256), ssl, y, None) == 4    # not [R, S, N, K]
+    assert G(h, x, sx, w, sw, sl, T(F32, SC, 4, 2, 32, 1), y, None) == 4      # slot scales K/128
+    assert G(h, x, sx, w, sw, sl, T(BF16, SC, 4, 2, 32, 2), y, None) == 3
+    assert G(h, x, sx, w, sw, sl, ssl, y, None) == 5                          # not planned
+    assert G(h, x, sx, w, sw, T(FP8, W, 8, 32, 256), T(F32, SC, 8, 32, 2), y, None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
