@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
       sb[(kt) & 1][swz((tid + i * kGemmThreads) / kChunks, c_ld)] = rb0[i];                   \
   ssc[(kt) % kScaleBufs][tid] = rs;
 
-  f32x16 acc[kFM][kFN], part[kFM][kFN];
+  f32x16 acc[kFM][kFN];
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
@@ -373,55 +373,74 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};                               \
     }                                                                                          \
   }
-  // cbsz = blgp = 0: both operands e4m3; scale exponents 127: 2^0
-#define MFMAK(FA, FB, FIRST)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                              \
-  _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                              \
-      part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                            \
-          FA[i], FB[j], (FIRST) ? f32x16{} : part[i][j], 0, 0, 0, 127, 0, 127);
+  // One 32 x 32 output block over a whole slab (both 64-deep steps) into the
+  // partial sum P.  cbsz = blgp = 0: both operands e4m3; scale exponents
+  // 127: 2^0.
+#define BLOCK(P, i, j)                                                                         \
+  P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], f32x16{}, 0, 0, 0, 127,  \
+                                                      0, 127);                                 \
+  P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], P, 0, 0, 0, 127, 0, 127);
+  // acc += P * (row scale * column scale); accumulator r of a lane is tile
+  // row wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4, column wn*64 + j*32 + lane%32
+#define FOLD(P, i, j)                                                                          \
+  _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4)                                             \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                \
+      acc[i][j][g4 * 4 + q] += P[g4 * 4 + q] * (srow[g4][q] * scol[j]);
+#define ROWSCALES(i)                                                                           \
+  _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) srow[g4] =                                  \
+      *reinterpret_cast<const f32x4 *>(sc + wm * kWTM + (i) * 32 + g4 * 8 + (lane >> 5) * 4);
 
   static_assert(kChunks * 16 == kF8Block, "a slab is one scale block");
+  static_assert(kFM == 2 && kFN == 2, "the block order below is written for 2 x 2 blocks");
   const int KT = K / kF8Block;
-  // One set of fragments: the second step's LDS reads are issued behind the
-  // first step's MFMAs (the registers of the partial sums and of the slab in
-  // flight leave no room for a second set at two waves per SIMD).
-  i32x8 fa[kFM], fb[kFN];
+  // Both steps' fragments of a slab are held at once.  The four 32 x 32
+  // blocks of a wave run one after another on two partial sums in turn, so
+  // the fold of one block (vector ALU) is issued while the MFMAs of the next
+  // are in flight; the last fold of a slab goes behind the barrier that
+  // publishes the next one, and the next slab's fragments are read after it
+  // (reading them before it needs more registers than two waves per SIMD
+  // have).  sched_barrier keeps that order.
+  i32x8 fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
+  f32x16 p0, p1;
+  float scol[kFN];
+  f32x4 srow[4];
   GLOAD(0);
   SWRITE(0);
   if (KT > 1) { GLOAD(1); }
   __syncthreads();
+  READK(fa0, fb0, 0, 0);
+  READK(fa1, fb1, 0, 1);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    READK(fa, fb, buf, 0);
-    MFMAK(fa, fb, true);
-    READK(fa, fb, buf, 1);
-    MFMAK(fa, fb, false);
+    const float *sc = ssc[kt % kScaleBufs];
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];
+    ROWSCALES(0);
+    BLOCK(p0, 0, 0);
+    BLOCK(p1, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    FOLD(p0, 0, 0);
+    BLOCK(p0, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    FOLD(p1, 0, 1);
+    BLOCK(p1, 1, 1);
+    ROWSCALES(1);
+    __builtin_amdgcn_sched_barrier(0);
+    FOLD(p0, 1, 0);
     if (kt + 1 < KT) {
       SWRITE(kt + 1);
       if (kt + 2 < KT) { GLOAD(kt + 2); }
       __syncthreads();
     }
-    // fold: accumulator r of a lane is tile row wm*64 + i*32 + (r/4)*8 +
-    // (lane/32)*4 + r%4, column wn*64 + j*32 + lane%32
-    const float *sc = ssc[kt % kScaleBufs];
-    float scol[kFN];
-#pragma unroll
-    for (int j = 0; j < kFN; ++j) scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];
-#pragma unroll
-    for (int i = 0; i < kFM; ++i)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 srow =
-            *reinterpret_cast<const f32x4 *>(sc + wm * kWTM + i * 32 + g4 * 8 + (lane >> 5) * 4);
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[i][j][g4 * 4 + q] += part[i][j][g4 * 4 + q] * (srow[q] * scol[j]);
-      }
+    FOLD(p1, 1, 1);
+    if (kt + 1 < KT) {
+      READK(fa0, fb0, (kt + 1) & 1, 0);
+      READK(fa1, fb1, (kt + 1) & 1, 1);
+    }
   }
+#undef BLOCK
+#undef FOLD
+#undef ROWSCALES
 #undef READK
-#undef MFMAK
 #undef GLOAD
 #undef SWRITE
 
