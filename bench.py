@@ -59,6 +59,14 @@ def parse():
                         "[rows, H] bf16 tokens times one [N, H] bf16 matrix per expert (through "
                         "the prefetch slots with --prefetch); reported beside the step, its "
                         "roofline against the bf16 MFMA peak")
+    p.add_argument("--microbatches", type=int, default=1, metavar="M",
+                   help="one step = M independent micro-batches of the workload (forward chain "
+                        "plan -> dispatch -> combine), each with its own inputs, handle, receive "
+                        "and output buffers (M-deep buffering); value = M*T tokens per step")
+    p.add_argument("--overlap", action="store_true",
+                   help="with --microbatches: micro-batch i on stream i, launches interleaved op "
+                        "by op, so one micro-batch's plan/dispatch runs beside another's combine "
+                        "(without it: all micro-batches in turn on one stream)")
     p.add_argument("--graph", action="store_true",
                    help="time the step as one captured HIP graph (replayed K times) instead of "
                         "K eager launches of each call; per-kernel times stay eager")
@@ -171,12 +179,188 @@ def cpu_baseline(name, rho, fp8, budget_s):
             "value_1_thread": round(Ts * runs1 / el1, 1), "cpu_model": model}
 
 
+def run_microbatches(a):
+    """Several micro-batches in flight: the one-GPU form of double-buffered
+    dispatch/combine ([NCCL-EP] Table II and Figure 2: LL mode overlaps the
+    dispatch and combine phases of consecutive batches through double
+    buffers).  Every micro-batch has its own handle, receive and output
+    buffers; with --overlap each runs on its own stream (default priority) and
+    the launches are interleaved op by op, so the GPU sees micro-batch i's
+    plan and dispatch beside micro-batch j's combine."""
+    import numpy as np
+    import torch
+    import combine_ep_plan_amd as ep
+    import workloads
+
+    name, M = a.workload, a.microbatches
+    if name == "training" or a.route or a.prefetch or a.gemm or a.graph or a.cold:
+        print("bench.py: --microbatches times the forward chain only (no training, --route, "
+              "--prefetch, --gemm, --graph or --cold)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    main_stream = torch.cuda.current_stream()
+    c = workloads.get_config(name, a.rho)
+    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S)
+    streams = [torch.cuda.Stream() for _ in range(M)] if a.overlap else [main_stream] * M
+    mbs = []
+    for i in range(M):
+        inp = workloads.make_inputs(name, i, a.rho)
+        h = ep.Handle(g, c.T)
+        x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        idx = torch.from_numpy(inp.topk_idx).to(dev)
+        w = torch.from_numpy(inp.topk_w).to(dev)
+        recv = torch.empty(g.recv_shape(c.T), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((c.T, c.H), dtype=torch.float32 if c.out_fp32 else torch.bfloat16, device=dev)
+        ep.ep_plan(h.ptr, idx, main_stream)
+        ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, main_stream)   # bf16 rows feed combine
+        rq = rs = None
+        if a.fp8:
+            rq = torch.empty(g.recv_shape(c.T), dtype=torch.float8_e4m3fn, device=dev)
+            rs = torch.empty((h.recv_rows, c.H // 128), dtype=torch.float32, device=dev)
+        st = streams[i]
+
+        def ops_for(h=h, x=x, idx=idx, w=w, recv=recv, y=y, rq=rq, rs=rs, st=st):
+            disp = ((lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, st)) if a.fp8 else
+                    (lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, st)))
+            return [("plan", lambda: ep.ep_plan(h.ptr, idx, st)), ("dispatch", disp),
+                    ("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, st))]
+        mbs.append((h, ops_for()))
+    n_ops = len(mbs[0][1])
+    start = torch.cuda.Event()
+    ends = [torch.cuda.Event() for _ in range(M)]
+
+    def step():
+        # one pass over every micro-batch; with --overlap the streams are not
+        # joined between steps (micro-batch i's next step depends only on its
+        # own previous one), only around the timed region
+        if a.overlap:
+            for j in range(n_ops):
+                for _, ops in mbs:
+                    ops[j][1]()
+        else:
+            for _, ops in mbs:
+                for _, f in ops:
+                    f()
+
+    def fork():
+        start.record(main_stream)
+        for st in streams:
+            st.wait_event(start)
+
+    def join():
+        for st, e in zip(streams, ends):
+            e.record(st)
+            main_stream.wait_event(e)
+
+    if a.overlap:
+        fork()
+    for _ in range(a.warmup):
+        step()
+    if a.overlap:
+        join()
+    torch.cuda.synchronize()
+    for h, _ in mbs:
+        assert h.status() == 0, "device flags raised on the benchmark input"
+    K = a.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]
+    torch.cuda.synchronize()
+    e0.record(main_stream)
+    if a.overlap:
+        fork()
+    for i in range(K):
+        step()
+        if i < K - 1 and not a.overlap:
+            marks[i].record(main_stream)
+    if a.overlap:
+        join()
+    e1.record(main_stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / K
+    if a.overlap:
+        median_ms = None   # the streams run free between the fork and the join
+    else:
+        bounds = [e0] + marks + [e1]
+        step_list = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(K))
+        median_ms = step_list[K // 2] if K % 2 else 0.5 * (step_list[K // 2 - 1] + step_list[K // 2])
+
+    # per-kernel durations: micro-batch 0's launches one by one on the main
+    # stream (nothing beside them), for the roofline of the dominant kernel
+    h0, _ = mbs[0]
+    inp0 = workloads.make_inputs(name, 0, a.rho)
+    x0 = torch.from_numpy(inp0.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx0 = torch.from_numpy(inp0.topk_idx).to(dev)
+    w0 = torch.from_numpy(inp0.topk_w).to(dev)
+    recv0 = torch.empty(g.recv_shape(c.T), dtype=torch.bfloat16, device=dev)
+    y0 = torch.empty((c.T, c.H), dtype=torch.float32 if c.out_fp32 else torch.bfloat16, device=dev)
+    rq0 = torch.empty(g.recv_shape(c.T), dtype=torch.float8_e4m3fn, device=dev) if a.fp8 else None
+    rs0 = torch.empty((h0.recv_rows, c.H // 128), dtype=torch.float32, device=dev) if a.fp8 else None
+    serial = [("plan", lambda: ep.ep_plan(h0.ptr, idx0, main_stream)),
+              ("dispatch", (lambda: ep.ep_dispatch(h0.ptr, x0, None, rq0, rs0, None, None, main_stream)) if a.fp8
+               else (lambda: ep.ep_dispatch(h0.ptr, x0, None, recv0, None, None, None, main_stream))),
+              ("combine", lambda: ep.ep_combine(h0.ptr, recv0, w0, y0, main_stream))]
+    ep.ep_plan(h0.ptr, idx0, main_stream)
+    ep.ep_dispatch(h0.ptr, x0, None, recv0, None, None, None, main_stream)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in serial]
+           for _ in range(K)]
+    for sidx in range(K):
+        for (b, e), (_, f) in zip(evs[sidx], serial):
+            b.record(main_stream)
+            f()
+            e.record(main_stream)
+    torch.cuda.synchronize()
+    per_us = {nm: 1000.0 * sum(evs[sidx][i][0].elapsed_time(evs[sidx][i][1]) for sidx in range(K)) / K
+              for i, (nm, _) in enumerate(serial)}
+    ab = algorithmic_bytes(c, a.fp8)
+    dom = max(("dispatch", "combine"), key=lambda nm: per_us[nm])
+    dom_gbps = ab[dom] / (per_us[dom] * 1e-6) / 1e9
+    step_s = step_ms / 1000.0
+    chain_bytes = M * sum(ab[nm] for nm, _ in serial)
+    out = {
+        "metric": METRIC,
+        "value": round(M * c.T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "median_ms_per_step": None if median_ms is None else round(median_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name} {c.layout.upper()} T={c.T} H={c.H} E={c.E} top-{c.k}"
+                               f"{' fp8' if a.fp8 else ''}, {M} micro-batches "
+                               f"{'overlapped on ' + str(M) + ' streams' if a.overlap else 'in turn on one stream'}",
+                   "T": c.T, "H": c.H, "E": c.E, "top_k": c.k, "layout": c.layout,
+                   "microbatches": M, "overlap": a.overlap,
+                   "step": " -> ".join(nm for nm, _ in serial) + f" (x{M})"},
+        "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
+        "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": chain_bytes,
+        "kernels_us_alone": {k: round(v, 2) for k, v in per_us.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": ab[dom], "avg_us": round(per_us[dom], 2)},
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(name, a.rho, a.fp8, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); logical "
               "expert-parallel ranks are regions of that GPU's HBM.", file=sys.stderr)
         sys.exit(2)
+    if a.microbatches > 1 or a.overlap:
+        if a.microbatches < 2:
+            print("bench.py: --overlap needs --microbatches M with M >= 2", file=sys.stderr)
+            sys.exit(2)
+        return run_microbatches(a)
     import numpy as np
     import torch
     import combine_ep_plan_amd as ep
