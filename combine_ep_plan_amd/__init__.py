@@ -127,25 +127,34 @@ def _check(code: int, what: str) -> None:
         raise EpError(code, what)
 
 
+_VIEWS: dict = {}
+_VIEWS_MAX = 4096
+
+
 def _tensor(t: torch.Tensor | None, tag: int):
-    """ep_tensor_t view of a contiguous device tensor (None -> NULL)."""
+    """ep_tensor_t view of a contiguous device tensor (None -> NULL).  A view
+    is a pure function of (address, dtype, shape, tag) and the library never
+    writes to it, so built views are kept and reused: the marshalling of a
+    call that repeats its tensors costs a dictionary lookup."""
     if t is None:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
+    key = (t.data_ptr(), t.dtype, t.shape, tag)
+    v = _VIEWS.get(key)
+    if v is not None:
+        return v
     if t.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {t.dtype}")
     if t.dim() < 1 or t.dim() > 4:
         raise ValueError("tensors must have 1..4 dimensions")
-    v = ep_tensor_t()
-    v.data = t.data_ptr() if t.numel() > 0 else None
-    v.dtype = _DTYPES[t.dtype]
-    v.tag = tag
-    v.ndim = t.dim()
-    v.reserved = 0
-    for i, s in enumerate(t.shape):
-        v.sizes[i] = int(s)
-    return ctypes.pointer(v)
+    sizes = (c_int64 * 4)(*(int(x) for x in t.shape))
+    v = ctypes.pointer(ep_tensor_t(t.data_ptr() if t.numel() > 0 else None, _DTYPES[t.dtype], tag,
+                                   t.dim(), 0, sizes))
+    if len(_VIEWS) >= _VIEWS_MAX:
+        _VIEWS.clear()
+    _VIEWS[key] = v
+    return v
 
 
 def _stream(stream) -> c_void_p:
