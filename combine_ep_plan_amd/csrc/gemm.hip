@@ -19,7 +19,11 @@
 //    the global loads of slab kt+2 are in flight during slab kt+1; within a
 //    slab, the fragments of the next 16-deep step are read from LDS while
 //    the MFMAs of the current one run, and the first step of the next slab
-//    is read right after the barrier that publishes it.
+//    is read right after the barrier that publishes it.  In the steady state
+//    (no branches) all 16 MFMAs of a slab come before the barrier and
+//    sched_group_barrier spreads the LDS reads over the first 8 and the next
+//    slab's LDS writes and the global loads of the one after over the last 8,
+//    so the matrix cores stay busy while the wave issues its memory traffic.
 //    LDS: rows of a slab are 128 bytes (eight 16-byte chunks); with 64
 //    4-byte banks two rows share a 256-byte bank row, so chunk c of row r is
 //    stored at c ^ ((r / 2) % 8): the 16 rows one 16-lane phase of an MFMA
@@ -221,7 +225,27 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
   if (KT > 1) { GLOAD(ra0, rb0, 1); }
   __syncthreads();
   READK(fa0, fb0, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS write,
+  // 0x020 global load; each call asks for the next n instructions of that kind
+#define SGB(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) {   // steady state
+    const int buf = kt & 1;
+    READK(fa1, fb1, buf, 1);
+    MFMAK(fa0, fb0);
+    READK(fa0, fb0, buf, 2);
+    MFMAK(fa1, fb1);
+    READK(fa1, fb1, buf, 3);
+    MFMAK(fa0, fb0);
+    SWRITE(ra0, rb0, buf ^ 1);
+    GLOAD(ra0, rb0, kt + 2);
+    MFMAK(fa1, fb1);
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); }
+    __syncthreads();
+    READK(fa0, fb0, buf ^ 1, 0);
+  }
+  for (; kt < KT; ++kt) {   // the last two slabs (no more global loads)
     const int buf = kt & 1;
     READK(fa1, fb1, buf, 1);
     MFMAK(fa0, fb0);
@@ -231,12 +255,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
     MFMAK(fa0, fb0);
     if (kt + 1 < KT) {
       SWRITE(ra0, rb0, buf ^ 1);
-      if (kt + 2 < KT) { GLOAD(ra0, rb0, kt + 2); }
       __syncthreads();
       READK(fa0, fb0, buf ^ 1, 0);
     }
     MFMAK(fa1, fb1);
   }
+#undef SGB
 #undef READK
 #undef MFMAK
 #undef GLOAD
