@@ -476,7 +476,7 @@ ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weight
     if (sl->sizes[sl->ndim - tail + i] != w->sizes[1 + i]) return EP_ERR_BAD_SHAPE;
   const int64_t elem = dt == EP_DTYPE_FP32 ? 4 : dt == EP_DTYPE_BF16 ? 2 : 1;
   const int64_t row_bytes = P * elem;
-  if (row_bytes % 16 != 0) return EP_ERR_BAD_SHAPE;
+  if (row_bytes % 4 != 0) return EP_ERR_BAD_SHAPE;
   if (!h->planned) return EP_ERR_NOT_PLANNED;
   return hip_status(epk::launch_prefetch(g, h->ws, static_cast<const uint8_t *>(w->data),
                                          row_bytes, static_cast<uint8_t *>(sl->data),

@@ -24,6 +24,8 @@
 //    sched_group_barrier spreads the LDS reads over the first 8 and the next
 //    slab's LDS writes and the global loads of the one after over the last 8,
 //    so the matrix cores stay busy while the wave issues its memory traffic.
+//    Epilogue (N a multiple of 8): the tile goes through LDS as bf16 rows and
+//    leaves with 16-byte row stores instead of 2-byte column stores.
 //    LDS: rows of a slab are 128 bytes (eight 16-byte chunks); with 64
 //    4-byte banks two rows share a 256-byte bank row, so chunk c of row r is
 //    stored at c ^ ((r / 2) % 8): the 16 rows one 16-lane phase of an MFMA
@@ -266,6 +268,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
 #undef GLOAD
 #undef SWRITE
 
+  if ((N & 7) == 0) {
+    // Through LDS: the tile as bf16 rows of 128, the 16-byte chunk of column c
+    // of row r stored at chunk (c / 8) ^ (((r / 4) % 4) * 4), so the two
+    // half-waves of a store (rows r and r + 4) land on different banks; then
+    // 16-byte row stores.
+    __syncthreads();   // every wave is done with the slab buffers
+    uint16_t *so = reinterpret_cast<uint16_t *>(&sa[0][0]);
+    static_assert(kTileM * kBN * 2 <= (int)sizeof(sa), "output tile fits the slab buffers");
+#define OSW(r_, cv_) ((r_) * kBN + (((cv_) ^ ((((r_) >> 2) & 3) << 2)) << 3))
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        const int c = wn * kWTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int rr = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+          so[OSW(rr, c >> 3) + (c & 7)] = (uint16_t)(p & 0xFFFFu);
+          so[OSW(rr + 1, c >> 3) + (c & 7)] = (uint16_t)(p >> 16);
+        }
+      }
+    __syncthreads();
+    constexpr int kVecs = kTileM * kBN / 8;   // 16-byte vectors in the tile
+#pragma unroll
+    for (int q = 0; q < kVecs / kGemmThreads; ++q) {
+      const int idx = tid + q * kGemmThreads;
+      const int rr = idx / (kBN / 8), cv = idx % (kBN / 8);
+      const int col = n0 + cv * 8;
+      if (rr < rows && col < N)
+        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
+            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+    }
+#undef OSW
+    return;
+  }
   // accumulator r of a lane: row (r / 4) * 8 + (lane / 32) * 4 + r % 4, column lane % 32
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
@@ -467,6 +505,43 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
 #undef READK
 #undef GLOAD
 #undef SWRITE
+
+  if ((N & 7) == 0) {
+    // Through LDS: the tile as bf16 rows of 128, the 16-byte chunk of column c
+    // of row r stored at chunk (c / 8) ^ (((r / 4) % 4) * 4), so the two
+    // half-waves of a store (rows r and r + 4) land on different banks; then
+    // 16-byte row stores.
+    __syncthreads();   // every wave is done with the slab buffers
+    uint16_t *so = reinterpret_cast<uint16_t *>(&sa[0][0]);
+    static_assert(kTileM * kBN * 2 <= (int)sizeof(sa), "output tile fits the slab buffers");
+#define OSW(r_, cv_) ((r_) * kBN + (((cv_) ^ ((((r_) >> 2) & 3) << 2)) << 3))
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        const int c = wn * kWTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int rr = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+          so[OSW(rr, c >> 3) + (c & 7)] = (uint16_t)(p & 0xFFFFu);
+          so[OSW(rr + 1, c >> 3) + (c & 7)] = (uint16_t)(p >> 16);
+        }
+      }
+    __syncthreads();
+    constexpr int kVecs = kTileM * kBN / 8;   // 16-byte vectors in the tile
+#pragma unroll
+    for (int q = 0; q < kVecs / kGemmThreads; ++q) {
+      const int idx = tid + q * kGemmThreads;
+      const int rr = idx / (kBN / 8), cv = idx % (kBN / 8);
+      const int col = n0 + cv * 8;
+      if (rr < rows && col < N)
+        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
+            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+    }
+#undef OSW
+    return;
+  }
 
 #pragma unroll
   for (int i = 0; i < kFM; ++i)

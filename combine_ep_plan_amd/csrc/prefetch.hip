@@ -8,10 +8,12 @@
 // compacts the filled slots into LDS (segment i with seg_slot[i] = s >= 0
 // gives source expert segments[i][0] and destination slot
 // segments[i][1] * S + s; at most E + R of them), then walks the
-// (slot, 32 KB chunk) pairs with a grid stride.  Each chunk is 512 lanes x 4
-// 16-byte vectors: all loads issue before any store, every load and store is
-// a full 16-byte vector, a wave covers 1 KB contiguous.  Distinct segments
-// name distinct slots, so no two workgroups write the same bytes.
+// (slot, chunk) pairs with a grid stride.  Each chunk is 512 lanes x 4
+// vectors: all loads issue before any store, a wave covers 64 contiguous
+// vectors.  Rows that are a multiple of 16 bytes move in 16-byte vectors
+// (32 KB chunks); other rows (a multiple of 4 bytes, such as the fp32 scale
+// rows of FP8 weights) in 4-byte words.  Distinct segments name distinct
+// slots, so no two workgroups write the same bytes.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -19,9 +21,12 @@ namespace epk {
 
 constexpr int kPrefetchThreads = 512;
 constexpr int kPrefetchUnroll = 4;
-constexpr int64_t kPrefetchChunk = (int64_t)kPrefetchThreads * kPrefetchUnroll * 16;  // bytes
 constexpr int kPrefetchMaxBlocks = 2048;
 
+template <typename V>
+constexpr int64_t prefetch_chunk() { return (int64_t)kPrefetchThreads * kPrefetchUnroll * sizeof(V); }
+
+template <typename V>
 __global__ __launch_bounds__(kPrefetchThreads) void k_prefetch(
     const uint8_t *__restrict__ weights, uint8_t *__restrict__ slots,
     const int32_t *__restrict__ segments, const int32_t *__restrict__ seg_slot,
@@ -63,16 +68,17 @@ __global__ __launch_bounds__(kPrefetchThreads) void k_prefetch(
     __syncthreads();
   }
 
-  const int64_t cpr = (row_bytes + kPrefetchChunk - 1) / kPrefetchChunk;  // chunks per row
+  constexpr int64_t kChunk = prefetch_chunk<V>();
+  const int64_t cpr = (row_bytes + kChunk - 1) / kChunk;  // chunks per row
   const int64_t work = (int64_t)nfill * cpr;
   for (int64_t q = blockIdx.x; q < work; q += gridDim.x) {
     const int32_t j = (int32_t)(q / cpr);
-    const int64_t off = (q - (int64_t)j * cpr) * kPrefetchChunk;
-    const int64_t bytes = row_bytes - off < kPrefetchChunk ? row_bytes - off : kPrefetchChunk;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(weights + (int64_t)s_src[j] * row_bytes + off);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(slots + (int64_t)s_dst[j] * row_bytes + off);
-    const int32_t nv = (int32_t)(bytes / 16);
-    u32x4 v[kPrefetchUnroll];
+    const int64_t off = (q - (int64_t)j * cpr) * kChunk;
+    const int64_t bytes = row_bytes - off < kChunk ? row_bytes - off : kChunk;
+    const V *src = reinterpret_cast<const V *>(weights + (int64_t)s_src[j] * row_bytes + off);
+    V *dst = reinterpret_cast<V *>(slots + (int64_t)s_dst[j] * row_bytes + off);
+    const int32_t nv = (int32_t)(bytes / (int64_t)sizeof(V));
+    V v[kPrefetchUnroll];
 #pragma unroll
     for (int u = 0; u < kPrefetchUnroll; ++u) {
       const int32_t x = u * kPrefetchThreads + tid;
@@ -90,13 +96,20 @@ hipError_t launch_prefetch(const Geometry &g, const Workspace &ws, const uint8_t
                            int64_t row_bytes, uint8_t *slots, hipStream_t s) {
   if ((int64_t)g.R * g.S == 0 || row_bytes == 0) return hipSuccess;
   const int32_t max_segments = g.E + g.R;
-  const int64_t cpr = (row_bytes + kPrefetchChunk - 1) / kPrefetchChunk;
+  const bool wide = row_bytes % 16 == 0;
+  const int64_t chunk = wide ? prefetch_chunk<u32x4>() : prefetch_chunk<uint32_t>();
+  const int64_t cpr = (row_bytes + chunk - 1) / chunk;
   // no more slots can be filled than segments, nor than slots
   const int64_t most = (int64_t)(max_segments < g.R * g.S ? max_segments : g.R * g.S) * cpr;
   const unsigned blocks = (unsigned)(most < kPrefetchMaxBlocks ? most : kPrefetchMaxBlocks);
-  hipLaunchKernelGGL(k_prefetch, dim3(blocks), dim3(kPrefetchThreads), 0, s, weights, slots,
-                     ws.segments, ws.seg_slot, ws.n_segments, max_segments, g.E, g.R, g.S,
-                     row_bytes);
+  if (wide)
+    hipLaunchKernelGGL(k_prefetch<u32x4>, dim3(blocks), dim3(kPrefetchThreads), 0, s, weights,
+                       slots, ws.segments, ws.seg_slot, ws.n_segments, max_segments, g.E, g.R,
+                       g.S, row_bytes);
+  else
+    hipLaunchKernelGGL(k_prefetch<uint32_t>, dim3(blocks), dim3(kPrefetchThreads), 0, s, weights,
+                       slots, ws.segments, ws.seg_slot, ws.n_segments, max_segments, g.E, g.R,
+                       g.S, row_bytes);
   return hipGetLastError();
 }
 

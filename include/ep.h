@@ -312,7 +312,8 @@ ep_status_t ep_dup_grad_reduce(ep_handle_t h, const ep_tensor_t *replica_grads,
  *                 or the scales of FP8 weights: tag FP8_SCALES, fp32.
  * slot_weights:   [R, S, P...] output, same tag and dtype; the 2-D form
  *                 [R*S, P] is accepted too.
- * A row (P elements) must be a multiple of 16 bytes.  Errors:
+ * A row (P elements) must be a multiple of 4 bytes (rows that are a
+ * multiple of 16 bytes take the 16-byte vector path).  Errors:
  * EP_ERR_UNSUPPORTED for a non-STATIC handle, EP_ERR_NOT_PLANNED before
  * ep_plan, EP_ERR_BAD_SHAPE for mismatched sizes.  Reads only the plan
  * tables on the device; enqueues one kernel (none if R*S or P is 0). */

@@ -291,7 +291,8 @@ def test_prefetch_argument_validation(lib):
     assert P(h, w, T(BF16, W, 4, 3, 64), None) == 4      # not [R, S, ...]
     assert P(h, w, T(BF16, W, 4, 2, 32), None) == 4      # rows differ
     assert P(h, w, T(BF16, W, 9, 64), None) == 4         # 2-D form needs R*S rows
-    assert P(h, T(BF16, W, 8, 4), T(BF16, W, 4, 2, 4), None) == 4   # 8-byte rows
+    assert P(h, T(BF16, W, 8, 1), T(BF16, W, 4, 2, 1), None) == 4   # 2-byte rows
+    assert P(h, T(BF16, W, 8, 4), T(BF16, W, 4, 2, 4), None) == 5   # 8-byte rows: the 4-byte path
     assert P(h, w, sl, None) == 5                        # not planned
     assert P(h, w, T(BF16, W, 8, 64), None) == 5         # 2-D form, not planned
     assert P(h, T(FP8, W, 8, 2, 16), T(FP8, W, 4, 2, 2, 16), None) == 5

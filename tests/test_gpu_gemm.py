@@ -73,6 +73,8 @@ CASES = [
     ("static_slots", 600, 32, 4, "static", 0, 8, 4, "training", 128, 160, 1.5, 0.02, 5, True),
     ("static_inference_overflow", 800, 32, 8, "static", 0, 8, 1, "inference", 256, 128, 1.8, 0.0, 6, True),
     ("single_row", 1, 4, 1, "ht", 0, 1, 0, "training", 64, 8, 0.0, 0.0, 7, False),
+    ("ht_n_not_multiple_of_8", 300, 8, 4, "ht", 0, 1, 0, "training", 64, 37, 1.0, 0.0, 9, False),   # per-element epilogue
+    ("static_slots_n_odd", 600, 32, 4, "static", 0, 8, 4, "training", 128, 131, 1.5, 0.02, 10, True),
     ("empty", 0, 8, 2, "ht", 0, 1, 0, "training", 64, 64, 0.0, 0.0, 8, False),
 ]
 

@@ -77,7 +77,9 @@ def _bytes_case(E, R, S, row_bytes, seed):
 
 
 @pytest.mark.parametrize("dtype,P", [(torch.bfloat16, 8), (torch.bfloat16, 20000),
-                                     (torch.float32, 12), (torch.float8_e4m3fn, 70000)])
+                                     (torch.float32, 12), (torch.float8_e4m3fn, 70000),
+                                     # rows that are not a multiple of 16 bytes (4-byte path)
+                                     (torch.float32, 3), (torch.bfloat16, 6), (torch.float32, 5003)])
 @pytest.mark.parametrize("c", PLANS, ids=[c[0] for c in PLANS])
 def test_prefetch_parity(c, dtype, P):
     print(f"[prefetch] copy {c[0]} {dtype} P={P}", flush=True)
@@ -151,3 +153,18 @@ def test_prefetch_training_workload_full_size():
         want = oracle.prefetch(wb, np.array([[0]], np.int32), np.zeros((1, 1, wb.shape[1]), np.uint8))
         assert np.array_equal(got, want[0, 0])
     assert h.status() == 0
+
+
+def test_prefetch_fp8_weight_scales():
+    # the fp32 scales of FP8 weights, tagged FP8_SCALES: [E, N, K/128] rows of
+    # 131 * 2 * 4 = 1048 bytes (not a multiple of 16)
+    c = PLANS[0]
+    g, h, L, _, _ = _planned(c)
+    E, R, S = c[2], c[4], c[5]
+    rng = np.random.default_rng(77)
+    ws = rng.random((E, 131, 2)).astype(np.float32)
+    ss = rng.random((R, S, 131, 2)).astype(np.float32)
+    st = torch.from_numpy(ss).cuda()
+    ep.Buffer(g).prefetch_replicas(torch.from_numpy(ws).cuda(), h, st, scales=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), oracle.prefetch(ws, L.plan.replica, ss))
