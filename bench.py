@@ -47,6 +47,9 @@ def parse():
                         "fp8 MFMA peak)")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
+    p.add_argument("--fused-route", action="store_true",
+                   help="start the step from router logits with routing fused into the layout "
+                        "launch (ep_route_plan instead of ep_route + ep_plan)")
     p.add_argument("--prefetch", action="store_true",
                    help="STATIC workloads: add the replica-weight prefetch of one [4096, 1536] "
                         "bf16 projection per expert after the plan")
@@ -99,6 +102,7 @@ def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P, slot_
         b["dispatch_bwd"] = N * row + N * 4 + c.T * row
         P = 4096 * 1536
         b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
+    b["route_plan"] = b["route"] + b["plan"]
     b["prefetch"] = filled_slots * slot_elems * slot_elem_bytes * 2   # each filled slot: owner row read, slot written
     b["prefetch_scales"] = filled_slots * (slot_elems // 128) * 4 * 2  # FP8 weights: their fp32 scales
     return b
@@ -193,8 +197,8 @@ def run_microbatches(a):
     import workloads
 
     name, M = a.workload, a.microbatches
-    if name == "training" or a.route or a.prefetch or a.gemm or a.graph or a.cold:
-        print("bench.py: --microbatches times the forward chain only (no training, --route, "
+    if name == "training" or a.route or a.fused_route or a.prefetch or a.gemm or a.graph or a.cold:
+        print("bench.py: --microbatches times the forward chain only (no training, --route, --fused-route, "
               "--prefetch, --gemm, --graph or --cold)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda", 0)
@@ -417,11 +421,15 @@ def main():
 
     LS = {"s": stream}   # the stream the library calls launch on (a capture stream under --graph)
     ops = []
-    if a.route:   # the pass starts from router logits: plan and combine use the routed outputs
+    if a.route or a.fused_route:   # the pass starts from router logits: plan and combine use the routed outputs
         logits = torch.from_numpy(inp.logits).to(dev)
         idx, w = torch.empty_like(idx), torch.empty_like(w)
-        ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, LS["s"])))
-    ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, LS["s"])))
+    if a.fused_route:
+        ops.append(("route_plan", lambda: ep.ep_route_plan(h.ptr, logits, idx, w, LS["s"])))
+    else:
+        if a.route:
+            ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, LS["s"])))
+        ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, LS["s"])))
     slot_elems = a.gemm * c.H if a.gemm else PREFETCH_P
     slots = None
     if a.gemm:   # one [N, H] projection per expert, the GEMM's weights
@@ -611,7 +619,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
-                   "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route,
+                   "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route or a.fused_route,
                    "hip_graph": a.graph},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
         **({"gemm": gemm_info} if gemm_info else {}),

@@ -26,7 +26,7 @@ __all__ = [
     "FLAG_SLOT_BUDGET", "Group", "Handle", "Buffer", "library_path", "load_library",
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
-    "ep_handle_status", "ep_route", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
+    "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
@@ -105,6 +105,7 @@ def load_library():
         "ep_handle_query": (S, [c_void_p, POINTER(ep_handle_view_t)]),
         "ep_handle_status": (S, [c_void_p, c_void_p, POINTER(c_uint32)]),
         "ep_route": (S, [c_void_p, _T, _T, _T, c_void_p]),
+        "ep_route_plan": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_plan": (S, [c_void_p, _T, c_void_p]),
         "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
@@ -227,6 +228,14 @@ def ep_route(h: int, logits: torch.Tensor, topk_idx: torch.Tensor,
                                    _tensor(topk_idx, TAG_TOPK_IDX),
                                    _tensor(topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)),
            "ep_route")
+
+
+def ep_route_plan(h: int, logits: torch.Tensor, topk_idx: torch.Tensor,
+                  topk_weights: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_route_plan(c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
+                                        _tensor(topk_idx, TAG_TOPK_IDX),
+                                        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)),
+           "ep_route_plan")
 
 
 def ep_plan(h: int, topk_idx: torch.Tensor, stream=None) -> None:
@@ -363,6 +372,15 @@ class Handle:
         idx = torch.empty((self.num_tokens, k), dtype=torch.int32, device=logits.device)
         w = torch.empty((self.num_tokens, k), dtype=torch.float32, device=logits.device)
         ep_route(self.ptr, logits, idx, w, stream)
+        return idx, w
+
+    def route_plan(self, logits: torch.Tensor, stream=None):
+        """Routing and the layout of its ids in one pass (ep_route + ep_plan,
+        one launch fewer): returns (topk_idx, weights); the handle is planned."""
+        k = self.group.top_k
+        idx = torch.empty((self.num_tokens, k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((self.num_tokens, k), dtype=torch.float32, device=logits.device)
+        ep_route_plan(self.ptr, logits, idx, w, stream)
         return idx, w
 
     def plan(self, topk_idx: torch.Tensor, stream=None) -> "Handle":

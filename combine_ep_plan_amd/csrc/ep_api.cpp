@@ -285,6 +285,27 @@ ep_status_t ep_route(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk
                                       as_stream(stream)));
 }
 
+ep_status_t ep_route_plan(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk_idx,
+                          ep_tensor_t *topk_weights, void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(logits, EP_TAG_ROUTER_LOGITS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(logits, g.T, g.E)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(topk_idx, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_idx, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = check_tensor(topk_weights, EP_TAG_TOPK_WEIGHTS, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_weights, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = hip_status(epk::launch_route_plan(g, h->ws, static_cast<const float *>(logits->data),
+                                         static_cast<int32_t *>(topk_idx->data),
+                                         static_cast<float *>(topk_weights->data),
+                                         as_stream(stream)));
+  if (st == EP_OK) h->planned = true;
+  return st;
+}
+
 ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream) {
   if (!h) return EP_ERR_INVALID_ARG;
   const epk::Geometry &g = h->geo;

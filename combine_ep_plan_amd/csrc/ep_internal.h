@@ -68,6 +68,10 @@ size_t plan_lds_bytes(int32_t E, int32_t R);
 // Launchers (return the HIP error of the launch).
 hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,
                        hipStream_t s);
+// routing (launch_route's rule) and the layout of its ids in one layout
+// launch when E allows, else routing then layout
+hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float *logits,
+                             int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                 int32_t H, uint16_t *recv, hipStream_t s);
 hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uint16_t *x,

@@ -21,13 +21,17 @@
 // follows from counts (LL), load (STATIC) or offsets[E] (HT).
 #include "device.h"
 #include "ep_internal.h"
+#include "route_impl.h"
 
 namespace epk {
 
 struct PlanArgs {
   Geometry g;
   Workspace ws;
-  const int32_t *idx;
+  const int32_t *idx;     // top-k ids [T, k] (read when the layout kernel does not route)
+  const float *logits;    // fused routing: router logits [T, E]
+  int32_t *idx_out;       // fused routing: top-k ids and weights written here
+  float *w_out;
 };
 
 // In-place exclusive scan of a[0, n) in LDS by the 64 lanes of the calling
@@ -257,6 +261,11 @@ __host__ __device__ inline int32_t plan_region_a(int32_t E, int32_t R) {
   return waves > planner ? waves : planner;
 }
 
+// RG > 0: the tile first routes the tokens its entries belong to (RG lanes
+// per token, RPER logits per lane; route_impl.h), writes their ids and
+// weights and ranks them from LDS: routing and the tile histogram in one
+// launch.  RG = 0: the ids come from a.idx.
+template <int RG, int RPER>
 __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   extern __shared__ int32_t lds[];
   __shared__ uint32_t s_flags;
@@ -271,18 +280,42 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   int32_t *pl = lds;                                     // planner tables (after ranking)
   int32_t *cnt = lds + plan_region_a(E, g.layout == kStatic ? g.R : 0);   // [E]
   int32_t *offs = cnt + E;                               // [E+1]
+  int32_t *s_idx = offs + E + 1;                         // RG > 0: the tile's routed ids
 
   for (int i = tid; i < kTileWaves * E; i += kTileThreads) wcnt[i] = 0;
   if (tid == 0) s_flags = 0;
+  const int64_t f0 = (int64_t)blockIdx.x * kTileEntries;   // the tile's first entry
+  if constexpr (RG > 0) {
+    // The tokens whose entries fall in [f0, f1); a token split between two
+    // tiles is routed by both (same result), each keeping its own entries.
+    const int64_t f1 = f0 + kTileEntries < g.n ? f0 + kTileEntries : g.n;
+    const int64_t t0 = f0 / g.k, t1 = (f1 + g.k - 1) / g.k;
+    constexpr int kPass = kTileThreads / RG;   // tokens per pass
+    const int sub = lane & (RG - 1);
+    for (int64_t tb = t0; tb < t1; tb += kPass) {
+      const int64_t t = tb + tid / RG;
+      const bool live = t < t1;
+      int32_t ri;
+      float rw;
+      route_token<RG, RPER>(a.logits, live ? t : t0, live, E, g.k, lane, ri, rw);
+      const int64_t f = t * g.k + sub;
+      if (live && sub < g.k && f >= f0 && f < f1) {
+        a.idx_out[f] = ri;
+        a.w_out[f] = rw;
+        s_idx[f - f0] = ri;
+      }
+    }
+  }
   __syncthreads();
 
-  const int64_t wbase = (int64_t)blockIdx.x * kTileEntries + (int64_t)w * (64 * kTileChunks);
+  const int64_t wbase = f0 + (int64_t)w * (64 * kTileChunks);
   int32_t ev[kTileChunks], rr[kTileChunks];
   uint32_t flags = 0;
 #pragma unroll
   for (int c = 0; c < kTileChunks; ++c) {   // all loads in flight before any ranking
     const int64_t f = wbase + c * 64 + lane;
-    ev[c] = f < g.n ? a.idx[f] : -1;
+    if constexpr (RG > 0) ev[c] = f < g.n ? s_idx[f - f0] : -1;
+    else ev[c] = f < g.n ? a.idx[f] : -1;
   }
 #pragma unroll
   for (int c = 0; c < kTileChunks; ++c) {
@@ -442,19 +475,52 @@ size_t plan_lds_bytes(int32_t E, int32_t R) {
   return (size_t)(plan_region_a(E, R) + 2 * E + 1) * sizeof(int32_t);
 }
 
-hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,
-                       hipStream_t s) {
-  PlanArgs a{g, ws, topk_idx};
-  const size_t lds = plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0);
-  hipLaunchKernelGGL(k_plan_tiles, dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+static hipError_t launch_plan_dst(const Geometry &g, const PlanArgs &a, hipStream_t s) {
   if (g.ntiles > 1) {
     const int64_t blocks = (g.n + 255) / 256;
     hipLaunchKernelGGL(k_plan_dst, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    err = hipGetLastError();
   }
-  return err;
+  return hipGetLastError();
+}
+
+// Fused routing + layout: 16 lanes per token, up to 32 logits per lane
+// (E <= 512); larger E routes in its own launch first.
+constexpr int kFusedRouteLanes = 16;
+constexpr int kFusedRouteMaxPer = 32;
+
+hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float *logits,
+                             int32_t *idx, float *w, hipStream_t s) {
+  const int per = (g.E + kFusedRouteLanes - 1) / kFusedRouteLanes;
+  if (per > kFusedRouteMaxPer) {
+    hipError_t err = launch_route(logits, g.T, g.E, g.k, idx, w, s);
+    return err != hipSuccess ? err : launch_plan(g, ws, idx, s);
+  }
+  PlanArgs a{g, ws, idx, logits, idx, w};
+  const size_t lds =
+      plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0) + (size_t)kTileEntries * sizeof(int32_t);
+#define L(P)                                                                                    \
+  hipLaunchKernelGGL((k_plan_tiles<kFusedRouteLanes, P>), dim3(g.ntiles), dim3(kTileThreads), \
+                     lds, s, a)
+  if (per <= 1) L(1);
+  else if (per <= 2) L(2);
+  else if (per <= 4) L(4);
+  else if (per <= 8) L(8);
+  else if (per <= 16) L(16);
+  else L(32);
+#undef L
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_plan_dst(g, a, s);
+}
+
+hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *topk_idx,
+                       hipStream_t s) {
+  PlanArgs a{g, ws, topk_idx, nullptr, nullptr, nullptr};
+  const size_t lds = plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0);
+  hipLaunchKernelGGL((k_plan_tiles<0, 0>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_plan_dst(g, a, s);
 }
 
 }  // namespace epk

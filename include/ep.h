@@ -214,6 +214,23 @@ ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
 ep_status_t ep_route(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk_idx,
                      ep_tensor_t *topk_weights, void *stream);
 
+/* Routing and layout together: the result of ep_route followed by ep_plan
+ * on its topk_idx, with the routing done inside the layout kernel (the
+ * fused top-k + routing operator of the "Ultra-Large MoE Models" article,
+ * sections 3.1-3.2, carrying on into the per-expert histogram of the NCCL
+ * EP listing's Table III layouts): the tile of entries a workgroup ranks is
+ * routed by that workgroup, so the ids are ranked from LDS and the pass
+ * takes one launch fewer.  Same arguments, outputs and errors as ep_route;
+ * afterwards the handle is planned as by ep_plan.  E > 512 routes in a
+ * launch of its own first (same results).
+ * Cost: the routing then runs on the layout's workgroups (one per 2048
+ * entries) instead of one per few tokens, so this is faster than ep_route +
+ * ep_plan only when the routing work per tile is small (a few tokens times
+ * few experts, such as T = 64, E = 8, k = 2); for decode-sized batches with
+ * hundreds of experts the two calls are faster. */
+ep_status_t ep_route_plan(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t *topk_idx,
+                          ep_tensor_t *topk_weights, void *stream);
+
 /* Layout (and, for EP_LAYOUT_STATIC, the static-shape plan) of one pass.
  * topk_idx: int32 [T, k], tag EP_TAG_TOPK_IDX.  Writes counts, offsets,
  * dst, recv_src (rows that hold an entry) and the status word; STATIC also

@@ -101,3 +101,79 @@ def test_route_signed_zero_and_infinities():
     gi, _ = _route_gpu(big, k)
     ri, _ = oracle.route(big, k)
     assert np.array_equal(gi, ri)
+
+
+# ---------------------------------------------------------------------------
+# routing fused into the layout launch (ep_route_plan)
+# ---------------------------------------------------------------------------
+
+from tests.gpu_util import check_layout  # noqa: E402
+
+
+# name, T, E, k, layout, cap, R, S, logit skew
+FUSED = [
+    ("decode_ll", 128, 256, 8, "ll", 64, 1, 0, 1.0),
+    ("prefill_ht_tiles", 4096, 256, 8, "ht", 0, 1, 0, 1.1),
+    ("static_k3_split_tokens", 1500, 64, 3, "static", 0, 8, 4, 1.5),   # 2048 % 3 != 0: tokens span tiles
+    ("static_k6_inference", 1000, 48, 6, "static", 0, 6, 1, 2.0),
+    ("ht_e384_per32", 700, 384, 8, "ht", 0, 1, 0, 0.5),
+    ("ll_e1024_unfused", 300, 1024, 16, "ll", 8, 1, 0, 1.0),            # E > 512: two launches
+    ("ht_e5_k7", 50, 5, 7, "ht", 0, 1, 0, 0.0),                        # fewer experts than k
+    ("empty", 0, 16, 4, "ht", 0, 1, 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("c", FUSED, ids=[c[0] for c in FUSED])
+def test_route_plan_matches_route_then_plan_and_oracle(c):
+    name, T, E, k, kind, cap, R, S, skew = c
+    print(f"[route_plan] {name} T={T} E={E} k={k} {kind}", flush=True)
+    rng = np.random.default_rng(4000 + T + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if skew:
+        lg += workloads.zipf_bias(E, skew)[None, :].astype(np.float32)
+    lg[: T // 4, :: 7] = np.round(lg[: T // 4, :: 7], 1)   # ties inside a token
+    mode = "inference" if "inference" in name else "training"
+    g = make_group(E, R, 8, k, T, kind, cap, S, mode)
+    hf, hs = ep.Handle(g, T), ep.Handle(g, T)
+    logits = dev_f32(lg)
+    fi, fw = hf.route_plan(logits)
+    si, sw = hs.route(logits)
+    hs.plan(si)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fi), host(si))
+    assert np.array_equal(host(fw).view(np.uint32), host(sw).view(np.uint32))
+    tf = {key: host(v) for key, v in hf.tables().items()}
+    ts = {key: host(v) for key, v in hs.tables().items()}
+    ns = int(tf["n_segments"][0]) if "n_segments" in tf else 0
+    used = tf["dst"][tf["dst"] >= 0]
+    for key in tf:
+        a, b = tf[key], ts[key]
+        if key in ("segments", "seg_slot"):      # defined up to n_segments
+            a, b = a[:ns], b[:ns]
+        elif key == "recv_src":                  # defined on the rows that hold an entry
+            a, b = a[used], b[used]
+        assert np.array_equal(a, b), key
+    assert hf.status() == hs.status()
+    ri, rw = oracle.route(lg, k)
+    assert np.array_equal(host(fi), ri)
+    m = ri >= 0
+    assert np.all(np.abs(host(fw)[m] - rw[m]) <= W_TOL * rw[m] + 1e-30)
+    L = oracle.layout(ri, E, kind, cap=cap, R=R, S=S,
+                      slot_mode=oracle.SLOTS_INFERENCE if mode == "inference" else oracle.SLOTS_TRAINING)
+    check_layout(hf, L, kind, ri, None)
+
+
+def test_route_plan_then_the_whole_pass():
+    # route+plan fused, dispatch, combine with identity experts: x comes back
+    inp = workloads.make_inputs("prefill")
+    c = inp.cfg
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht")
+    h = ep.Handle(g, c.T)
+    idx, w = h.route_plan(dev_f32(inp.logits))
+    buf = ep.Buffer(g)
+    x = dev_bf16(inp.x)
+    recv, _, _, _, _ = buf.dispatch(x, idx, w, handle=h, recv_meta=False)
+    y = buf.combine(recv, h, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), inp.topk_idx)
+    assert same_up_to_zero_sign_np(host_bits(y), inp.x)
