@@ -249,12 +249,13 @@ def test_dup_reduce_argument_validation(lib):
     lib.ep_group_destroy(g)
 
 
-def test_route_argument_validation(lib):
+@pytest.mark.parametrize("entry", ["ep_route", "ep_route_plan"])
+def test_route_argument_validation(lib, entry):
     g, h, _ = make_handle(lib)
     lg = T(F32, ep.TAG_ROUTER_LOGITS, 64, 8)
     idx = T(I32, ep.TAG_TOPK_IDX, 64, 2)
     w = T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2)
-    Rt = lib.ep_route
+    Rt = getattr(lib, entry)
     assert Rt(h, T(F32, ep.TAG_TOKENS, 64, 8), idx, w, None) == 2
     assert Rt(h, T(BF16, ep.TAG_ROUTER_LOGITS, 64, 8), idx, w, None) == 3
     assert Rt(h, T(F32, ep.TAG_ROUTER_LOGITS, 64, 9), idx, w, None) == 4
