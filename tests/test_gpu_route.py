@@ -177,3 +177,13 @@ def test_route_plan_then_the_whole_pass():
     torch.cuda.synchronize()
     assert np.array_equal(host(idx), inp.topk_idx)
     assert same_up_to_zero_sign_np(host_bits(y), inp.x)
+
+
+def test_route_large_logits():
+    # logits near +-1000: the softmax over the chosen ones must use their
+    # differences (exp of the raw values overflows fp32)
+    rng = np.random.default_rng(91)
+    lg = (rng.standard_normal((300, 64)) + 1000.0 * rng.choice([-1.0, 1.0], size=(300, 1))).astype(np.float32)
+    _check(lg, 6)
+    _, gw = _route_gpu(lg, 6)
+    assert np.all(np.isfinite(gw))

@@ -842,3 +842,17 @@ def test_grouped_gemm_fp8_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.grouped_gemm_fp8(x, np.ones((4, 1), np.float32), np.zeros((1, 2, 128), np.uint8),
                                 np.ones((1, 2, 1), np.float32), np.array([[2, 4, 0]], np.int32))
+
+
+def test_route_softmax_of_large_logits_is_the_closed_form():
+    # the softmax over the chosen logits depends only on their differences:
+    # logits near 1000 (exp overflows in double without the shift) give the
+    # same weights as the same differences near 0
+    lg = np.array([[1000.0, 999.0, 0.0, 998.5], [1.0, 0.0, -1000.0, -0.5]], np.float32)
+    idx, w = oracle.route(lg, 3)
+    assert idx.tolist() == [[0, 1, 3], [0, 1, 3]]
+    z = np.exp(np.array([0.0, -1.0, -1.5]))
+    want = z / z.sum()
+    assert np.all(np.isfinite(w))
+    assert np.allclose(w[0], want, rtol=1e-6, atol=0)
+    assert np.allclose(w[1], want, rtol=1e-6, atol=0)
