@@ -7,7 +7,8 @@ when H allows) -> combine -> combine backward -> dispatch backward via the C
 ABI and is compared with the oracle: tables, dispatched rows, FP8 codes and
 scales and combine-backward rows bit-exact; combine, dispatch backward and
 grad_w as in the parity tests (one bf16 ulp elementwise and 2e-3
-norm-wise)."""
+norm-wise).  A second sweep runs both grouped GEMMs (bf16 and FP8) on random
+K, N, layouts and prefetch slots, to the GEMM tests' tolerances."""
 
 from __future__ import annotations
 
@@ -102,3 +103,82 @@ def test_random_configuration(seed):
     rx = bf16_bits_to_f32(oracle.combine(eo_bits, L.dst, None)).astype(np.float64)
     assert rel_err(bf16_bits_to_f32(host_bits(gx)).astype(np.float64), rx) <= 2e-3
     assert h.status() == L.flags
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMMs (bf16 and FP8) on random shapes and layouts
+# ---------------------------------------------------------------------------
+
+N_GEMM = 16
+
+
+def draw_gemm(seed: int) -> dict:
+    rng = np.random.default_rng(91_000 + seed)
+    R = int(rng.choice([1, 2, 4, 8]))
+    E = R * int(rng.choice([1, 2, 4, 8]))
+    k = min(int(rng.choice([1, 2, 4, 8])), E)
+    kind = str(rng.choice(["ll", "ht", "static"]))
+    T = int(rng.choice([0, 1, 33, 200, 700, 1500]))
+    cap = int(rng.integers(1, max(2, (T * k) // E + 8))) if kind == "ll" else 0
+    S = int(rng.integers(0, 3)) if kind == "static" else 0
+    mode = str(rng.choice(["training", "inference"])) if kind == "static" else "training"
+    K = 128 * int(rng.integers(1, 5))
+    N = int(rng.choice([1, 8, 37, 64, 128, 200, 257]))
+    return dict(R=R, E=E, k=k, kind=kind, T=T, cap=cap, S=S, mode=mode, K=K, N=N,
+                skew=float(rng.choice([0.0, 1.5])), slots=bool(kind == "static" and S > 0 and rng.random() < 0.7))
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("seed", range(N_GEMM))
+def test_random_grouped_gemm(seed, fp8):
+    from tests.test_gpu_gemm import check_gemm
+    from tests.test_gpu_gemm_fp8 import check_gemm_fp8, dev_u8, finite_codes, host_u8
+    c = draw_gemm(seed)
+    print(f"[random gemm] fp8={fp8} {c}", flush=True)
+    E, R, k, kind, T, cap, S, K, N = c["E"], c["R"], c["k"], c["kind"], c["T"], c["cap"], c["S"], c["K"], c["N"]
+    idx, _, _ = workloads.random_case(6000 + seed, T, 8, E, k, skew=c["skew"])
+    g = make_group(E, R, 8, k, T, kind, cap, S, c["mode"])
+    h = ep.Handle(g, T)
+    h.plan(dev_i32(idx))
+    slot_mode = oracle.SLOTS_INFERENCE if c["mode"] == "inference" else oracle.SLOTS_TRAINING
+    L = oracle.layout(idx, E, kind, cap=cap, R=R, S=S, slot_mode=slot_mode)
+    groups = oracle.expert_groups(L, kind, E, cap=cap, R=R, S=S, use_slots=c["slots"])
+    rng = np.random.default_rng(seed)
+    buf = ep.Buffer(g)
+    SENT = 0x7F7F
+    y = torch.full((L.rows, N), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    if not fp8:
+        xb = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, K)).astype(np.float32))
+        wb = workloads.f32_to_bf16_bits((rng.standard_normal((E, N, K)) / np.sqrt(K)).astype(np.float32))
+        wt = dev_bf16(wb.reshape(E, N * K)).view(E, N, K)
+        slots = buf.prefetch_replicas(wt, h) if c["slots"] else None
+        buf.expert_gemm(dev_bf16(xb), wt, h, slots, out=y)
+        torch.cuda.synchronize()
+        w_all = wb
+        if c["slots"]:
+            w_all = np.concatenate([wb, host_bits(slots).reshape(R * S, N, K)])
+        ref = oracle.grouped_gemm(xb, w_all, groups, np.full((L.rows, N), SENT, np.uint16))
+        check_gemm(host_bits(y), ref, xb, w_all, groups)
+    else:
+        NB = K // 128
+        x = finite_codes(rng, (L.rows, K))
+        sx = (rng.random((L.rows, NB)) * 2.0 ** -3).astype(np.float32)
+        w = finite_codes(rng, (E, N, K))
+        sw = (rng.random((E, N, NB)) * 2.0 ** -8).astype(np.float32)
+        wt, swt = dev_u8(w), dev_f32(sw)
+        slots = slot_sc = None
+        if c["slots"]:
+            slots = buf.prefetch_replicas(wt, h)
+            slot_sc = buf.prefetch_replicas(swt, h, scales=True)
+        buf.expert_gemm_fp8(dev_u8(x), dev_f32(sx), wt, swt, h, slots, slot_sc, out=y)
+        torch.cuda.synchronize()
+        w_all, sw_all = w, sw
+        if c["slots"]:
+            w_all = np.concatenate([w, host_u8(slots).reshape(R * S, N, K)])
+            sw_all = np.concatenate([sw, host(slot_sc).reshape(R * S, N, NB)])
+        ref = oracle.grouped_gemm_fp8(x, sx, w_all, sw_all, groups, np.full((L.rows, N), SENT, np.uint16))
+        check_gemm_fp8(host_bits(y), ref, x, sx, w_all, sw_all, groups)
+    covered = np.zeros(L.rows, bool)
+    for r0, n, _ in groups:
+        covered[r0:r0 + n] = True
+    assert np.all(host_bits(y)[~covered] == SENT)
