@@ -357,7 +357,7 @@ def run_microbatches(a):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); logical "
+        print(f"bench.py: the library runs on one GPU only (got --gpus {a.gpus}); logical "
               "expert-parallel ranks are regions of that GPU's HBM.", file=sys.stderr)
         sys.exit(2)
     if a.microbatches > 1 or a.overlap:

@@ -64,7 +64,7 @@ typedef enum ep_status {
   EP_ERR_BAD_SHAPE = 4,
   EP_ERR_NOT_PLANNED = 5,         /* dispatch/combine before any ep_plan on the handle */
   EP_ERR_WORKSPACE_TOO_SMALL = 6,
-  EP_ERR_UNSUPPORTED = 7,         /* a valid request this build does not serve */
+  EP_ERR_UNSUPPORTED = 7,         /* a valid request the library does not serve */
   EP_ERR_HIP = 8                  /* a HIP launch or copy failed */
 } ep_status_t;
 
