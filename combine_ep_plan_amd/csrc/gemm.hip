@@ -8,11 +8,23 @@
 // (an expert's rows, or a STATIC segment through its prefetch slot):
 //   Y[row][n] = bf16( sum_c X[row][c] * W[n][c] ),  fp32 accumulation.
 //
-// Two kernels:
+// Kernels:
 //  * k_gemm_tiles (one workgroup) cuts the groups of the current plan into
-//    row tiles of kGemmBM rows -- (row0, rows, weight index) -- with a prefix
-//    sum over the groups, so the GEMM grid can have a fixed size;
-//  * k_grouped_gemm: one 256-thread workgroup per (row tile, 128 columns),
+//    row tiles -- (row0, rows, weight index) -- with a prefix sum over the
+//    groups, so the GEMM grid can have a fixed size;
+//  * k_grouped_gemm_256 for large groups (at least 128 rows per expert on
+//    average) and N >= 256: one 256-thread workgroup per CU and per
+//    (256-row tile, 256 columns); each wave owns a 128 x 128 block as 4 x 4
+//    MFMA accumulators (256 accumulation registers), which halves the LDS
+//    bytes read per flop against the 128 x 128 tile -- LDS bandwidth, not
+//    the matrix cores, is what bounds these kernels.  Loads are buffer loads
+//    (a scalar resource and one 32-bit offset per lane); the next slab is
+//    staged in registers, and its LDS writes and the global loads of the one
+//    after go under the first two 16-deep steps' MFMAs, the LDS reads of the
+//    next step under the first half of each step, and the one barrier per
+//    slab sits before the last step, so the first reads of the next slab run
+//    under that step's MFMAs;
+//  * k_grouped_gemm: one 256-thread workgroup per (128-row tile, 128 columns),
 //    two per CU; four waves in a 2 x 2 arrangement, each owning a 64 x 64
 //    block of the output as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.
 //    Slabs 64 deep of X and W go through LDS, double-buffered.  Pipelining:
@@ -95,6 +107,7 @@ __device__ __forceinline__ void group_of(const TileArgs &a, int32_t q, int32_t &
   }
 }
 
+template <int TM>
 __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_tiles) {
   __shared__ int32_t s_wave[16];
   __shared__ int32_t s_base;
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
     const int32_t q = q0 + tid;
     int32_t row0 = 0, rows = 0, widx = 0;
     if (q < ngroups) group_of(a, q, row0, rows, widx);
-    const int32_t nt = rows > 0 ? (rows + kTileM - 1) / kTileM : 0;
+    const int32_t nt = rows > 0 ? (rows + TM - 1) / TM : 0;
     // inclusive scan of nt over the workgroup: lanes, then waves
     int32_t x = nt;
 #pragma unroll
@@ -126,8 +139,8 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
     int32_t t = before + x - nt;
     for (int32_t i = 0; i < nt && t < max_tiles; ++i, ++t) {
       int32_t *e = a.ws.gemm_tiles + (int64_t)t * 4;
-      e[0] = row0 + i * kTileM;
-      e[1] = rows - i * kTileM < kTileM ? rows - i * kTileM : kTileM;
+      e[0] = row0 + i * TM;
+      e[1] = rows - i * TM < TM ? rows - i * TM : TM;
       e[2] = widx;
       e[3] = 0;
     }
@@ -315,6 +328,214 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
       for (int r = 0; r < 16; r += 2) {
         const int row = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);  // rows row, row + 1
+        if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
+        if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grouped GEMM, 256 x 256 tiles (large groups)
+
+constexpr int kBM2 = 256, kBN2 = 256;                     // tile
+constexpr int kWTM2 = kBM2 / 2, kWTN2 = kBN2 / 2;         // one wave's block (2 x 2 waves)
+constexpr int kFM2 = kWTM2 / 32, kFN2 = kWTN2 / 32;       // 4 x 4 MFMA accumulators per wave
+constexpr int kLoads2 = kBM2 * kChunks / kGemmThreads;    // 16-byte loads per thread per slab of X
+constexpr int kLoadsB2 = kBN2 * kChunks / kGemmThreads;   // ... and of W
+constexpr int kSlabA2 = kBM2 * kChunks, kSlabB2 = kBN2 * kChunks;
+constexpr int kBufDword3 = 0x00020000;                    // buffer resource word 3 (raw, 32-bit data)
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
+    const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
+    int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
+  // two 64-deep slabs of X and W (128 KB), then the bf16 output tile
+  __shared__ u32x4 lds[2 * kSlabA2 + 2 * kSlabB2];
+  u32x4 *const sa = lds, *const sb = lds + 2 * kSlabA2;
+  const int32_t valid = *ntiles * n_col_tiles;
+  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
+  const int32_t slot = blockIdx.x / kXcds;
+  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || lid >= valid) return;
+  const int32_t tile = lid / n_col_tiles;
+  const int32_t n0 = (lid - tile * n_col_tiles) * kBN2;
+  const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
+  const int64_t KV = K / 8;  // 16-byte vectors per row
+  const u32x4 *Xt = X + (int64_t)row0 * KV;
+  const u32x4 *Wt = (widx < E ? W + (int64_t)widx * N * KV : Wslot + (int64_t)(widx - E) * N * KV) +
+                    (int64_t)n0 * KV;
+  const int32_t wrows = N - n0 < kBN2 ? N - n0 : kBN2;
+  // Buffer resources over the tile's rows of X and W.  Every offset below is
+  // in range by construction (rows past the end are clamped to the last
+  // row); the hardware range check is a second guard.
+  const __amdgpu_buffer_rsrc_t rX =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Xt, (short)0, rows * K * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rW =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Wt, (short)0, wrows * K * 2, kBufDword3);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int c_ld = tid & (kChunks - 1);
+  // byte offsets of this thread's chunks: chunk q = tid + i * 256 of a slab
+  // is row q / 8, 16-byte chunk q % 8; rows past the tile's end read the last
+  // row (their products land in outputs that are never stored)
+  int32_t oa[kLoads2], ob[kLoadsB2];
+#pragma unroll
+  for (int i = 0; i < kLoads2; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    oa[i] = ((r < rows ? r : rows - 1) * (int32_t)KV + c_ld) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsB2; ++i) {
+    const int r = (tid + i * kGemmThreads) / kChunks;
+    ob[i] = ((r < wrows ? r : wrows - 1) * (int32_t)KV + c_ld) * 16;
+  }
+  u32x4 ra[kLoads2], rb[kLoadsB2];
+#define GLOAD_A(kt)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < kLoads2; ++i) ra[i] =                                  \
+      __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, oa[i], (kt) * 128, 0));
+#define GLOAD_B(kt)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i) rb[i] =                                 \
+      __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, ob[i], (kt) * 128, 0));
+#define SWRITE_A(buf)                                                                          \
+  _Pragma("unroll") for (int i = 0; i < kLoads2; ++i)                                          \
+      sa[(buf) * kSlabA2 + swz((tid + i * kGemmThreads) / kChunks, c_ld)] = ra[i];
+#define SWRITE_B(buf)                                                                          \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i)                                         \
+      sb[(buf) * kSlabB2 + swz((tid + i * kGemmThreads) / kChunks, c_ld)] = rb[i];
+#define READK(FA, FB, buf, kk)                                                                 \
+  {                                                                                            \
+    const int c_ = (kk) * 2 + (lane >> 5);                                                     \
+    _Pragma("unroll") for (int i = 0; i < kFM2; ++i) FA[i] = __builtin_bit_cast(               \
+        bf16x8, sa[(buf) * kSlabA2 + swz(wm * kWTM2 + i * 32 + (lane & 31), c_)]);            \
+    _Pragma("unroll") for (int j = 0; j < kFN2; ++j) FB[j] = __builtin_bit_cast(               \
+        bf16x8, sb[(buf) * kSlabB2 + swz(wn * kWTN2 + j * 32 + (lane & 31), c_)]);            \
+  }
+#define MFMAK(FA, FB)                                                                          \
+  _Pragma("unroll") for (int i = 0; i < kFM2; ++i)                                             \
+  _Pragma("unroll") for (int j = 0; j < kFN2; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
+#define SGB(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
+// the next step's 8 LDS reads over the first 8 of a step's 16 MFMAs ...
+#define SCHED_READS()                                                                          \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }              \
+  SGB(0x008, 8);
+// ... and, in the first two steps, 8 LDS writes and 8 global loads over the other 8
+#define SCHED_READS_WRITES_LOADS()                                                             \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }              \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); }
+
+  f32x16 acc[kFM2][kFN2];
+#pragma unroll
+  for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int KT = K / kBK;
+  bf16x8 fa0[kFM2], fb0[kFN2], fa1[kFM2], fb1[kFN2];
+  GLOAD_A(0);
+  GLOAD_B(0);
+  SWRITE_A(0);
+  SWRITE_B(0);
+  if (KT > 1) {
+    GLOAD_A(1);
+    GLOAD_B(1);
+  }
+  __syncthreads();
+  READK(fa0, fb0, 0, 0);
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) {  // steady state: slab kt in LDS, slab kt + 1 in registers
+    const int buf = kt & 1;
+    READK(fa1, fb1, buf, 1);
+    SWRITE_A(buf ^ 1);
+    GLOAD_A(kt + 2);
+    MFMAK(fa0, fb0);
+    SCHED_READS_WRITES_LOADS();
+    READK(fa0, fb0, buf, 2);
+    SWRITE_B(buf ^ 1);
+    GLOAD_B(kt + 2);
+    MFMAK(fa1, fb1);
+    SCHED_READS_WRITES_LOADS();
+    READK(fa1, fb1, buf, 3);
+    MFMAK(fa0, fb0);
+    SCHED_READS();
+    __syncthreads();  // slab kt + 1 is in LDS; every wave is done reading slab kt
+    READK(fa0, fb0, buf ^ 1, 0);
+    MFMAK(fa1, fb1);
+    SCHED_READS();
+  }
+  for (; kt < KT; ++kt) {  // the last two slabs (no more global loads)
+    const int buf = kt & 1;
+    READK(fa1, fb1, buf, 1);
+    MFMAK(fa0, fb0);
+    READK(fa0, fb0, buf, 2);
+    MFMAK(fa1, fb1);
+    READK(fa1, fb1, buf, 3);
+    MFMAK(fa0, fb0);
+    if (kt + 1 < KT) {
+      SWRITE_A(buf ^ 1);
+      SWRITE_B(buf ^ 1);
+      __syncthreads();
+      READK(fa0, fb0, buf ^ 1, 0);
+    }
+    MFMAK(fa1, fb1);
+  }
+#undef SCHED_READS_WRITES_LOADS
+#undef SCHED_READS
+#undef SGB
+#undef MFMAK
+#undef READK
+#undef SWRITE_B
+#undef SWRITE_A
+#undef GLOAD_B
+#undef GLOAD_A
+
+  if ((N & 7) == 0) {
+    // through LDS as bf16 rows of 256 (same chunk swizzle as the 128 x 128
+    // kernel's epilogue), then 16-byte row stores
+    __syncthreads();
+    uint16_t *so = reinterpret_cast<uint16_t *>(lds);
+    static_assert(kBM2 * kBN2 * 2 <= (int)sizeof(lds), "output tile fits the slab buffers");
+#define OSW(r_, cv_) ((r_) * kBN2 + (((cv_) ^ ((((r_) >> 2) & 3) << 2)) << 3))
+#pragma unroll
+    for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN2; ++j) {
+        const int c = wn * kWTN2 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int rr = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+          so[OSW(rr, c >> 3) + (c & 7)] = (uint16_t)(p & 0xFFFFu);
+          so[OSW(rr + 1, c >> 3) + (c & 7)] = (uint16_t)(p >> 16);
+        }
+      }
+    __syncthreads();
+    constexpr int kVecs = kBM2 * kBN2 / 8;
+#pragma unroll 4
+    for (int q = 0; q < kVecs / kGemmThreads; ++q) {
+      const int idx = tid + q * kGemmThreads;
+      const int rr = idx / (kBN2 / 8), cv = idx % (kBN2 / 8);
+      const int col = n0 + cv * 8;
+      if (rr < rows && col < N)
+        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
+            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+    }
+#undef OSW
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN2; ++j) {
+      const int col = n0 + wn * kWTN2 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
         if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
         if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
       }
@@ -564,13 +785,34 @@ int32_t gemm_max_tiles(const Geometry &g) {
   return (int32_t)((g.n + kTileM - 1) / kTileM + groups);
 }
 
+// The 256 x 256 kernel pays off once the groups fill its row tiles: at
+// least 128 receive rows per expert on average, and N of a full column tile.
+// Its buffer offsets are 32-bit: a tile's rows of X must span under 2 GiB.
+static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
+  return N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E && (int64_t)kBM2 * K * 2 <= INT32_MAX;
+}
+
 hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
                                uint16_t *y, hipStream_t s) {
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
-  hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  if (gemm_uses_wide_tiles(g, K, N)) {
+    // at most as many 256-row tiles as the table holds 128-row ones
+    const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
+    const int32_t max2 = (int32_t)((g.n + kBM2 - 1) / kBM2 + groups);
+    hipLaunchKernelGGL(k_gemm_tiles<kBM2>, dim3(1), dim3(1024), 0, s, ta, max2);
+    const int32_t ncol = (N + kBN2 - 1) / kBN2;
+    int64_t blocks = (int64_t)max2 * ncol;
+    blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(k_grouped_gemm_256, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+                       reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
+                       reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
+                       g.E, ncol, y);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_gemm_tiles<kTileM>, dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
   int64_t blocks = (int64_t)max_tiles * ncol;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the XCD remap needs a multiple of 8
@@ -588,7 +830,7 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
-  hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  hipLaunchKernelGGL(k_gemm_tiles<kTileM>, dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
   int64_t blocks = (int64_t)max_tiles * ncol;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;

@@ -2,7 +2,10 @@
 oracle, through the C ABI, on every layout: HT, LL (capacity drops),
 STATIC (kept rows and segments, owner weights or prefetch slots, inference
 overflow), ragged row tiles, column counts that are not a multiple of the
-128-column tile, empty experts, and the full training shapes on sampled rows.
+column tile, empty experts, and the full training shapes on sampled rows.
+Both tile kernels are covered: 128 x 128 tiles for small groups or N < 256,
+256 x 256 tiles once N >= 256 and there are at least 128 rows per expert on
+average (the "wide_" cases and the training shapes).
 
 Tolerance, from the arithmetic: both sides multiply bf16 values exactly; the
 GPU sums K products in fp32 (error <= K * 2^-24 * S with S = sum |x||w|),
@@ -76,6 +79,14 @@ CASES = [
     ("ht_n_not_multiple_of_8", 300, 8, 4, "ht", 0, 1, 0, "training", 64, 37, 1.0, 0.0, 9, False),   # per-element epilogue
     ("static_slots_n_odd", 600, 32, 4, "static", 0, 8, 4, "training", 128, 131, 1.5, 0.02, 10, True),
     ("empty", 0, 8, 2, "ht", 0, 1, 0, "training", 64, 64, 0.0, 0.0, 8, False),
+    # N >= 256 and at least 128 rows per expert on average: the 256 x 256 tile
+    # kernel (K of 1 to 6 slabs of 64, a ragged second column tile, N not a
+    # multiple of 8, LL capacity drops, STATIC slots in both slot modes)
+    ("wide_ht_k384_n320", 2048, 8, 4, "ht", 0, 1, 0, "training", 384, 320, 1.0, 0.02, 11, False),
+    ("wide_static_slots_k256_n264", 1500, 16, 4, "static", 0, 4, 2, "training", 256, 264, 1.5, 0.0, 12, True),
+    ("wide_n_odd_k64", 1200, 4, 2, "ht", 0, 1, 0, "training", 64, 263, 0.5, 0.0, 13, False),
+    ("wide_ll_k128_n256", 600, 4, 2, "ll", 280, 1, 0, "training", 128, 256, 1.5, 0.0, 14, False),
+    ("wide_static_inference_k192_n512", 2000, 8, 4, "static", 0, 4, 1, "inference", 192, 512, 1.8, 0.0, 15, True),
 ]
 
 
