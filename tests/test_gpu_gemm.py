@@ -194,3 +194,42 @@ def test_grouped_gemm_training_shapes_sampled(use_slots):
     got = host_bits(y[torch.from_numpy(rows).cuda()])
     check_gemm(got, ref, xb, wb, np.array(sub_groups, np.int32))
     assert h.status() == 0
+
+
+def test_grouped_gemm_prefill_shapes_sampled():
+    # prefill shapes: HT, 4096 tokens x top-8 over 256 experts (Zipf-skewed,
+    # ragged groups), K = 7168, N = 2048 (the 256 x 256-tile kernel over 112
+    # slabs of K); sampled rows of sampled groups, the largest one included
+    inp = workloads.make_inputs("prefill")
+    c = inp.cfg
+    K, N = c.H, 2048
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht")
+    h = ep.Handle(g, c.T)
+    h.plan(dev_i32(inp.topk_idx))
+    L = oracle.layout(inp.topk_idx, c.E, "ht")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(779)
+    x = torch.randn((L.rows, K), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((c.E, N, K), generator=gen, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    y = ep.Buffer(g).expert_gemm(x, w, h)
+    torch.cuda.synchronize()
+    groups = oracle.expert_groups(L, "ht", c.E)
+    rng = np.random.default_rng(14)
+    pick = groups[rng.choice(len(groups), size=5, replace=False)]
+    pick = np.concatenate([pick, groups[np.argmax(groups[:, 1])][None]])
+    sub, sub_groups, wsel = [], [], []
+    at = 0
+    for r0, n, wi in pick:
+        rows = np.sort(rng.choice(n, size=min(n, 24), replace=False)) + r0
+        sub.append(rows)
+        wsel.append(host_bits(w[wi]))
+        sub_groups.append((at, len(rows), len(wsel) - 1))
+        at += len(rows)
+    rows = np.concatenate(sub)
+    ri = torch.from_numpy(rows).cuda()
+    xb = host_bits(x[ri])
+    wb = np.stack(wsel)
+    gr = np.array(sub_groups, np.int32)
+    ref = oracle.grouped_gemm(xb, wb, gr)
+    check_gemm(host_bits(y[ri]), ref, xb, wb, gr)
+    assert h.status() == 0

@@ -309,3 +309,51 @@ def test_grouped_gemm_fp8_training_shapes_sampled(use_slots):
     ref = oracle.grouped_gemm_fp8(xs, sxs, ws_, sws, gr)
     check_gemm_fp8(host_bits(y[ri]), ref, xs, sxs, ws_, sws, gr, norm=True, separable=True)
     assert h.status() == 0
+
+
+def test_grouped_gemm_fp8_prefill_shapes_sampled():
+    # prefill shapes in FP8: HT, 4096 tokens x top-8 over 256 experts, K = 7168,
+    # N = 2048, quantised Gaussian rows and weights; sampled rows of sampled
+    # groups, the largest one included
+    inp = workloads.make_inputs("prefill")
+    c = inp.cfg
+    K, N = c.H, 2048
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht")
+    h = ep.Handle(g, c.T)
+    h.plan(dev_i32(inp.topk_idx))
+    L = oracle.layout(inp.topk_idx, c.E, "ht")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(780)
+
+    def quantised(shape):
+        v = torch.randn(shape, generator=gen, device="cuda").view(*shape[:-1], shape[-1] // 128, 128)
+        amax = v.abs().amax(-1)
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (v / sc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return q.view(torch.uint8).view(shape), sc.contiguous()
+
+    x, sx = quantised((L.rows, K))
+    w, sw = quantised((c.E, N, K))
+    y = ep.Buffer(g).expert_gemm_fp8(x.view(torch.float8_e4m3fn), sx, w.view(torch.float8_e4m3fn), sw, h)
+    torch.cuda.synchronize()
+    groups = oracle.expert_groups(L, "ht", c.E)
+    rng = np.random.default_rng(15)
+    pick = groups[rng.choice(len(groups), size=5, replace=False)]
+    pick = np.concatenate([pick, groups[np.argmax(groups[:, 1])][None]])
+    sub, sub_groups, wsel, ssel = [], [], [], []
+    at = 0
+    for r0, n, wi in pick:
+        rows = np.sort(rng.choice(n, size=min(n, 24), replace=False)) + r0
+        sub.append(rows)
+        wsel.append(host_u8(w[wi]))
+        ssel.append(host(sw[wi]))
+        sub_groups.append((at, len(rows), len(wsel) - 1))
+        at += len(rows)
+    rows = np.concatenate(sub)
+    ri = torch.from_numpy(rows).cuda()
+    xs, sxs = host_u8(x[ri]), host(sx[ri])
+    ws_, sws = np.stack(wsel), np.stack(ssel)
+    gr = np.array(sub_groups, np.int32)
+    ref = oracle.grouped_gemm_fp8(xs, sxs, ws_, sws, gr)
+    check_gemm_fp8(host_bits(y[ri]), ref, xs, sxs, ws_, sws, gr, norm=True, separable=True)
+    assert h.status() == 0
