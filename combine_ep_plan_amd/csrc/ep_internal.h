@@ -15,7 +15,7 @@ constexpr int kTileEntries = kTileThreads * kTileChunks;  // 2048
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kLdsLimit = 65536;
-constexpr int kGemmBM = 128;  // rows of one grouped-GEMM tile
+constexpr int kGemmBM = 128;  // rows of the smaller grouped-GEMM tile (sizes the tile table)
 
 constexpr uint32_t kFlagIndexRange = 1u;
 constexpr uint32_t kFlagCapacity = 2u;

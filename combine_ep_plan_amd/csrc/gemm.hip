@@ -780,6 +780,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
     }
 }
 
+// Row tiles of kTileM rows the plan can produce; the 256-row tiling needs no more.
 int32_t gemm_max_tiles(const Geometry &g) {
   const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
   return (int32_t)((g.n + kTileM - 1) / kTileM + groups);
