@@ -24,7 +24,7 @@ from tests.helpers import bf16_bits_to_f32, rel_err
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 200
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -109,7 +109,7 @@ def test_random_configuration(seed):
 # grouped GEMMs (bf16 and FP8) on random shapes and layouts
 # ---------------------------------------------------------------------------
 
-N_GEMM = 16
+N_GEMM = 48
 
 
 def draw_gemm(seed: int) -> dict:
