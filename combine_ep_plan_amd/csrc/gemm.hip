@@ -373,7 +373,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
   const __amdgpu_buffer_rsrc_t rW =
       __builtin_amdgcn_make_buffer_rsrc((void *)Wt, (short)0, wrows * K * 2, kBufDword3);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wv >> 1, wn = wv & 1;
   const int c_ld = tid & (kChunks - 1);
   // byte offsets of this thread's chunks: chunk q = tid + i * 256 of a slab
@@ -403,27 +404,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
 #define SWRITE_B(buf)                                                                          \
   _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i)                                         \
       sb[(buf) * kSlabB2 + swz((tid + i * kGemmThreads) / kChunks, c_ld)] = rb[i];
-#define READK(FA, FB, buf, kk)                                                                 \
+// NB: the wave's 32-row blocks that hold rows of the tile (the others are
+// neither read nor multiplied); all four column blocks are always live
+#define READK(FA, FB, buf, kk, NB)                                                             \
   {                                                                                            \
     const int c_ = (kk) * 2 + (lane >> 5);                                                     \
-    _Pragma("unroll") for (int i = 0; i < kFM2; ++i) FA[i] = __builtin_bit_cast(               \
+    _Pragma("unroll") for (int i = 0; i < (NB); ++i) FA[i] = __builtin_bit_cast(               \
         bf16x8, sa[(buf) * kSlabA2 + swz(wm * kWTM2 + i * 32 + (lane & 31), c_)]);            \
     _Pragma("unroll") for (int j = 0; j < kFN2; ++j) FB[j] = __builtin_bit_cast(               \
         bf16x8, sb[(buf) * kSlabB2 + swz(wn * kWTN2 + j * 32 + (lane & 31), c_)]);            \
   }
-#define MFMAK(FA, FB)                                                                          \
-  _Pragma("unroll") for (int i = 0; i < kFM2; ++i)                                             \
+#define MFMAK(FA, FB, NB)                                                                      \
+  _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                             \
   _Pragma("unroll") for (int j = 0; j < kFN2; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
 #define SGB(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
-// the next step's 8 LDS reads over the first 8 of a step's 16 MFMAs ...
-#define SCHED_READS()                                                                          \
-  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }              \
-  SGB(0x008, 8);
-// ... and, in the first two steps, 8 LDS writes and 8 global loads over the other 8
-#define SCHED_READS_WRITES_LOADS()                                                             \
-  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }              \
-  _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); }
+// Full blocks (NB = 4): the next step's 8 LDS reads over the first 8 of a
+// step's 16 MFMAs ...
+#define SCHED_READS(NB)                                                                        \
+  if constexpr ((NB) == kFM2) {                                                                \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }            \
+    SGB(0x008, 8);                                                                             \
+  }
+// ... and, in the first two steps, 8 LDS writes and 8 global loads over the
+// other 8; waves with fewer live blocks are left to the compiler's schedule
+#define SCHED_READS_WRITES_LOADS(NB)                                                           \
+  if constexpr ((NB) == kFM2) {                                                                \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }            \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); } \
+  }
 
   f32x16 acc[kFM2][kFN2];
 #pragma unroll
@@ -444,44 +453,57 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
     GLOAD_B(1);
   }
   __syncthreads();
-  READK(fa0, fb0, 0, 0);
-  int kt = 0;
-  for (; kt + 2 < KT; ++kt) {  // steady state: slab kt in LDS, slab kt + 1 in registers
-    const int buf = kt & 1;
-    READK(fa1, fb1, buf, 1);
-    SWRITE_A(buf ^ 1);
-    GLOAD_A(kt + 2);
-    MFMAK(fa0, fb0);
-    SCHED_READS_WRITES_LOADS();
-    READK(fa0, fb0, buf, 2);
-    SWRITE_B(buf ^ 1);
-    GLOAD_B(kt + 2);
-    MFMAK(fa1, fb1);
-    SCHED_READS_WRITES_LOADS();
-    READK(fa1, fb1, buf, 3);
-    MFMAK(fa0, fb0);
-    SCHED_READS();
-    __syncthreads();  // slab kt + 1 is in LDS; every wave is done reading slab kt
-    READK(fa0, fb0, buf ^ 1, 0);
-    MFMAK(fa1, fb1);
-    SCHED_READS();
+  // The loop is compiled once per count of live 32-row blocks and each wave
+  // runs its own (every copy has the same barriers); a tile of 18 rows costs
+  // one block of MFMAs in one wave instead of sixteen.
+#define WIDE_LOOP(NB)                                                                          \
+  {                                                                                            \
+    READK(fa0, fb0, 0, 0, NB);                                                                 \
+    int kt = 0;                                                                                \
+    for (; kt + 2 < KT; ++kt) { /* slab kt in LDS, slab kt + 1 in registers */                 \
+      const int buf = kt & 1;                                                                  \
+      READK(fa1, fb1, buf, 1, NB);                                                             \
+      SWRITE_A(buf ^ 1);                                                                       \
+      GLOAD_A(kt + 2);                                                                         \
+      MFMAK(fa0, fb0, NB);                                                                     \
+      SCHED_READS_WRITES_LOADS(NB);                                                            \
+      READK(fa0, fb0, buf, 2, NB);                                                             \
+      SWRITE_B(buf ^ 1);                                                                       \
+      GLOAD_B(kt + 2);                                                                         \
+      MFMAK(fa1, fb1, NB);                                                                     \
+      SCHED_READS_WRITES_LOADS(NB);                                                            \
+      READK(fa1, fb1, buf, 3, NB);                                                             \
+      MFMAK(fa0, fb0, NB);                                                                     \
+      SCHED_READS(NB);                                                                         \
+      __syncthreads(); /* slab kt + 1 is in LDS; every wave is done reading slab kt */         \
+      READK(fa0, fb0, buf ^ 1, 0, NB);                                                         \
+      MFMAK(fa1, fb1, NB);                                                                     \
+      SCHED_READS(NB);                                                                         \
+    }                                                                                          \
+    for (; kt < KT; ++kt) { /* the last two slabs (no more global loads) */                    \
+      const int buf = kt & 1;                                                                  \
+      READK(fa1, fb1, buf, 1, NB);                                                             \
+      MFMAK(fa0, fb0, NB);                                                                     \
+      READK(fa0, fb0, buf, 2, NB);                                                             \
+      MFMAK(fa1, fb1, NB);                                                                     \
+      READK(fa1, fb1, buf, 3, NB);                                                             \
+      MFMAK(fa0, fb0, NB);                                                                     \
+      if (kt + 1 < KT) {                                                                       \
+        SWRITE_A(buf ^ 1);                                                                     \
+        SWRITE_B(buf ^ 1);                                                                     \
+        __syncthreads();                                                                       \
+        READK(fa0, fb0, buf ^ 1, 0, NB);                                                       \
+      }                                                                                        \
+      MFMAK(fa1, fb1, NB);                                                                     \
+    }                                                                                          \
   }
-  for (; kt < KT; ++kt) {  // the last two slabs (no more global loads)
-    const int buf = kt & 1;
-    READK(fa1, fb1, buf, 1);
-    MFMAK(fa0, fb0);
-    READK(fa0, fb0, buf, 2);
-    MFMAK(fa1, fb1);
-    READK(fa1, fb1, buf, 3);
-    MFMAK(fa0, fb0);
-    if (kt + 1 < KT) {
-      SWRITE_A(buf ^ 1);
-      SWRITE_B(buf ^ 1);
-      __syncthreads();
-      READK(fa0, fb0, buf ^ 1, 0);
-    }
-    MFMAK(fa1, fb1);
-  }
+  const int live = (rows - wm * kWTM2 + 31) / 32;  // wave-uniform
+  if (live >= kFM2) WIDE_LOOP(kFM2)
+  else if (live == 3) WIDE_LOOP(3)
+  else if (live == 2) WIDE_LOOP(2)
+  else if (live == 1) WIDE_LOOP(1)
+  else WIDE_LOOP(0)
+#undef WIDE_LOOP
 #undef SCHED_READS_WRITES_LOADS
 #undef SCHED_READS
 #undef SGB

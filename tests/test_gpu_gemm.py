@@ -87,6 +87,10 @@ CASES = [
     ("wide_n_odd_k64", 1200, 4, 2, "ht", 0, 1, 0, "training", 64, 263, 0.5, 0.0, 13, False),
     ("wide_ll_k128_n256", 600, 4, 2, "ll", 280, 1, 0, "training", 128, 256, 1.5, 0.0, 14, False),
     ("wide_static_inference_k192_n512", 2000, 8, 4, "static", 0, 4, 1, "inference", 192, 512, 1.8, 0.0, 15, True),
+    # skewed groups: tiles of every size, so each wave's count of live 32-row
+    # blocks (0 to 4) occurs
+    ("wide_skewed_k192_n256", 1024, 16, 2, "ht", 0, 1, 0, "training", 192, 256, 2.0, 0.0, 16, False),
+    ("wide_skewed_static_k320_n264", 1200, 8, 4, "static", 0, 4, 2, "training", 320, 264, 2.0, 0.0, 17, True),
 ]
 
 
