@@ -174,7 +174,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
   const int64_t KV = K / 8;  // 16-byte vectors per row
   const u32x4 *Wm = widx < E ? W + (int64_t)widx * N * KV : Wslot + (int64_t)(widx - E) * N * KV;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wv / kWavesN, wn = wv % kWavesN;
 
   // loader: chunk q = tid + i * 256 of a slab is row q / 8, chunk q % 8.
@@ -219,16 +220,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
   // kt+1 is read right after the barrier that publishes it, under the last
   // MFMAs of slab kt.  The global loads of slab kt+2 are in flight during
   // all of slab kt+1.
-#define READK(FA, FB, buf, kk)                                                                      \
+#define READK(FA, FB, buf, kk, LB)                                                                  \
   {                                                                                                 \
     const int c_ = (kk) * 2 + (lane >> 5);                                                          \
-    _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                                 \
+    _Pragma("unroll") for (int i = 0; i < (LB); ++i)                                                \
         FA[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(wm * kWTM + i * 32 + (lane & 31), c_)]);     \
     _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                                 \
         FB[j] = __builtin_bit_cast(bf16x8, sb[buf][swz(wn * kWTN + j * 32 + (lane & 31), c_)]);     \
   }
-#define MFMAK(FA, FB)                                                                               \
-  _Pragma("unroll") for (int i = 0; i < kFM; ++i)                                                   \
+#define MFMAK(FA, FB, LB)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < (LB); ++i)                                                  \
   _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
 
@@ -239,42 +240,55 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
   SWRITE(ra0, rb0, 0);
   if (KT > 1) { GLOAD(ra0, rb0, 1); }
   __syncthreads();
-  READK(fa0, fb0, 0, 0);
   // sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS write,
   // 0x020 global load; each call asks for the next n instructions of that kind
 #define SGB(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
-  int kt = 0;
-  for (; kt + 2 < KT; ++kt) {   // steady state
-    const int buf = kt & 1;
-    READK(fa1, fb1, buf, 1);
-    MFMAK(fa0, fb0);
-    READK(fa0, fb0, buf, 2);
-    MFMAK(fa1, fb1);
-    READK(fa1, fb1, buf, 3);
-    MFMAK(fa0, fb0);
-    SWRITE(ra0, rb0, buf ^ 1);
-    GLOAD(ra0, rb0, kt + 2);
-    MFMAK(fa1, fb1);
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); }
-    __syncthreads();
-    READK(fa0, fb0, buf ^ 1, 0);
+  // LB: the wave's 32-row blocks that hold rows of the tile (2, 1 or 0); the
+  // loop is compiled for each with the same barriers, and empty blocks are
+  // neither read nor multiplied.  The interleaving pattern is for full waves.
+#define MAIN_LOOP(LB)                                                                               \
+  {                                                                                                 \
+    READK(fa0, fb0, 0, 0, LB);                                                                      \
+    int kt = 0;                                                                                     \
+    for (; kt + 2 < KT; ++kt) { /* steady state */                                                  \
+      const int buf = kt & 1;                                                                       \
+      READK(fa1, fb1, buf, 1, LB);                                                                  \
+      MFMAK(fa0, fb0, LB);                                                                          \
+      READK(fa0, fb0, buf, 2, LB);                                                                  \
+      MFMAK(fa1, fb1, LB);                                                                          \
+      READK(fa1, fb1, buf, 3, LB);                                                                  \
+      MFMAK(fa0, fb0, LB);                                                                          \
+      SWRITE(ra0, rb0, buf ^ 1);                                                                    \
+      GLOAD(ra0, rb0, kt + 2);                                                                      \
+      MFMAK(fa1, fb1, LB);                                                                          \
+      if constexpr ((LB) == kFM) {                                                                  \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x100, 1); }             \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) { SGB(0x008, 1); SGB(0x200, 1); SGB(0x020, 1); } \
+      }                                                                                             \
+      __syncthreads();                                                                              \
+      READK(fa0, fb0, buf ^ 1, 0, LB);                                                              \
+    }                                                                                               \
+    for (; kt < KT; ++kt) { /* the last two slabs (no more global loads) */                         \
+      const int buf = kt & 1;                                                                       \
+      READK(fa1, fb1, buf, 1, LB);                                                                  \
+      MFMAK(fa0, fb0, LB);                                                                          \
+      READK(fa0, fb0, buf, 2, LB);                                                                  \
+      MFMAK(fa1, fb1, LB);                                                                          \
+      READK(fa1, fb1, buf, 3, LB);                                                                  \
+      MFMAK(fa0, fb0, LB);                                                                          \
+      if (kt + 1 < KT) {                                                                            \
+        SWRITE(ra0, rb0, buf ^ 1);                                                                  \
+        __syncthreads();                                                                            \
+        READK(fa0, fb0, buf ^ 1, 0, LB);                                                            \
+      }                                                                                             \
+      MFMAK(fa1, fb1, LB);                                                                          \
+    }                                                                                               \
   }
-  for (; kt < KT; ++kt) {   // the last two slabs (no more global loads)
-    const int buf = kt & 1;
-    READK(fa1, fb1, buf, 1);
-    MFMAK(fa0, fb0);
-    READK(fa0, fb0, buf, 2);
-    MFMAK(fa1, fb1);
-    READK(fa1, fb1, buf, 3);
-    MFMAK(fa0, fb0);
-    if (kt + 1 < KT) {
-      SWRITE(ra0, rb0, buf ^ 1);
-      __syncthreads();
-      READK(fa0, fb0, buf ^ 1, 0);
-    }
-    MFMAK(fa1, fb1);
-  }
+  const int live = (rows - wm * kWTM + 31) / 32;  // wave-uniform
+  if (live >= kFM) MAIN_LOOP(kFM)
+  else if (live == 1) MAIN_LOOP(1)
+  else MAIN_LOOP(0)
+#undef MAIN_LOOP
 #undef SGB
 #undef READK
 #undef MFMAK
@@ -612,7 +626,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   const u32x4 *Wm = (own ? W : Wslot) + wsel * N * KV;
   const float *SWm = (own ? SW : SWslot) + wsel * N * NB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wv / kWavesN, wn = wv % kWavesN;
 
   constexpr int kLoads = kTileM * kChunks / kGemmThreads;
@@ -662,10 +677,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   // Step h (0, 1) of a slab: a lane of the upper half-wave takes chunks
   // 4h + 2, 4h + 3 of its row, the lower half chunks 4h, 4h + 1 (the same
   // K positions for A and B, which is all the product needs).
-#define READK(FA, FB, buf, h)                                                                  \
+#define READK(FA, FB, buf, h, LB)                                                              \
   {                                                                                            \
     const int c_ = (h) * 4 + (lane >> 5) * 2;                                                  \
-    _Pragma("unroll") for (int i = 0; i < kFM; ++i) {                                          \
+    _Pragma("unroll") for (int i = 0; i < (LB); ++i) {                                         \
       const int r_ = wm * kWTM + i * 32 + (lane & 31);                                         \
       const u32x4 lo = sa[buf][swz(r_, c_)], hi = sa[buf][swz(r_, c_ + 1)];                    \
       FA[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,                                \
@@ -713,35 +728,52 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   SWRITE(0);
   if (KT > 1) { GLOAD(1); }
   __syncthreads();
-  READK(fa0, fb0, 0, 0);
-  READK(fa1, fb1, 0, 1);
-  for (int kt = 0; kt < KT; ++kt) {
-    const float *sc = ssc[kt % kScaleBufs];
-#pragma unroll
-    for (int j = 0; j < kFN; ++j) scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];
-    ROWSCALES(0);
-    BLOCK(p0, 0, 0);
-    BLOCK(p1, 0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    FOLD(p0, 0, 0);
-    BLOCK(p0, 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    FOLD(p1, 0, 1);
-    BLOCK(p1, 1, 1);
-    ROWSCALES(1);
-    __builtin_amdgcn_sched_barrier(0);
-    FOLD(p0, 1, 0);
-    if (kt + 1 < KT) {
-      SWRITE(kt + 1);
-      if (kt + 2 < KT) { GLOAD(kt + 2); }
-      __syncthreads();
-    }
-    FOLD(p1, 1, 1);
-    if (kt + 1 < KT) {
-      READK(fa0, fb0, (kt + 1) & 1, 0);
-      READK(fa1, fb1, (kt + 1) & 1, 1);
-    }
+  // LB: the wave's 32-row blocks that hold rows of the tile; the loop is
+  // compiled for 2, 1 and 0 of them (same barriers in every copy) and the
+  // empty blocks are neither read, multiplied nor folded.
+#define F8_LOOP(LB)                                                                            \
+  {                                                                                            \
+    READK(fa0, fb0, 0, 0, LB);                                                                 \
+    READK(fa1, fb1, 0, 1, LB);                                                                 \
+    for (int kt = 0; kt < KT; ++kt) {                                                          \
+      const float *sc = ssc[kt % kScaleBufs];                                                  \
+      if constexpr ((LB) > 0) {                                                                \
+        _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                        \
+            scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];                           \
+        ROWSCALES(0);                                                                          \
+        BLOCK(p0, 0, 0);                                                                       \
+        BLOCK(p1, 0, 1);                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        FOLD(p0, 0, 0);                                                                        \
+      }                                                                                        \
+      if constexpr ((LB) == 2) {                                                               \
+        BLOCK(p0, 1, 0);                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        FOLD(p1, 0, 1);                                                                        \
+        BLOCK(p1, 1, 1);                                                                       \
+        ROWSCALES(1);                                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        FOLD(p0, 1, 0);                                                                        \
+      } else if constexpr ((LB) == 1) {                                                        \
+        FOLD(p1, 0, 1);                                                                        \
+      }                                                                                        \
+      if (kt + 1 < KT) {                                                                       \
+        SWRITE(kt + 1);                                                                        \
+        if (kt + 2 < KT) { GLOAD(kt + 2); }                                                    \
+        __syncthreads();                                                                       \
+      }                                                                                        \
+      if constexpr ((LB) == 2) { FOLD(p1, 1, 1); }                                             \
+      if (kt + 1 < KT) {                                                                       \
+        READK(fa0, fb0, (kt + 1) & 1, 0, LB);                                                  \
+        READK(fa1, fb1, (kt + 1) & 1, 1, LB);                                                  \
+      }                                                                                        \
+    }                                                                                          \
   }
+  const int live = (rows - wm * kWTM + 31) / 32;  // wave-uniform
+  if (live >= kFM) F8_LOOP(kFM)
+  else if (live == 1) F8_LOOP(1)
+  else F8_LOOP(0)
+#undef F8_LOOP
 #undef BLOCK
 #undef FOLD
 #undef ROWSCALES
