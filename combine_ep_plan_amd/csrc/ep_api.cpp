@@ -61,7 +61,7 @@ int64_t numel(const ep_tensor_t *t) {
   return n;
 }
 
-// Generic checks: non-NULL, tag, dtype, ndim in 1..4, sizes >= 0, data set.
+// Generic checks: non-NULL, tag, dtype, ndim in 1..4, sizes >= 0, data set and aligned.
 ep_status_t check_tensor(const ep_tensor_t *t, int32_t tag, int32_t dtype) {
   if (!t) return EP_ERR_INVALID_ARG;
   if (t->tag != tag) return EP_ERR_BAD_TAG;
@@ -70,6 +70,11 @@ ep_status_t check_tensor(const ep_tensor_t *t, int32_t tag, int32_t dtype) {
   for (int i = 0; i < t->ndim; ++i)
     if (t->sizes[i] < 0) return EP_ERR_BAD_SHAPE;
   if (!t->data && numel(t) > 0) return EP_ERR_INVALID_ARG;
+  // rows of tokens, expert weights and gradients move as 16-byte vectors;
+  // ids, router weights, logits and scales as 4-byte words
+  const uintptr_t need =
+      (tag == EP_TAG_TOKENS || tag == EP_TAG_EXPERT_WEIGHTS || tag == EP_TAG_EXPERT_GRADS) ? 16 : 4;
+  if (reinterpret_cast<uintptr_t>(t->data) % need != 0) return EP_ERR_INVALID_ARG;
   return EP_OK;
 }
 

@@ -111,7 +111,10 @@ typedef enum ep_slot_mode {
                              directly (seg_slot -1) and set no flag */
 } ep_slot_mode_t;
 
-/* Non-owning view of a contiguous row-major device tensor. */
+/* Non-owning view of a contiguous row-major device tensor.  data must be
+ * 16-byte aligned for the tags TOKENS, EXPERT_WEIGHTS and EXPERT_GRADS (rows
+ * move as 16-byte vectors) and 4-byte aligned for the others; a misaligned
+ * view is rejected with EP_ERR_INVALID_ARG. */
 typedef struct ep_tensor {
   void *data;           /* device pointer (may be NULL only if the tensor is empty) */
   int32_t dtype;        /* ep_dtype_t */

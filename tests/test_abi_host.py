@@ -375,3 +375,18 @@ def test_expert_gemm_fp8_argument_validation(lib):
     assert G(h, x, sx, w, sw, T(FP8, W, 8, 32, 256), T(F32, SC, 8, 32, 2), y, None) == 5
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
+
+
+def test_misaligned_tensor_data_is_rejected(lib):
+    g, h, _ = make_handle(lib)                       # HT, T=64, k=2, H=256
+    D = lib.ep_dispatch
+    recv = T(BF16, ep.TAG_TOKENS, 128, 256)
+    # token rows need 16-byte alignment
+    assert D(h, T(BF16, ep.TAG_TOKENS, 64, 256, data=FAKE + 8), None, recv, None, None, None, None) == 1
+    assert D(h, T(BF16, ep.TAG_TOKENS, 64, 256, data=FAKE + 16), None, recv, None, None, None, None) == 5
+    # router weights only 4-byte alignment
+    x = T(BF16, ep.TAG_TOKENS, 64, 256)
+    assert D(h, x, T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2, data=FAKE + 2), recv, None, None, None, None) == 1
+    assert D(h, x, T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2, data=FAKE + 4), recv, None, None, None, None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
