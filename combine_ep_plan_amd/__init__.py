@@ -139,6 +139,8 @@ def _tensor(t: torch.Tensor | None, tag: int):
     call that repeats its tensors costs a dictionary lookup."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     key = (t.data_ptr(), t.dtype, t.shape, tag)

@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import combine_ep_plan_amd as ep
 
@@ -390,3 +391,10 @@ def test_misaligned_tensor_data_is_rejected(lib):
     assert D(h, x, T(F32, ep.TAG_TOPK_WEIGHTS, 64, 2, data=FAKE + 4), recv, None, None, None, None) == 5
     lib.ep_handle_destroy(h)
     lib.ep_group_destroy(g)
+
+
+def test_binding_refuses_host_tensors():
+    # the binding hands raw pointers to the kernels: a host tensor must never
+    # reach them
+    with pytest.raises(ValueError, match="on the GPU"):
+        ep._tensor(torch.zeros(4, 8), ep.TAG_TOKENS)
