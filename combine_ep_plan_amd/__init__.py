@@ -447,9 +447,10 @@ class Buffer:
     def dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
                  handle: Handle | None = None, fp8: bool = False, recv_meta: bool = True,
                  out: torch.Tensor | None = None, stream=None):
-        """Plan (if ``handle`` is None or not yet planned with these indices) and
-        dispatch.  Returns ``recv_x, recv_i, recv_w, handle, event`` (plus the
-        FP8 scales as ``recv_x = (codes, scales)`` when ``fp8``)."""
+        """Dispatch; with ``handle`` None, first plan ``topk_idx`` on a new
+        handle for these tokens (a handle passed in must already be planned).
+        Returns ``recv_x, recv_i, recv_w, handle, event`` (plus the FP8 scales
+        as ``recv_x = (codes, scales)`` when ``fp8``)."""
         T = x.shape[0]
         if handle is None:
             handle = Handle(self.group, T, x.device)
