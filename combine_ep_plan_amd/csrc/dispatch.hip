@@ -6,8 +6,11 @@
 //
 // One workgroup per token (per piece of a token's row when there are too
 // few tokens to fill the GPU): the row is read once with 16-byte loads and
-// written to each of its k destinations with 16-byte streaming stores, so
-// x costs one HBM read and every receive row one HBM write.
+// written to each of its k destinations with 16-byte stores, so x costs one
+// HBM read and every receive row one HBM write.  The stores are cached while
+// the rows written fit in twice the 256 MB Infinity Cache (the next kernel
+// then finds much of them there) and non-temporal beyond that, where cached
+// stores only leave write-backs for the next kernel to pay.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -15,6 +18,7 @@ namespace epk {
 
 constexpr int kRowThreads = 512;
 constexpr int kUnroll = 2;
+constexpr int64_t kCachedStoreBytes = (int64_t)512 << 20;  // twice the Infinity Cache
 
 // Pieces per row: small batches (decode) split each row over several
 // workgroups, so the grid reaches about kSplitTarget workgroups; pieces are
@@ -32,7 +36,7 @@ int32_t row_pieces(int32_t T, int32_t V, int32_t *chunk) {
   return (V + c - 1) / c;
 }
 
-template <int K>
+template <int K, bool NT>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__restrict__ x,
                                                                const int32_t *__restrict__ dst,
                                                                u32x4 *__restrict__ recv,
@@ -60,7 +64,10 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__re
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int32_t v = v0 + u * kRowThreads;
-        if (v < hi) store_stream(o + v, val[u]);
+        if (v < hi) {
+          if constexpr (NT) store_stream(o + v, val[u]);
+          else o[v] = val[u];
+        }
       }
     }
   }
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__re
 // those 16 lanes.  scale = amax / 448 and x / scale are IEEE fp32 divisions,
 // the quotient is clamped to +-448 and rounded to nearest even by
 // v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950).
-template <int K>
+template <int K, bool NT>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__restrict__ x,
                                                               const int32_t *__restrict__ dst,
                                                               u32x2 *__restrict__ recv_q,
@@ -107,7 +114,8 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
       if (K == 0 && j >= k) break;
       const int32_t d = dt[j];
       if (d < 0 || d >= rows) continue;
-      store_stream(recv_q + (int64_t)d * V + v, packed);
+      if constexpr (NT) store_stream(recv_q + (int64_t)d * V + v, packed);
+      else recv_q[(int64_t)d * V + v] = packed;
       if ((v & 15) == 0) recv_s[(int64_t)d * nb + (v >> 4)] = s;
     }
   }
@@ -142,12 +150,19 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-#define L(KK)                                                                          \
-  hipLaunchKernelGGL(k_dispatch_bf16<KK>, dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
+  const bool nt = g.n * H * 2 > kCachedStoreBytes;
+#define L2(KK, NT)                                                                     \
+  hipLaunchKernelGGL((k_dispatch_bf16<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
                      reinterpret_cast<u32x4 *>(recv), g.rows, V, g.k, chunk)
+#define L(KK)               \
+  do {                      \
+    if (nt) L2(KK, true);   \
+    else L2(KK, false);     \
+  } while (0)
   EP_K_SWITCH(g.k, L)
 #undef L
+#undef L2
   return hipGetLastError();
 }
 
@@ -157,13 +172,20 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-#define L(KK)                                                                          \
-  hipLaunchKernelGGL(k_dispatch_fp8<KK>, dim3(g.T, pieces), dim3(kRowThreads), 0, s,  \
+  const bool nt = g.n * (H + H / 128 * 4) > kCachedStoreBytes;
+#define L2(KK, NT)                                                                     \
+  hipLaunchKernelGGL((k_dispatch_fp8<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
                      reinterpret_cast<u32x2 *>(recv_q), recv_scale, g.rows, V,        \
                      g.k, chunk)
+#define L(KK)               \
+  do {                      \
+    if (nt) L2(KK, true);   \
+    else L2(KK, false);     \
+  } while (0)
   EP_K_SWITCH(g.k, L)
 #undef L
+#undef L2
   return hipGetLastError();
 }
 
