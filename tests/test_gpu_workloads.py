@@ -214,3 +214,36 @@ def test_workload_other_seeds(name, s):
     _check_dispatch_full(inp, recv, L, x)
     y = buf.combine(recv, h, w, out_dtype=torch.float32 if c.out_fp32 else torch.bfloat16)
     _check_combine_sampled(inp, L, recv, y, inp.topk_w, n=256, out_fp32=c.out_fp32)
+
+
+@pytest.mark.parametrize("name", ["prefill", "training"])
+def test_fp8_dispatch_at_full_sizes(name):
+    # prefill writes 242 MB of codes and scales (cached stores), training 553 MB
+    # (non-temporal stores): sampled tokens bit-exact against the oracle, and in
+    # full on the device every copy of a token equal to its first copy
+    inp = workloads.make_inputs(name)
+    c = inp.cfg
+    print(f"[workload fp8] {name} T={c.T} H={c.H} E={c.E} k={c.k} layout={c.layout}", flush=True)
+    g = make_group(c.E, c.R, c.H, c.k, c.T, c.layout, c.cap, c.S)
+    h = ep.Handle(g, c.T)
+    buf = ep.Buffer(g)
+    h.plan(dev_i32(inp.topk_idx))
+    (q, s), _, _, _, _ = buf.dispatch(dev_bf16(inp.x), None, None, handle=h, fp8=True, recv_meta=False)
+    torch.cuda.synchronize()
+    L = oracle.layout(inp.topk_idx, c.E, c.layout, cap=c.cap, R=c.R, S=c.S)
+    qr = q.view(torch.uint8).view(L.rows, c.H)
+    sr = s.view(L.rows, c.H // 128)
+    d = torch.from_numpy(L.dst.astype(np.int64)).cuda()            # [T, k]
+    ok = d >= 0
+    first = d[:, :1].expand_as(d)
+    assert bool(ok[:, 0].all())                                       # no entry masked here
+    assert torch.equal(qr[d[ok]], qr[first[ok]])
+    assert torch.equal(sr[d[ok]], sr[first[ok]])
+    rng = np.random.default_rng(c.T + 7)
+    for t in np.sort(rng.choice(c.T, size=64, replace=False)):
+        wq, ws = oracle.dispatch_fp8(inp.x[t:t + 1], np.zeros((1, 1), np.int32), 1)
+        for j in range(c.k):
+            r = int(L.dst[t, j])
+            assert np.array_equal(qr[r].cpu().numpy(), wq[0]), (t, j)
+            assert np.array_equal(sr[r].cpu().numpy(), ws[0]), (t, j)
+    assert h.status() == 0
