@@ -29,7 +29,7 @@ struct ep_handle {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kFp8GemmMaxK = (int64_t)1 << 28;  // bytes per row of an FP8 GEMM operand
+constexpr int64_t kFp8GemmMaxK = (int64_t)1 << 24;  // bytes per row of an FP8 GEMM operand
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -566,7 +566,7 @@ ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
   if (w->ndim != 3 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
   const int64_t N = w->sizes[1], K = w->sizes[2];
   if (K <= 0 || K % 128 != 0 || K > INT32_MAX || N < 1 || N > INT32_MAX) return EP_ERR_BAD_SHAPE;
-  // the kernel addresses a tile's rows with 32-bit offsets (16-byte units)
+  // the kernel addresses a tile's 128 rows of K bytes through 32-bit buffer offsets
   if (K > kFp8GemmMaxK) return EP_ERR_UNSUPPORTED;
   const int64_t NB = K / 128;
   if (!(ws->ndim == 3 && ws->sizes[0] == g.E && ws->sizes[1] == N && ws->sizes[2] == NB))

@@ -633,20 +633,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   constexpr int kLoads = kTileM * kChunks / kGemmThreads;
   constexpr int kLoadsB = kBN * kChunks / kGemmThreads;
   const int c_ld = tid & (kChunks - 1);
-  // Uniform tile bases and 32-bit lane offsets (a tile spans at most 128
-  // rows of K bytes), so the loads take a scalar base.
+  // Buffer loads: a scalar resource over the tile's rows and one 32-bit byte
+  // offset per lane (the library takes K <= 2^24, so 128 rows of K bytes stay
+  // within the resource's 32-bit range); rows past the end read the last row.
   const u32x4 *Xt = X + (int64_t)row0 * KV;
   const u32x4 *Wt = Wm + (int64_t)n0 * KV;
+  const int32_t wrows = N - n0 < kBN ? N - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t rX =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Xt, (short)0, rows * K, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rW =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Wt, (short)0, wrows * K, kBufDword3);
   uint32_t oa[kLoads], ob[kLoadsB];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = (tid + i * kGemmThreads) / kChunks;
-    oa[i] = (uint32_t)((r < rows ? r : rows - 1) * KV + c_ld);
+    oa[i] = (uint32_t)(((r < rows ? r : rows - 1) * KV + c_ld) * 16);
   }
 #pragma unroll
   for (int i = 0; i < kLoadsB; ++i) {
     const int r = (tid + i * kGemmThreads) / kChunks;
-    ob[i] = (uint32_t)((n0 + r < N ? r : N - 1 - n0) * KV + c_ld);
+    ob[i] = (uint32_t)(((r < wrows ? r : wrows - 1) * KV + c_ld) * 16);
   }
   // thread t < 128 stages the scale of tile row t, thread 128 + c that of column c
   const float *ps = tid < kTileM
@@ -656,8 +662,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   float rs;
 
 #define GLOAD(kt)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) ra0[i] = (Xt + (kt) * kChunks)[oa[i]]; \
-  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i) rb0[i] = (Wt + (kt) * kChunks)[ob[i]]; \
+  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) ra0[i] = __builtin_bit_cast(             \
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, oa[i], (kt) * 128, 0));                   \
+  _Pragma("unroll") for (int i = 0; i < kLoadsB; ++i) rb0[i] = __builtin_bit_cast(            \
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, ob[i], (kt) * 128, 0));                   \
   rs = ps[kt];
 #define SWRITE(kt)                                                                            \
   _Pragma("unroll") for (int i = 0; i < kLoads; ++i)                                          \

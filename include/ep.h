@@ -377,7 +377,7 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
  *   out[i, n] = bf16( sum_b recv_scales[i, b] * W_scales[n, b] *
  *                     sum_{c in block b} recv_tokens[i, c] * W[n, c] )
  * (exact e4m3 products, fp32 accumulation, one rounding to nearest even).
- * recv_tokens:   e4m3 [recv_rows, K], tag TOKENS; K % 128 == 0, K <= 2^28.
+ * recv_tokens:   e4m3 [recv_rows, K], tag TOKENS; K % 128 == 0, K <= 2^24.
  * recv_scales:   fp32 [recv_rows, K/128], tag FP8_SCALES.
  * expert_weights: e4m3 [E, N, K], tag EXPERT_WEIGHTS.
  * expert_scales: fp32 [E, N, K/128], tag FP8_SCALES.
@@ -388,7 +388,7 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
  *                not written.
  * Errors: EP_ERR_BAD_SHAPE, EP_ERR_INVALID_ARG (only one of the slot
  * tensors given), EP_ERR_UNSUPPORTED (slots for a non-STATIC handle, or
- * K > 2^28),
+ * K > 2^24),
  * EP_ERR_NOT_PLANNED.  Enqueues two kernels (tile table, GEMM). */
 ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
                                const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,

@@ -355,7 +355,7 @@ def test_expert_gemm_fp8_argument_validation(lib):
              T(F32, SC, 8, 32, 1), None, None, y, None) == 4                  # K % 128
     assert G(h, x, T(F32, SC, 128, 1), w, sw, None, None, y, None) == 4       # row scales K/128
     assert G(h, x, sx, w, T(F32, SC, 8, 32, 1), None, None, y, None) == 4     # weight scales K/128
-    KB = (1 << 28) + 128                                                      # beyond 32-bit tile offsets
+    KB = (1 << 24) + 128                                                      # beyond 32-bit tile offsets
     assert G(h, T(FP8, TK, 128, KB), T(F32, SC, 128, KB // 128), T(FP8, W, 8, 32, KB),
              T(F32, SC, 8, 32, KB // 128), None, None, y, None) == 7
     assert G(h, x, sx, w, T(F32, SC, 7, 32, 2), None, None, y, None) == 4
