@@ -43,7 +43,11 @@
 //    stored at c ^ ((r / 2) % 8): the 16 rows one 16-lane phase of an MFMA
 //    operand read touches then cover all 64 banks once (no conflicts).
 //    Rows past a tile's end load a valid row instead of branching (their
-//    products land in outputs that are never stored).
+//    products land in outputs that are never stored), and a wave whose
+//    32-row blocks hold no rows of the tile skips their fragment reads and
+//    MFMAs: the main loop is compiled once per count of live blocks and each
+//    wave runs its own copy (all copies have the same barriers).  The wide
+//    and FP8 kernels do the same.
 //    Workgroup order: workgroup b runs on XCD b % 8; each XCD takes an equal,
 //    contiguous share of the valid (row tile, column tile) pairs, column tile
 //    fastest, so the column tiles of one row tile share its X rows in that
