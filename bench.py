@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--prefetch", action="store_true",
                    help="STATIC workloads: add the replica-weight prefetch of one [4096, 1536] "
                         "bf16 projection per expert after the plan")
+    p.add_argument("--dispatch-stores", choices=("auto", "cached", "streaming"), default="auto",
+                   help="how dispatch writes the receive rows (default: cached while they fit in "
+                        "512 MiB, non-temporal beyond)")
     p.add_argument("--slot-mode", choices=("training", "inference"), default="training",
                    help="STATIC workloads: what the plan does past a rank's S-th replica slot")
     p.add_argument("--slots", type=int, default=None,
@@ -205,7 +208,8 @@ def run_microbatches(a):
     torch.cuda.set_device(dev)
     main_stream = torch.cuda.current_stream()
     c = workloads.get_config(name, a.rho)
-    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S)
+    g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S,
+                 dispatch_stores=a.dispatch_stores)
     streams = [torch.cuda.Stream() for _ in range(M)] if a.overlap else [main_stream] * M
     mbs = []
     for i in range(M):
@@ -339,7 +343,7 @@ def run_microbatches(a):
                                f"{' fp8' if a.fp8 else ''}, {M} micro-batches "
                                f"{'overlapped on ' + str(M) + ' streams' if a.overlap else 'in turn on one stream'}",
                    "T": c.T, "H": c.H, "E": c.E, "top_k": c.k, "layout": c.layout,
-                   "microbatches": M, "overlap": a.overlap,
+                   "microbatches": M, "overlap": a.overlap, "dispatch_stores": a.dispatch_stores,
                    "step": " -> ".join(nm for nm, _ in serial) + f" (x{M})"},
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
@@ -396,7 +400,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=S,
-                 slot_mode=a.slot_mode)
+                 slot_mode=a.slot_mode, dispatch_stores=a.dispatch_stores)
     h = ep.Handle(g, c.T)
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(inp.topk_idx).to(dev)
@@ -625,6 +629,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
+                   "dispatch_stores": a.dispatch_stores,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route or a.fused_route,
                    "hip_graph": a.graph},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),

@@ -30,6 +30,7 @@ __all__ = [
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
+    "STORES_AUTO", "STORES_CACHED", "STORES_STREAMING",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,8 @@ TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0
 TAG_ROUTER_LOGITS, TAG_EXPERT_WEIGHTS = 5, 6
 SLOTS_TRAINING, SLOTS_INFERENCE = 0, 1
 _SLOT_MODES = {"training": SLOTS_TRAINING, "inference": SLOTS_INFERENCE}
+STORES_AUTO, STORES_CACHED, STORES_STREAMING = 0, 1, 2
+_STORES = {"auto": STORES_AUTO, "cached": STORES_CACHED, "streaming": STORES_STREAMING}
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
 _STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
            "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",
@@ -63,7 +66,8 @@ class ep_tensor_t(ctypes.Structure):
 class ep_group_config_t(ctypes.Structure):
     _fields_ = [("num_experts", c_int32), ("num_ranks", c_int32), ("hidden", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
-                ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32)]
+                ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32),
+                ("dispatch_stores", c_int32)]
 
 
 class ep_handle_view_t(ctypes.Structure):
@@ -316,11 +320,13 @@ class Group:
 
     def __init__(self, num_experts: int, num_ranks: int, hidden: int, top_k: int,
                  max_tokens: int, layout: str | int = "ht", capacity: int = 0,
-                 slots_per_rank: int = 0, slot_mode: str | int = "training"):
+                 slots_per_rank: int = 0, slot_mode: str | int = "training",
+                 dispatch_stores: str | int = "auto"):
         self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
         mode = _SLOT_MODES[slot_mode] if isinstance(slot_mode, str) else int(slot_mode)
+        stores = _STORES[dispatch_stores] if isinstance(dispatch_stores, str) else int(dispatch_stores)
         self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
-                                     self.layout, capacity, slots_per_rank, mode)
+                                     self.layout, capacity, slots_per_rank, mode, stores)
         self.ptr = ep_group_create(self.cfg)
 
     @property

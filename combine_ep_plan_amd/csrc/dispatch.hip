@@ -7,10 +7,11 @@
 // One workgroup per token (per piece of a token's row when there are too
 // few tokens to fill the GPU): the row is read once with 16-byte loads and
 // written to each of its k destinations with 16-byte stores, so x costs one
-// HBM read and every receive row one HBM write.  The stores are cached while
-// the rows written fit in twice the 256 MB Infinity Cache (the next kernel
-// then finds much of them there) and non-temporal beyond that, where cached
-// stores only leave write-backs for the next kernel to pay.
+// HBM read and every receive row one HBM write.  By default the stores are
+// cached while the rows written fit in twice the 256 MB Infinity Cache (the
+// next kernel then finds much of them there) and non-temporal beyond that,
+// where cached stores only leave write-backs for the next kernel to pay; the
+// group's configuration can fix either kind.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -150,7 +151,7 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-  const bool nt = g.n * H * 2 > kCachedStoreBytes;
+  const bool nt = g.stores == 2 || (g.stores == 0 && g.n * H * 2 > kCachedStoreBytes);
 #define L2(KK, NT)                                                                     \
   hipLaunchKernelGGL((k_dispatch_bf16<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
@@ -172,7 +173,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-  const bool nt = g.n * (H + H / 128 * 4) > kCachedStoreBytes;
+  const bool nt = g.stores == 2 || (g.stores == 0 && g.n * (H + H / 128 * 4) > kCachedStoreBytes);
 #define L2(KK, NT)                                                                     \
   hipLaunchKernelGGL((k_dispatch_fp8<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \

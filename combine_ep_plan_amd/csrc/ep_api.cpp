@@ -42,6 +42,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.R = c.num_ranks;
   geo.S = c.slots_per_rank;
   geo.slot_mode = c.slot_mode;
+  geo.stores = c.dispatch_stores;
   geo.layout = c.layout;
   geo.cap = c.capacity;
   geo.n = (int64_t)T * c.top_k;
@@ -172,6 +173,8 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
     return EP_ERR_INVALID_ARG;
   if (c.layout == EP_LAYOUT_STATIC &&
       (c.slots_per_rank < 0 || (int64_t)c.num_ranks * c.slots_per_rank > INT32_MAX))
+    return EP_ERR_INVALID_ARG;
+  if (c.dispatch_stores < EP_STORES_AUTO || c.dispatch_stores > EP_STORES_STREAMING)
     return EP_ERR_INVALID_ARG;
   if (c.slot_mode != EP_SLOTS_TRAINING &&
       !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))

@@ -50,6 +50,7 @@ struct Workspace {
 struct Geometry {
   int32_t T, k, E, R, S, layout, cap;
   int32_t slot_mode;  // 0 training (overflow flags SLOT_BUDGET), 1 inference
+  int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
   int32_t nbits;    // bits of an expert id, >= 1

@@ -111,6 +111,18 @@ typedef enum ep_slot_mode {
                              directly (seg_slot -1) and set no flag */
 } ep_slot_mode_t;
 
+/* How dispatch writes the receive rows.  Cached stores leave the rows in the
+ * 256 MB Infinity Cache for the next kernel; past about twice its size they
+ * only leave write-backs for that kernel to pay, and non-temporal stores
+ * win.  AUTO picks cached stores while the rows one dispatch writes fit in
+ * 512 MiB.  A caller that keeps several passes in flight at once (their rows
+ * together decide) can choose instead. */
+typedef enum ep_dispatch_stores {
+  EP_STORES_AUTO = 0,
+  EP_STORES_CACHED = 1,
+  EP_STORES_STREAMING = 2  /* non-temporal */
+} ep_dispatch_stores_t;
+
 /* Non-owning view of a contiguous row-major device tensor.  data must be
  * 16-byte aligned for the tags TOKENS, EXPERT_WEIGHTS and EXPERT_GRADS (rows
  * move as 16-byte vectors) and 4-byte aligned for the others; a misaligned
@@ -135,6 +147,7 @@ typedef struct ep_group_config {
   int32_t capacity;        /* LL only: rows per expert, >= 1 */
   int32_t slots_per_rank;  /* STATIC only: replica slots S per rank, >= 0 */
   int32_t slot_mode;       /* ep_slot_mode_t (STATIC only; 0 otherwise) */
+  int32_t dispatch_stores; /* ep_dispatch_stores_t */
 } ep_group_config_t;
 
 typedef struct ep_group *ep_group_t;

@@ -337,3 +337,33 @@ def test_hip_graph_replays_match_eager():
         assert np.array_equal(got[1].reshape(L.rows, H)[used], host_bits(recv_ref).reshape(L.rows, H)[used])
         assert np.array_equal(got[2], host_bits(y_ref))
         assert h.status() == 0
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_dispatch_store_kinds_give_identical_rows(fp8):
+    # the group's dispatch_stores choice changes only how rows are written:
+    # cached, non-temporal and the size-chosen default give the same bytes
+    T, H, E, k = 700, 512, 32, 4
+    idx, w, x = workloads.random_case(4242, T, H, E, k, skew=1.0)
+    L = oracle.layout(idx, E, "ht")
+    used = L.dst[L.dst >= 0]
+    outs = []
+    for stores in ("auto", "cached", "streaming"):
+        g = ep.Group(E, 4, H, k, T, "ht", dispatch_stores=stores)
+        h = ep.Handle(g, T)
+        h.plan(dev_i32(idx))
+        recv, _, _, _, _ = ep.Buffer(g).dispatch(dev_bf16(x), None, None, handle=h, fp8=fp8, recv_meta=False)
+        torch.cuda.synchronize()
+        if fp8:
+            q, s = recv
+            outs.append((q.view(torch.uint8).cpu().numpy().reshape(L.rows, H)[used], host(s)[used]))
+        else:
+            outs.append((host_bits(recv).reshape(L.rows, H)[used],))
+    if fp8:
+        oq, osc = oracle.dispatch_fp8(x, L.dst, L.rows)
+        want = (oq[used], osc[used])
+    else:
+        want = (oracle.dispatch(x, L.dst, L.rows)[used],)
+    for o in outs:
+        for a, b in zip(o, want):
+            assert np.array_equal(a, b)
