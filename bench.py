@@ -54,8 +54,8 @@ def parse():
                    help="STATIC workloads: add the replica-weight prefetch of one [4096, 1536] "
                         "bf16 projection per expert after the plan")
     p.add_argument("--dispatch-stores", choices=("auto", "cached", "streaming"), default="auto",
-                   help="how dispatch writes the receive rows (default: cached while they fit in "
-                        "512 MiB, non-temporal beyond)")
+                   help="how dispatch writes the receive rows (default: cached for 64 MiB to "
+                        "512 MiB of rows, non-temporal otherwise)")
     p.add_argument("--slot-mode", choices=("training", "inference"), default="training",
                    help="STATIC workloads: what the plan does past a rank's S-th replica slot")
     p.add_argument("--slots", type=int, default=None,

@@ -10,8 +10,10 @@
 // HBM read and every receive row one HBM write.  By default the stores are
 // cached while the rows written fit in twice the 256 MB Infinity Cache (the
 // next kernel then finds much of them there) and non-temporal beyond that,
-// where cached stores only leave write-backs for the next kernel to pay; the
-// group's configuration can fix either kind.
+// where cached stores only leave write-backs for the next kernel to pay;
+// below 64 MiB the dispatch is latency-bound and writing its dirty lines
+// back at the kernel's end costs more than the cache saves, so small batches
+// stream too.  The group's configuration can fix either kind.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -20,6 +22,14 @@ namespace epk {
 constexpr int kRowThreads = 512;
 constexpr int kUnroll = 2;
 constexpr int64_t kCachedStoreBytes = (int64_t)512 << 20;  // twice the Infinity Cache
+constexpr int64_t kCachedStoreMin = (int64_t)64 << 20;     // below: latency-bound
+
+// The size rule of the default store choice: cached between 64 MiB and
+// 512 MiB of rows written.
+static bool streaming_stores(int32_t stores, int64_t bytes) {
+  if (stores != 0) return stores == 2;
+  return bytes <= kCachedStoreMin || bytes > kCachedStoreBytes;
+}
 
 // Pieces per row: small batches (decode) split each row over several
 // workgroups, so the grid reaches about kSplitTarget workgroups; pieces are
@@ -151,7 +161,7 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-  const bool nt = g.stores == 2 || (g.stores == 0 && g.n * H * 2 > kCachedStoreBytes);
+  const bool nt = streaming_stores(g.stores, g.n * H * 2);
 #define L2(KK, NT)                                                                     \
   hipLaunchKernelGGL((k_dispatch_bf16<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \
@@ -173,7 +183,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-  const bool nt = g.stores == 2 || (g.stores == 0 && g.n * (H + H / 128 * 4) > kCachedStoreBytes);
+  const bool nt = streaming_stores(g.stores, g.n * (H + H / 128 * 4));
 #define L2(KK, NT)                                                                     \
   hipLaunchKernelGGL((k_dispatch_fp8<KK, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, \
                      reinterpret_cast<const u32x4 *>(x), ws.dst,                      \

@@ -114,9 +114,10 @@ typedef enum ep_slot_mode {
 /* How dispatch writes the receive rows.  Cached stores leave the rows in the
  * 256 MB Infinity Cache for the next kernel; past about twice its size they
  * only leave write-backs for that kernel to pay, and non-temporal stores
- * win.  AUTO picks cached stores while the rows one dispatch writes fit in
- * 512 MiB.  A caller that keeps several passes in flight at once (their rows
- * together decide) can choose instead. */
+ * win; small dispatches are latency-bound and gain nothing.  AUTO picks
+ * cached stores when one dispatch writes between 64 MiB and 512 MiB of rows.
+ * A caller that keeps several passes in flight at once (their rows together
+ * decide) can choose instead. */
 typedef enum ep_dispatch_stores {
   EP_STORES_AUTO = 0,
   EP_STORES_CACHED = 1,
