@@ -77,6 +77,7 @@ def _L():
             "orc_route": (None, [i32, i32, i32, P, P, P]),
             "orc_grouped_gemm": (None, [i32, P, i32, i32, P, P, P]),
             "orc_grouped_gemm_fp8": (None, [i32, P, i32, i32, P, P, P, P, P]),
+            "orc_swiglu": (None, [i64, i32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -373,6 +374,18 @@ def grouped_gemm(x_bits: np.ndarray, w_bits: np.ndarray, groups: np.ndarray,
     y = np.zeros((x.shape[0], N), np.uint16) if y_bits is None else np.array(y_bits, np.uint16, copy=True, order="C")
     _L().orc_grouped_gemm(gr.shape[0], _p(gr), K, N, _p(x), _p(w), _p(y))
     return y
+
+
+def swiglu(h_bits: np.ndarray) -> np.ndarray:
+    """The expert FFN's activation over [rows, 2I] bf16 bit patterns whose
+    column pairs (2j, 2j + 1) hold gate and up: [rows, I] bf16 bits of
+    bf16(silu(gate) * up)."""
+    h = _c(h_bits, np.uint16)
+    if h.ndim != 2 or h.shape[1] % 2 != 0:
+        raise ValueError("swiglu: h must be [rows, 2I]")
+    out = np.zeros((h.shape[0], h.shape[1] // 2), np.uint16)
+    _L().orc_swiglu(h.shape[0], h.shape[1] // 2, _p(h), _p(out))
+    return out
 
 
 def quantize_rows_fp8(bits: np.ndarray):

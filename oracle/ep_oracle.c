@@ -27,6 +27,9 @@
  *            Inference Adaptation", section 3.1 (top-k routing operator;
  *            grouped GEMM over the tokens grouped by expert), section 4.1
  *            (experts split over devices in contiguous blocks).
+ *            The expert FFN around the grouped GEMM is not spelled out
+ *            there; READING: the gated SiLU (SwiGLU) of the large MoE
+ *            models those pages discuss, see orc_swiglu.
  * Every point those pages leave open is marked READING below and listed in
  * the design notes of the repository.
  *
@@ -735,4 +738,23 @@ void orc_route(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *id
     for (int32_t j = 0; j < k; ++j) w[t * k + j] = j < n ? (float)(z[j] / sum) : 0.0f;
     free(taken);
   }
+}
+
+/* The activation between the expert FFN's two grouped GEMMs ([ULMoE]
+ * section 3.1 names the grouped GEMM as the core of the expert computation;
+ * READING: the activation is SwiGLU, and the first GEMM's weight rows come
+ * interleaved, row 2j the gate projection of output j and row 2j + 1 its up
+ * projection, so each output column's pair is adjacent).  For h of
+ * [rows, 2I] bf16 and every j < I:
+ *   out[r, j] = bf16( silu(g) * u ),  g = h[r, 2j],  u = h[r, 2j + 1],
+ *   silu(g) = g / (1 + e^(-g)),
+ * in double, rounded once to nearest even. */
+void orc_swiglu(int64_t rows, int32_t I, const uint16_t *h, uint16_t *out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t j = 0; j < I; ++j) {
+      const double g = orc_bf16_to_double(h[r * 2 * I + 2 * j]);
+      const double u = orc_bf16_to_double(h[r * 2 * I + 2 * j + 1]);
+      const double silu = g / (1.0 + exp(-g));
+      out[r * I + j] = orc_bf16_from_double(silu * u);
+    }
 }

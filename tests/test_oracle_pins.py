@@ -856,3 +856,70 @@ def test_route_softmax_of_large_logits_is_the_closed_form():
     assert np.all(np.isfinite(w))
     assert np.allclose(w[0], want, rtol=1e-6, atol=0)
     assert np.allclose(w[1], want, rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# the expert FFN's activation (SwiGLU over interleaved gate / up columns)
+# ---------------------------------------------------------------------------
+
+def _round_bf16_f64(v: np.ndarray) -> np.ndarray:
+    """Exact round-to-nearest-even of each float64 to bf16 bits (a zero keeps
+    its sign, which a rational cannot carry)."""
+    return np.array([(0x8000 if np.signbit(x) else 0) if x == 0 else exact_round_bf16(Fraction(float(x)))
+                     for x in np.ravel(v)], np.uint16).reshape(np.shape(v))
+
+
+def test_swiglu_matches_the_logistic_function_of_scipy():
+    # silu(g) = g * expit(g): the library's logistic function, another route
+    # to the same value; one rounding of a double either way.
+    from scipy.special import expit
+    rng = np.random.default_rng(31)
+    h = _bits(rng.uniform(-12.0, 12.0, size=(37, 2 * 24)))
+    g = bf16_bits_to_f32(h[:, 0::2]).astype(np.float64)
+    u = bf16_bits_to_f32(h[:, 1::2]).astype(np.float64)
+    want = _round_bf16_f64(g * expit(g) * u)
+    got = oracle.swiglu(h)
+    assert got.shape == (37, 24)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_swiglu_closed_forms():
+    e = np.e
+    cases = [
+        (0.0, 5.0, 0.0),                         # silu(0) = 0
+        (3.5, 0.0, 0.0),                         # up = 0
+        (1.0, 1.0, e / (1.0 + e)),               # silu(1) = e / (1 + e)
+        (2.0, -3.0, -6.0 * e * e / (1.0 + e * e)),
+        (-20.0, 1.0, -20.0 / (1.0 + np.exp(20.0))),
+        (100.0, 3.0, 300.0),                     # e^-100 vanishes below half a bf16 ulp
+    ]
+    h = _bits([[v for c in cases for v in c[:2]]])
+    got = oracle.swiglu(h)[0]
+    want = _round_bf16_f64(np.array([c[2] for c in cases]))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_swiglu_takes_the_gate_from_the_even_column():
+    # swapping gate and up changes the value: silu(2) * -3 against silu(-3) * 2
+    got = oracle.swiglu(_bits([[2.0, -3.0, -3.0, 2.0]]))[0]
+    assert bf16_bits_to_f32(got[0:1])[0] < -5.0
+    assert -0.3 < bf16_bits_to_f32(got[1:2])[0] < -0.2
+
+
+def test_gemm_then_swiglu_equals_separate_gate_and_up_projections():
+    # Integer inputs make every GEMM sum exact in double, so the interleaved
+    # single GEMM followed by the activation must equal the two projections
+    # done apart with numpy and the activation from scipy.
+    from scipy.special import expit
+    rng = np.random.default_rng(32)
+    rows, K, I = 19, 64, 16
+    x = rng.integers(-3, 4, size=(rows, K)).astype(np.float64)
+    wg = rng.integers(-2, 3, size=(I, K)).astype(np.float64) / 8.0
+    wu = rng.integers(-2, 3, size=(I, K)).astype(np.float64) / 8.0
+    w1 = np.empty((1, 2 * I, K))
+    w1[0, 0::2], w1[0, 1::2] = wg, wu
+    h = oracle.grouped_gemm(_bits(x), _bits(w1), np.array([[0, rows, 0]], np.int32))
+    got = oracle.swiglu(h)
+    hg = bf16_bits_to_f32(_round_bf16_f64(x @ wg.T)).astype(np.float64)
+    hu = bf16_bits_to_f32(_round_bf16_f64(x @ wu.T)).astype(np.float64)
+    np.testing.assert_array_equal(got, _round_bf16_f64(hg * expit(hg) * hu))
