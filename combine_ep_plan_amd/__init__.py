@@ -28,6 +28,7 @@ __all__ = [
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
+    "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
     "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
     "STORES_AUTO", "STORES_CACHED", "STORES_STREAMING",
@@ -118,6 +119,8 @@ def load_library():
         "ep_prefetch_replicas": (S, [c_void_p, _T, _T, c_void_p]),
         "ep_expert_gemm": (S, [c_void_p, _T, _T, _T, _T, c_void_p]),
         "ep_expert_gemm_fp8": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_expert_gemm_swiglu": (S, [c_void_p, _T, _T, _T, _T, c_void_p]),
+        "ep_expert_gemm_fp8_swiglu": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -293,22 +296,37 @@ def ep_prefetch_replicas(h: int, expert_weights: torch.Tensor, slot_weights: tor
 
 
 def ep_expert_gemm(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
-                   slot_weights: torch.Tensor | None, out: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_expert_gemm(
+                   slot_weights: torch.Tensor | None, out: torch.Tensor, stream=None,
+                   swiglu: bool = False) -> None:
+    name = "ep_expert_gemm_swiglu" if swiglu else "ep_expert_gemm"
+    _check(getattr(load_library(), name)(
         c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
-        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream)),
-        "ep_expert_gemm")
+        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream)), name)
+
+
+def ep_expert_gemm_swiglu(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
+                          slot_weights: torch.Tensor | None, out: torch.Tensor, stream=None) -> None:
+    ep_expert_gemm(h, recv_tokens, expert_weights, slot_weights, out, stream, swiglu=True)
 
 
 def ep_expert_gemm_fp8(h: int, recv_tokens: torch.Tensor, recv_scales: torch.Tensor,
                        expert_weights: torch.Tensor, expert_scales: torch.Tensor,
                        slot_weights: torch.Tensor | None, slot_scales: torch.Tensor | None,
-                       out: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_expert_gemm_fp8(
+                       out: torch.Tensor, stream=None, swiglu: bool = False) -> None:
+    name = "ep_expert_gemm_fp8_swiglu" if swiglu else "ep_expert_gemm_fp8"
+    _check(getattr(load_library(), name)(
         c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
         _tensor(expert_weights, TAG_EXPERT_WEIGHTS), _tensor(expert_scales, TAG_FP8_SCALES),
         _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(slot_scales, TAG_FP8_SCALES),
-        _tensor(out, TAG_TOKENS), _stream(stream)), "ep_expert_gemm_fp8")
+        _tensor(out, TAG_TOKENS), _stream(stream)), name)
+
+
+def ep_expert_gemm_fp8_swiglu(h: int, recv_tokens: torch.Tensor, recv_scales: torch.Tensor,
+                              expert_weights: torch.Tensor, expert_scales: torch.Tensor,
+                              slot_weights: torch.Tensor | None, slot_scales: torch.Tensor | None,
+                              out: torch.Tensor, stream=None) -> None:
+    ep_expert_gemm_fp8(h, recv_tokens, recv_scales, expert_weights, expert_scales, slot_weights,
+                       slot_scales, out, stream, swiglu=True)
 
 
 # ---------------------------------------------------------------------------
@@ -513,30 +531,35 @@ class Buffer:
 
     def expert_gemm(self, recv: torch.Tensor, expert_weights: torch.Tensor, handle: Handle,
                     slots: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, swiglu: bool = False) -> torch.Tensor:
         """Grouped GEMM of the experts over the received rows: ``recv``
-        [rows, K] (any leading shape) times each group's [N, K] weights."""
+        [rows, K] (any leading shape) times each group's [N, K] weights.
+        With ``swiglu`` the weight rows interleave gate (even) and up (odd)
+        projections and the result is [rows, N/2] of silu(gate) * up."""
         N = expert_weights.shape[1]
         rows = handle.recv_rows
         if out is None:
-            out = torch.empty((rows, N), dtype=torch.bfloat16, device=recv.device)
+            out = torch.empty((rows, N // 2 if swiglu else N), dtype=torch.bfloat16, device=recv.device)
         ep_expert_gemm(handle.ptr, recv.view(rows, expert_weights.shape[2]), expert_weights, slots,
-                       out, stream)
+                       out, stream, swiglu=swiglu)
         return out
 
     def expert_gemm_fp8(self, recv: torch.Tensor, recv_scales: torch.Tensor,
                         expert_weights: torch.Tensor, expert_scales: torch.Tensor, handle: Handle,
                         slots: torch.Tensor | None = None, slot_scales: torch.Tensor | None = None,
-                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, stream=None,
+                        swiglu: bool = False) -> torch.Tensor:
         """The grouped GEMM on FP8 operands: ``recv`` e4m3 [rows, K] with fp32
         ``recv_scales`` [rows, K/128] (the FP8 dispatch output), weights e4m3
-        [E, N, K] with fp32 scales [E, N, K/128]."""
+        [E, N, K] with fp32 scales [E, N, K/128].  ``swiglu`` as in
+        ``expert_gemm``."""
         N, K = expert_weights.shape[1], expert_weights.shape[2]
         rows = handle.recv_rows
         if out is None:
-            out = torch.empty((rows, N), dtype=torch.bfloat16, device=recv.device)
+            out = torch.empty((rows, N // 2 if swiglu else N), dtype=torch.bfloat16, device=recv.device)
         ep_expert_gemm_fp8(handle.ptr, recv.view(rows, K), recv_scales.view(rows, K // 128),
-                           expert_weights, expert_scales, slots, slot_scales, out, stream)
+                           expert_weights, expert_scales, slots, slot_scales, out, stream,
+                           swiglu=swiglu)
         return out
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,

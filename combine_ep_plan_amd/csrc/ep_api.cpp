@@ -513,9 +513,10 @@ ep_status_t ep_prefetch_replicas(ep_handle_t h, const ep_tensor_t *expert_weight
                                          as_stream(stream)));
 }
 
-ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
-                           const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
-                           ep_tensor_t *out, void *stream) {
+// glu: the SwiGLU epilogue (out has N / 2 columns; N % 16 == 0)
+static ep_status_t expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                               const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
+                               ep_tensor_t *out, void *stream, bool glu) {
   if (!h) return EP_ERR_INVALID_ARG;
   const epk::Geometry &g = h->geo;
   ep_status_t st = check_tensor(recv_tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
@@ -528,7 +529,9 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
   if (w->ndim != 3 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
   const int64_t N = w->sizes[1], K = w->sizes[2];
   if (K <= 0 || K % 64 != 0 || K > INT32_MAX || N < 1 || N > INT32_MAX) return EP_ERR_BAD_SHAPE;
-  if (!is_rows(recv_tokens, g.rows, K) || !is_rows(out, g.rows, N)) return EP_ERR_BAD_SHAPE;
+  if (glu && N % 16 != 0) return EP_ERR_BAD_SHAPE;
+  if (!is_rows(recv_tokens, g.rows, K) || !is_rows(out, g.rows, glu ? N / 2 : N))
+    return EP_ERR_BAD_SHAPE;
   const uint16_t *wslot = nullptr;
   if (slot_weights) {
     st = check_tensor(slot_weights, EP_TAG_EXPERT_WEIGHTS, EP_DTYPE_BF16);
@@ -546,13 +549,29 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
   return hip_status(epk::launch_grouped_gemm(g, h->ws, static_cast<const uint16_t *>(recv_tokens->data),
                                              static_cast<const uint16_t *>(w->data), wslot,
                                              (int32_t)K, (int32_t)N,
-                                             static_cast<uint16_t *>(out->data), as_stream(stream)));
+                                             static_cast<uint16_t *>(out->data), glu,
+                                             as_stream(stream)));
 }
 
-ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
-                               const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,
-                               const ep_tensor_t *expert_scales, const ep_tensor_t *slot_weights,
-                               const ep_tensor_t *slot_scales, ep_tensor_t *out, void *stream) {
+ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                           const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
+                           ep_tensor_t *out, void *stream) {
+  return expert_gemm(h, recv_tokens, expert_weights, slot_weights, out, stream, false);
+}
+
+ep_status_t ep_expert_gemm_swiglu(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                                  const ep_tensor_t *expert_weights,
+                                  const ep_tensor_t *slot_weights, ep_tensor_t *out,
+                                  void *stream) {
+  return expert_gemm(h, recv_tokens, expert_weights, slot_weights, out, stream, true);
+}
+
+static ep_status_t expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                                   const ep_tensor_t *recv_scales,
+                                   const ep_tensor_t *expert_weights,
+                                   const ep_tensor_t *expert_scales,
+                                   const ep_tensor_t *slot_weights, const ep_tensor_t *slot_scales,
+                                   ep_tensor_t *out, void *stream, bool glu) {
   if (!h) return EP_ERR_INVALID_ARG;
   const epk::Geometry &g = h->geo;
   ep_status_t st = check_tensor(recv_tokens, EP_TAG_TOKENS, EP_DTYPE_FP8_E4M3);
@@ -569,13 +588,14 @@ ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
   if (w->ndim != 3 || w->sizes[0] != g.E) return EP_ERR_BAD_SHAPE;
   const int64_t N = w->sizes[1], K = w->sizes[2];
   if (K <= 0 || K % 128 != 0 || K > INT32_MAX || N < 1 || N > INT32_MAX) return EP_ERR_BAD_SHAPE;
+  if (glu && N % 16 != 0) return EP_ERR_BAD_SHAPE;
   // the kernel addresses a tile's 128 rows of K bytes through 32-bit buffer offsets
   if (K > kFp8GemmMaxK) return EP_ERR_UNSUPPORTED;
   const int64_t NB = K / 128;
   if (!(ws->ndim == 3 && ws->sizes[0] == g.E && ws->sizes[1] == N && ws->sizes[2] == NB))
     return EP_ERR_BAD_SHAPE;
   if (!is_rows(recv_tokens, g.rows, K) || !is_rows(recv_scales, g.rows, NB) ||
-      !is_rows(out, g.rows, N))
+      !is_rows(out, g.rows, glu ? N / 2 : N))
     return EP_ERR_BAD_SHAPE;
   if ((slot_weights == nullptr) != (slot_scales == nullptr)) return EP_ERR_INVALID_ARG;
   const uint8_t *wslot = nullptr;
@@ -601,7 +621,26 @@ ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
       g, h->ws, static_cast<const uint8_t *>(recv_tokens->data),
       static_cast<const float *>(recv_scales->data), static_cast<const uint8_t *>(w->data),
       static_cast<const float *>(ws->data), wslot, swslot, (int32_t)K, (int32_t)N,
-      static_cast<uint16_t *>(out->data), as_stream(stream)));
+      static_cast<uint16_t *>(out->data), glu, as_stream(stream)));
+}
+
+ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                               const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,
+                               const ep_tensor_t *expert_scales, const ep_tensor_t *slot_weights,
+                               const ep_tensor_t *slot_scales, ep_tensor_t *out, void *stream) {
+  return expert_gemm_fp8(h, recv_tokens, recv_scales, expert_weights, expert_scales, slot_weights,
+                         slot_scales, out, stream, false);
+}
+
+ep_status_t ep_expert_gemm_fp8_swiglu(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                                      const ep_tensor_t *recv_scales,
+                                      const ep_tensor_t *expert_weights,
+                                      const ep_tensor_t *expert_scales,
+                                      const ep_tensor_t *slot_weights,
+                                      const ep_tensor_t *slot_scales, ep_tensor_t *out,
+                                      void *stream) {
+  return expert_gemm_fp8(h, recv_tokens, recv_scales, expert_weights, expert_scales, slot_weights,
+                         slot_scales, out, stream, true);
 }
 
 }  // extern "C"

@@ -92,11 +92,11 @@ hipError_t launch_prefetch(const Geometry &g, const Workspace &ws, const uint8_t
 int32_t gemm_max_tiles(const Geometry &g);
 hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
-                               uint16_t *y, hipStream_t s);
+                               uint16_t *y, bool glu, hipStream_t s);
 hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const uint8_t *x,
                                    const float *sx, const uint8_t *w, const float *sw,
                                    const uint8_t *wslot, const float *swslot, int32_t K, int32_t N,
-                                   uint16_t *y, hipStream_t s);
+                                   uint16_t *y, bool glu, hipStream_t s);
 hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
                              int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
 

@@ -158,6 +158,24 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
 // ---------------------------------------------------------------------------
 // grouped GEMM
 
+// SwiGLU epilogue of the expert FFN's first GEMM.  Its weight rows come
+// interleaved (row 2j the gate projection of output j, row 2j + 1 the up
+// projection), so a 16-byte vector of the staged bf16 output tile holds four
+// (gate, up) pairs, gate in the low half of each 32-bit word.  Each pair
+// becomes bf16(silu(gate) * up), silu(g) = g / (1 + e^-g) in fp32 (a signed
+// zero where e^-g overflows, g < -88.7: the exact value is below 3e-37 |up|).
+__device__ __forceinline__ uint2 swiglu4(u32x4 v) {
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  float o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g = __uint_as_float(in[i] << 16), u = __uint_as_float(in[i] & 0xFFFF0000u);
+    o[i] = g / (1.0f + __expf(-g)) * u;
+  }
+  return uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+
+template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
 #undef GLOAD
 #undef SWRITE
 
-  if ((N & 7) == 0) {
+  if (GLU || (N & 7) == 0) {   // a SwiGLU launch has N % 16 == 0
     // Through LDS: the tile as bf16 rows of 128, the 16-byte chunk of column c
     // of row r stored at chunk (c / 8) ^ (((r / 4) % 4) * 4), so the two
     // half-waves of a store (rows r and r + 4) land on different banks; then
@@ -328,9 +346,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
       const int idx = tid + q * kGemmThreads;
       const int rr = idx / (kBN / 8), cv = idx % (kBN / 8);
       const int col = n0 + cv * 8;
-      if (rr < rows && col < N)
-        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
-            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+      if (rr < rows && col < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+        if constexpr (GLU)   // columns col .. col + 7 give outputs col / 2 .. col / 2 + 3
+          *reinterpret_cast<uint2 *>(Y + (int64_t)(row0 + rr) * (N / 2) + col / 2) = swiglu4(v);
+        else
+          *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) = v;
+      }
     }
 #undef OSW
     return;
@@ -363,6 +385,7 @@ constexpr int kLoadsB2 = kBN2 * kChunks / kGemmThreads;   // ... and of W
 constexpr int kSlabA2 = kBM2 * kChunks, kSlabB2 = kBN2 * kChunks;
 constexpr int kBufDword3 = 0x00020000;                    // buffer resource word 3 (raw, 32-bit data)
 
+template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
@@ -532,7 +555,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
 #undef GLOAD_B
 #undef GLOAD_A
 
-  if ((N & 7) == 0) {
+  if (GLU || (N & 7) == 0) {   // a SwiGLU launch has N % 16 == 0
     // through LDS as bf16 rows of 256 (same chunk swizzle as the 128 x 128
     // kernel's epilogue), then 16-byte row stores
     __syncthreads();
@@ -559,9 +582,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
       const int idx = tid + q * kGemmThreads;
       const int rr = idx / (kBN2 / 8), cv = idx % (kBN2 / 8);
       const int col = n0 + cv * 8;
-      if (rr < rows && col < N)
-        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
-            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+      if (rr < rows && col < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+        if constexpr (GLU)   // columns col .. col + 7 give outputs col / 2 .. col / 2 + 3
+          *reinterpret_cast<uint2 *>(Y + (int64_t)(row0 + rr) * (N / 2) + col / 2) = swiglu4(v);
+        else
+          *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) = v;
+      }
     }
 #undef OSW
     return;
@@ -605,6 +632,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kScaleBufs = 4;
 constexpr int kF8Block = 128;  // K per scale; also the slab depth in bytes
 
+template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
     const u32x4 *__restrict__ X, const float *__restrict__ SX, const u32x4 *__restrict__ W,
     const float *__restrict__ SW, const u32x4 *__restrict__ Wslot,
@@ -793,7 +821,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
 #undef GLOAD
 #undef SWRITE
 
-  if ((N & 7) == 0) {
+  if (GLU || (N & 7) == 0) {   // a SwiGLU launch has N % 16 == 0
     // Through LDS: the tile as bf16 rows of 128, the 16-byte chunk of column c
     // of row r stored at chunk (c / 8) ^ (((r / 4) % 4) * 4), so the two
     // half-waves of a store (rows r and r + 4) land on different banks; then
@@ -822,9 +850,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
       const int idx = tid + q * kGemmThreads;
       const int rr = idx / (kBN / 8), cv = idx % (kBN / 8);
       const int col = n0 + cv * 8;
-      if (rr < rows && col < N)
-        *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) =
-            *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+      if (rr < rows && col < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+        if constexpr (GLU)   // columns col .. col + 7 give outputs col / 2 .. col / 2 + 3
+          *reinterpret_cast<uint2 *>(Y + (int64_t)(row0 + rr) * (N / 2) + col / 2) = swiglu4(v);
+        else
+          *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) = v;
+      }
     }
 #undef OSW
     return;
@@ -855,13 +887,20 @@ int32_t gemm_max_tiles(const Geometry &g) {
 // The 256 x 256 kernel pays off once the groups fill its row tiles: at
 // least 128 receive rows per expert on average, and N of a full column tile.
 // Its buffer offsets are 32-bit: a tile's rows of X must span under 2 GiB.
+// the epilogue is a template parameter: plain bf16 output or SwiGLU pairs
+#define GEMM_LAUNCH(KERN, ...)                                \
+  do {                                                        \
+    if (glu) hipLaunchKernelGGL(KERN<true>, __VA_ARGS__);     \
+    else hipLaunchKernelGGL(KERN<false>, __VA_ARGS__);        \
+  } while (0)
+
 static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
   return N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E && (int64_t)kBM2 * K * 2 <= INT32_MAX;
 }
 
 hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
-                               uint16_t *y, hipStream_t s) {
+                               uint16_t *y, bool glu, hipStream_t s) {
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
@@ -873,7 +912,7 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
     const int32_t ncol = (N + kBN2 - 1) / kBN2;
     int64_t blocks = (int64_t)max2 * ncol;
     blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(k_grouped_gemm_256, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+    GEMM_LAUNCH(k_grouped_gemm_256, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
                        reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
                        reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
                        g.E, ncol, y);
@@ -883,7 +922,7 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
   const int32_t ncol = (N + kBN - 1) / kBN;
   int64_t blocks = (int64_t)max_tiles * ncol;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the XCD remap needs a multiple of 8
-  hipLaunchKernelGGL(k_grouped_gemm, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+  GEMM_LAUNCH(k_grouped_gemm, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
                      reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
                      reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
                      g.E, ncol, y);
@@ -893,7 +932,7 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
 hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const uint8_t *x,
                                    const float *sx, const uint8_t *w, const float *sw,
                                    const uint8_t *wslot, const float *swslot, int32_t K, int32_t N,
-                                   uint16_t *y, hipStream_t s) {
+                                   uint16_t *y, bool glu, hipStream_t s) {
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
@@ -901,7 +940,7 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
   const int32_t ncol = (N + kBN - 1) / kBN;
   int64_t blocks = (int64_t)max_tiles * ncol;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+  GEMM_LAUNCH(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
                      reinterpret_cast<const u32x4 *>(x), sx, reinterpret_cast<const u32x4 *>(w), sw,
                      reinterpret_cast<const u32x4 *>(wslot), swslot, ws.gemm_tiles,
                      ws.gemm_ntiles, K, N, g.E, ncol, y);

@@ -382,6 +382,24 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
                            const ep_tensor_t *expert_weights, const ep_tensor_t *slot_weights,
                            ep_tensor_t *out, void *stream);
 
+/* The expert FFN's first GEMM with its activation fused into the store
+ * ("Ultra-Large MoE Models" article, section 3.1, names the grouped GEMM as
+ * the core of the expert computation; the activation is not given there,
+ * and this library reads it as SwiGLU).  The weight rows interleave the two
+ * projections: row 2j of each [N, K] matrix is the gate of output j, row
+ * 2j + 1 its up projection.  With h[i, n] the bf16 result ep_expert_gemm
+ * would write, for every group row i and j < N/2:
+ *   out[i, j] = bf16( silu(h[i, 2j]) * h[i, 2j + 1] ),
+ *   silu(g) = g / (1 + e^-g) in fp32 (where e^-g overflows, g < -88.7,
+ *   the result is a signed zero; the exact value is below 3e-37 |u|).
+ * Arguments as for ep_expert_gemm, except out: bf16 [recv_rows, N/2], tag
+ * TOKENS, and N % 16 == 0 (else EP_ERR_BAD_SHAPE).  The FFN's second GEMM
+ * is ep_expert_gemm over out with K = N/2. */
+ep_status_t ep_expert_gemm_swiglu(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                                  const ep_tensor_t *expert_weights,
+                                  const ep_tensor_t *slot_weights, ep_tensor_t *out,
+                                  void *stream);
+
 /* The same grouped GEMM on FP8 operands ("Ultra-Large MoE Models" article,
  * section 3.1, over the receive rows the FP8 dispatch delivers: e4m3 codes
  * with one fp32 scale per 128 channels, NCCL EP listing, Table IV).  The
@@ -408,6 +426,18 @@ ep_status_t ep_expert_gemm_fp8(ep_handle_t h, const ep_tensor_t *recv_tokens,
                                const ep_tensor_t *recv_scales, const ep_tensor_t *expert_weights,
                                const ep_tensor_t *expert_scales, const ep_tensor_t *slot_weights,
                                const ep_tensor_t *slot_scales, ep_tensor_t *out, void *stream);
+
+/* ep_expert_gemm_fp8 with the SwiGLU store of ep_expert_gemm_swiglu: the
+ * same interleaved weight rows (codes and scales), out bf16 [recv_rows, N/2],
+ * N % 16 == 0 (else EP_ERR_BAD_SHAPE); other arguments and errors as for
+ * ep_expert_gemm_fp8. */
+ep_status_t ep_expert_gemm_fp8_swiglu(ep_handle_t h, const ep_tensor_t *recv_tokens,
+                                      const ep_tensor_t *recv_scales,
+                                      const ep_tensor_t *expert_weights,
+                                      const ep_tensor_t *expert_scales,
+                                      const ep_tensor_t *slot_weights,
+                                      const ep_tensor_t *slot_scales, ep_tensor_t *out,
+                                      void *stream);
 
 #ifdef __cplusplus
 }

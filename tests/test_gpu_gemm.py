@@ -94,7 +94,9 @@ CASES = [
 ]
 
 
-def _run(c):
+def _run(c, glu=None):
+    """One case through the C ABI; with a list ``glu``, the same GEMM with the
+    SwiGLU store is run too and its host bits appended to it."""
     name, T, E, k, kind, cap, R, S, mode, K, N, skew, mask, seed, use_slots = c
     print(f"[gemm] {name} T={T} E={E} k={k} {kind} K={K} N={N}", flush=True)
     idx, w, _ = workloads.random_case(3000 + seed, T, 8, E, k, mask_frac=mask, skew=skew)
@@ -113,8 +115,14 @@ def _run(c):
         w_all = np.concatenate([wb, sb.reshape(R * S, N, K)])
     y = torch.full((L.rows, N), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     buf = ep.Buffer(g)
-    buf.expert_gemm(dev_bf16(xb), dev_bf16(wb.reshape(E, N * K)).view(E, N, K), h, slots_t, out=y)
+    wt = dev_bf16(wb.reshape(E, N * K)).view(E, N, K)
+    buf.expert_gemm(dev_bf16(xb), wt, h, slots_t, out=y)
+    if glu is not None:
+        a = torch.full((L.rows, N // 2), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        buf.expert_gemm(dev_bf16(xb), wt, h, slots_t, out=a, swiglu=True)
     torch.cuda.synchronize()
+    if glu is not None:
+        glu.append(host_bits(a))
     groups = oracle.expert_groups(L, kind, E, cap=cap, R=R, S=S, use_slots=use_slots)
     ref = oracle.grouped_gemm(xb, w_all, groups, np.full((L.rows, N), SENTINEL, np.uint16))
     return host_bits(y), ref, xb, w_all, groups, L

@@ -139,7 +139,9 @@ CASES = [
 ]
 
 
-def _run(c):
+def _run(c, glu=None):
+    """One case through the C ABI; with a list ``glu``, the same GEMM with the
+    SwiGLU store is run too and its host bits appended to it."""
     name, T, E, k, kind, cap, R, S, mode, K, N, skew, mask, seed, use_slots = c
     print(f"[gemm_fp8] {name} T={T} E={E} k={k} {kind} K={K} N={N}", flush=True)
     idx, _, _ = workloads.random_case(3200 + seed, T, 8, E, k, mask_frac=mask, skew=skew)
@@ -171,8 +173,14 @@ def _run(c):
         w_all = np.concatenate([w, ws_.reshape(R * S, N, K)])
         sw_all = np.concatenate([sw, wss.reshape(R * S, N, NB)])
     y = torch.full((L.rows, N), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    buf.expert_gemm_fp8(dev_u8(x), dev_f32(sx), dev_u8(w), dev_f32(sw), h, slots_t, slot_sc_t, out=y)
+    xd, sxd, wd, swd = dev_u8(x), dev_f32(sx), dev_u8(w), dev_f32(sw)
+    buf.expert_gemm_fp8(xd, sxd, wd, swd, h, slots_t, slot_sc_t, out=y)
+    if glu is not None:
+        a = torch.full((L.rows, N // 2), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        buf.expert_gemm_fp8(xd, sxd, wd, swd, h, slots_t, slot_sc_t, out=a, swiglu=True)
     torch.cuda.synchronize()
+    if glu is not None:
+        glu.append(host_bits(a))
     groups = oracle.expert_groups(L, kind, E, cap=cap, R=R, S=S, use_slots=use_slots)
     ref = oracle.grouped_gemm_fp8(x, sx, w_all, sw_all, groups, np.full((L.rows, N), SENTINEL, np.uint16))
     return host_bits(y), ref, (x, sx, w_all, sw_all), groups, L
