@@ -65,6 +65,9 @@ def parse():
                         "[rows, H] bf16 tokens times one [N, H] bf16 matrix per expert (through "
                         "the prefetch slots with --prefetch); reported beside the step, its "
                         "roofline against the bf16 MFMA peak")
+    p.add_argument("--swiglu", action="store_true",
+                   help="with --gemm: the FFN's first GEMM with the SwiGLU store (weight rows "
+                        "interleave gate and up; output N/2 columns of silu(gate) * up)")
     p.add_argument("--microbatches", type=int, default=1, metavar="M",
                    help="one step = M independent micro-batches of the workload (forward chain "
                         "plan -> dispatch -> combine), each with its own inputs, handle, receive "
@@ -395,6 +398,9 @@ def main():
     inp = workloads.make_inputs(name, 0, a.rho) if name == "sweep" else workloads.make_inputs(name)
     c = inp.cfg
     S = c.S if a.slots is None else a.slots
+    if a.swiglu and (not a.gemm or a.gemm % 16):
+        print("bench.py: --swiglu needs --gemm N with N a multiple of 16", file=sys.stderr)
+        sys.exit(2)
     if (a.prefetch or a.slots is not None or a.slot_mode != "training") and c.layout != "static":
         print("bench.py: --prefetch, --slots and --slot-mode need a STATIC workload (sweep, training)",
               file=sys.stderr)
@@ -471,14 +477,17 @@ def main():
     else:
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, LS["s"])))
     if a.gemm:
-        gy_out = torch.empty((h.recv_rows, a.gemm), dtype=torch.bfloat16, device=dev)
+        gy_out = torch.empty((h.recv_rows, a.gemm // 2 if a.swiglu else a.gemm), dtype=torch.bfloat16,
+                             device=dev)
         if gemm_fp8:   # straight from the FP8 dispatch output
             rq2d = rq.view(h.recv_rows, c.H)
             ops.append(("gemm", lambda: ep.ep_expert_gemm_fp8(
-                h.ptr, rq2d, rs, wts, wsc, slots, slot_sc if a.prefetch else None, gy_out, LS["s"])))
+                h.ptr, rq2d, rs, wts, wsc, slots, slot_sc if a.prefetch else None, gy_out, LS["s"],
+                swiglu=a.swiglu)))
         else:
             recv2d = recv.view(h.recv_rows, c.H)
-            ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"])))
+            ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"],
+                                                          swiglu=a.swiglu)))
     ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, LS["s"])))
     if train:
         ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, LS["s"])))
@@ -583,9 +592,11 @@ def main():
         else:
             el, sc = 2, 0.0
             peak = MFMA_BF16_PEAK_TFLOPS
-        ab["gemm"] = int(grows * c.H * (el + sc) + mats * a.gemm * c.H * (el + sc) + grows * a.gemm * 2)
+        n_out = a.gemm // 2 if a.swiglu else a.gemm
+        ab["gemm"] = int(grows * c.H * (el + sc) + mats * a.gemm * c.H * (el + sc) + grows * n_out * 2)
         tflops = flops / (per_us["gemm"] * 1e-6) / 1e12
         gemm_info = {"N": a.gemm, "K": c.H, "dtype": "fp8-e4m3" if gemm_fp8 else "bf16",
+                     "epilogue": "swiglu" if a.swiglu else "plain",
                      "rows": grows, "weight_matrices": mats, "flops": flops,
                      "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1)}
         # the binding resource: MFMA time of the flops or HBM time of the bytes

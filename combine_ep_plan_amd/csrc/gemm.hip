@@ -162,15 +162,17 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
 // interleaved (row 2j the gate projection of output j, row 2j + 1 the up
 // projection), so a 16-byte vector of the staged bf16 output tile holds four
 // (gate, up) pairs, gate in the low half of each 32-bit word.  Each pair
-// becomes bf16(silu(gate) * up), silu(g) = g / (1 + e^-g) in fp32 (a signed
-// zero where e^-g overflows, g < -88.7: the exact value is below 3e-37 |up|).
+// becomes bf16(silu(gate) * up), silu(g) = g / (1 + e^-g) in fp32 with the
+// hardware reciprocal (about 1 ulp of fp32, far below the bf16 rounding).  Below
+// g = -87.34 the reciprocal is under the smallest normal fp32 and flushes, so
+// the result is a signed zero where the exact value is below 1.1e-36 |up|.
 __device__ __forceinline__ uint2 swiglu4(u32x4 v) {
   const uint32_t in[4] = {v.x, v.y, v.z, v.w};
   float o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float g = __uint_as_float(in[i] << 16), u = __uint_as_float(in[i] & 0xFFFF0000u);
-    o[i] = g / (1.0f + __expf(-g)) * u;
+    o[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
   }
   return uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
 }

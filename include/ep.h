@@ -390,8 +390,9 @@ ep_status_t ep_expert_gemm(ep_handle_t h, const ep_tensor_t *recv_tokens,
  * 2j + 1 its up projection.  With h[i, n] the bf16 result ep_expert_gemm
  * would write, for every group row i and j < N/2:
  *   out[i, j] = bf16( silu(h[i, 2j]) * h[i, 2j + 1] ),
- *   silu(g) = g / (1 + e^-g) in fp32 (where e^-g overflows, g < -88.7,
- *   the result is a signed zero; the exact value is below 3e-37 |u|).
+ *   silu(g) = g / (1 + e^-g) in fp32, the reciprocal to about 1 ulp of
+ *   fp32 (for g < -87.34 the reciprocal flushes to zero and so does the
+ *   result, where the exact value is below 1.1e-36 |u|).
  * Arguments as for ep_expert_gemm, except out: bf16 [recv_rows, N/2], tag
  * TOKENS, and N % 16 == 0 (else EP_ERR_BAD_SHAPE).  The FFN's second GEMM
  * is ep_expert_gemm over out with K = N/2. */

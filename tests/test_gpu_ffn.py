@@ -9,8 +9,9 @@ checks: rows no group covers are not written; the activation against the
 oracle's (its own GEMM, then its SwiGLU in double) norm-wise, the error of
 the GEMM carried through silu(g) * u; and, elementwise, against the plain
 kernel's own output put through silu(g) * u in double, within one bf16
-rounding (the kernel evaluates e^-g and the division in fp32, so where e^-g
-overflows, g < -88.7, it writes a signed zero for a value below 3e-37 |u|)."""
+rounding (the kernel evaluates e^-g and the reciprocal in fp32; for g < -87.34
+the reciprocal flushes, and it writes a signed zero for a value below
+1.1e-36 |u|)."""
 
 from __future__ import annotations
 
@@ -54,9 +55,9 @@ def check_glu(act, y_plain, ref_plain, groups, rows):
     g, u = h[:, 0::2], h[:, 1::2]
     with np.errstate(over="ignore"):
         own = g / (1.0 + np.exp(-g)) * u
-    # where e^-g overflows fp32 (g < -88.7) the kernel's quotient is 0 and the
-    # exact value is below 89 e^-88.7 |u| < 3e-37 |u|
-    bad = np.abs(got - own) > np.abs(own) * 2.0 ** -8 * 1.01 + 3e-37 * np.abs(u) + 2.0 ** -126
+    # for g < -87.34 the kernel's reciprocal of 1 + e^-g is below the smallest
+    # normal fp32 and flushes to 0; the exact value is below 87.34 e^-87.34 |u|
+    bad = np.abs(got - own) > np.abs(own) * 2.0 ** -8 * 1.01 + 1.1e-36 * np.abs(u) + 2.0 ** -126
     if bad.any():
         at = tuple(np.argwhere(bad)[:6].T)
         raise AssertionError(f"got {got[at]} own {own[at]} gate {g[at]} up {u[at]}")
