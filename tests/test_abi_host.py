@@ -336,6 +336,28 @@ def test_expert_gemm_argument_validation(lib):
     lib.ep_group_destroy(g)
 
 
+def test_expert_gemm_swiglu_argument_validation(lib):
+    # out has N/2 columns and N must be a multiple of 16; the rest as for the plain GEMMs
+    W, TK, SC = ep.TAG_EXPERT_WEIGHTS, ep.TAG_TOKENS, ep.TAG_FP8_SCALES
+    g, h, _ = make_handle(lib)                       # HT, T=64, k=2: 128 rows, E=8
+    G = lib.ep_expert_gemm_swiglu
+    x, w = T(BF16, TK, 128, 64), T(BF16, W, 8, 32, 64)
+    assert G(None, x, w, None, T(BF16, TK, 128, 16), None) == 1
+    assert G(h, x, w, None, T(BF16, TK, 128, 32), None) == 4                        # N columns, not N/2
+    assert G(h, x, T(BF16, W, 8, 40, 64), None, T(BF16, TK, 128, 20), None) == 4    # N % 16
+    assert G(h, x, w, None, T(BF16, TK, 128, 16), None) == 5                        # accepted; not planned
+    G8 = lib.ep_expert_gemm_fp8_swiglu
+    x8, sx = T(FP8, TK, 128, 128), T(F32, SC, 128, 1)
+    w8, sw = T(FP8, W, 8, 32, 128), T(F32, SC, 8, 32, 1)
+    assert G8(None, x8, sx, w8, sw, None, None, T(BF16, TK, 128, 16), None) == 1
+    assert G8(h, x8, sx, w8, sw, None, None, T(BF16, TK, 128, 32), None) == 4
+    assert G8(h, x8, sx, T(FP8, W, 8, 40, 128), T(F32, SC, 8, 40, 1), None, None,
+              T(BF16, TK, 128, 20), None) == 4
+    assert G8(h, x8, sx, w8, sw, None, None, T(BF16, TK, 128, 16), None) == 5
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
+
+
 def test_prefetch_accepts_fp8_weight_scales(lib):
     P = lib.ep_prefetch_replicas
     W, SC = ep.TAG_EXPERT_WEIGHTS, ep.TAG_FP8_SCALES
