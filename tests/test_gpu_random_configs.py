@@ -8,7 +8,8 @@ ABI and is compared with the oracle: tables, dispatched rows, FP8 codes and
 scales and combine-backward rows bit-exact; combine, dispatch backward and
 grad_w as in the parity tests (one bf16 ulp elementwise and 2e-3
 norm-wise).  A second sweep runs both grouped GEMMs (bf16 and FP8) on random
-K, N, layouts and prefetch slots, to the GEMM tests' tolerances."""
+K, N, layouts and prefetch slots, to the GEMM tests' tolerances, and, where N
+is a multiple of 16, the same GEMMs with the SwiGLU store."""
 
 from __future__ import annotations
 
@@ -153,6 +154,7 @@ def test_random_grouped_gemm(seed, fp8):
         wt = dev_bf16(wb.reshape(E, N * K)).view(E, N, K)
         slots = buf.prefetch_replicas(wt, h) if c["slots"] else None
         buf.expert_gemm(dev_bf16(xb), wt, h, slots, out=y)
+        glu_call = lambda a: buf.expert_gemm(dev_bf16(xb), wt, h, slots, out=a, swiglu=True)
         torch.cuda.synchronize()
         w_all = wb
         if c["slots"]:
@@ -171,6 +173,8 @@ def test_random_grouped_gemm(seed, fp8):
             slots = buf.prefetch_replicas(wt, h)
             slot_sc = buf.prefetch_replicas(swt, h, scales=True)
         buf.expert_gemm_fp8(dev_u8(x), dev_f32(sx), wt, swt, h, slots, slot_sc, out=y)
+        glu_call = lambda a: buf.expert_gemm_fp8(dev_u8(x), dev_f32(sx), wt, swt, h, slots, slot_sc, out=a,
+                                                 swiglu=True)
         torch.cuda.synchronize()
         w_all, sw_all = w, sw
         if c["slots"]:
@@ -182,3 +186,9 @@ def test_random_grouped_gemm(seed, fp8):
     for r0, n, _ in groups:
         covered[r0:r0 + n] = True
     assert np.all(host_bits(y)[~covered] == SENT)
+    if N % 16 == 0:   # the same GEMM with the expert FFN's SwiGLU store
+        from tests.test_gpu_ffn import check_glu
+        a = torch.full((L.rows, N // 2), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        glu_call(a)
+        torch.cuda.synchronize()
+        check_glu(host_bits(a), host_bits(y), ref, groups, L.rows)
