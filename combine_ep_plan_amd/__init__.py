@@ -85,7 +85,9 @@ _T = POINTER(ep_tensor_t)
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree libep_mi355x.so, or the file EP_MI355X_LIB names (e.g. the
+    host-sanitized build of the same sources)."""
+    return os.environ.get("EP_MI355X_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load_library():

@@ -163,16 +163,19 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
 // projection), so a 16-byte vector of the staged bf16 output tile holds four
 // (gate, up) pairs, gate in the low half of each 32-bit word.  Each pair
 // becomes bf16(silu(gate) * up), silu(g) = g / (1 + e^-g) in fp32 with the
-// hardware reciprocal (about 1 ulp of fp32, far below the bf16 rounding).  Below
-// g = -87.34 the reciprocal is under the smallest normal fp32 and flushes, so
-// the result is a signed zero where the exact value is below 1.1e-36 |up|.
+// hardware reciprocal (about 1 ulp of fp32, far below the bf16 rounding).
+// That reciprocal is a normal fp32 while 1 + e^-g < 2^126; from g < -64 on
+// (1 + e^-g > 2^92, and 1 + e^g == 1 in fp32) the value is taken as
+// g * up * e^g in double instead, so tiny and subnormal results match the
+// exact value to one rounding over the whole range.
 __device__ __forceinline__ uint2 swiglu4(u32x4 v) {
   const uint32_t in[4] = {v.x, v.y, v.z, v.w};
   float o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float g = __uint_as_float(in[i] << 16), u = __uint_as_float(in[i] & 0xFFFF0000u);
-    o[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+    if (g < -64.0f) o[i] = (float)((double)g * (double)u * exp((double)g));
+    else o[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
   }
   return uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
 }
@@ -668,15 +671,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   constexpr int kLoadsB = kBN * kChunks / kGemmThreads;
   const int c_ld = tid & (kChunks - 1);
   // Buffer loads: a scalar resource over the tile's rows and one 32-bit byte
-  // offset per lane (the library takes K <= 2^24, so 128 rows of K bytes stay
-  // within the resource's 32-bit range); rows past the end read the last row.
+  // offset per lane; rows past the end read the last row.  The library takes
+  // K <= 2^24, so 128 rows of K bytes are at most 2^31: the record count is
+  // formed in unsigned 32-bit arithmetic (the descriptor's field is unsigned)
+  // and every offset stays below it.
   const u32x4 *Xt = X + (int64_t)row0 * KV;
   const u32x4 *Wt = Wm + (int64_t)n0 * KV;
   const int32_t wrows = N - n0 < kBN ? N - n0 : kBN;
+  const int32_t nrec_x = (int32_t)((uint32_t)rows * (uint32_t)K);
+  const int32_t nrec_w = (int32_t)((uint32_t)wrows * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rX =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Xt, (short)0, rows * K, kBufDword3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)Xt, (short)0, nrec_x, kBufDword3);
   const __amdgpu_buffer_rsrc_t rW =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Wt, (short)0, wrows * K, kBufDword3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)Wt, (short)0, nrec_w, kBufDword3);
   uint32_t oa[kLoads], ob[kLoadsB];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {

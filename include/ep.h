@@ -185,20 +185,30 @@ typedef struct ep_handle_view {
                               -1 if it has none (past the S-th: overflow) */
 } ep_handle_view_t;
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL).  The
+ * codes are this library's own; the pages name no error interface. */
 const char *ep_status_string(ep_status_t st);
 
-/* Validate `cfg` and create a group (host memory only).
+/* Validate `cfg` and create a group (host memory only): the long-lived
+ * object of the NCCL EP listing's Table II, made once and used by every
+ * per-pass handle (Figure 2).
  * Errors: EP_ERR_INVALID_ARG for a NULL argument or a value outside the
  * ranges above; EP_ERR_UNSUPPORTED if the planner's on-chip tables for E
  * and R would not fit. */
 ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out);
 ep_status_t ep_group_destroy(ep_group_t g);
 
-/* Bytes of device workspace a handle for `num_tokens` tokens needs. */
+/* Bytes of device workspace a handle for `num_tokens` tokens needs.  The
+ * size depends only on the group and num_tokens, so a caller sizes one fixed
+ * buffer per pass shape up front and nothing is allocated per layer (MoonEP
+ * article, paragraph 4: static shapes avoid per-layer allocation and
+ * fragmentation). */
 ep_status_t ep_handle_workspace_bytes(ep_group_t g, int32_t num_tokens, size_t *bytes);
 
-/* Rows of the receive buffer for `num_tokens` tokens (see recv_rows). */
+/* Rows of the receive buffer for `num_tokens` tokens (see recv_rows): T*k
+ * (HT), E*capacity (LL, the 3D expert-major buffer of the NCCL EP listing's
+ * Table III) or R*C (STATIC, the fixed per-rank shape of the MoonEP
+ * article, paragraphs 3-4). */
 ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
 
 /* Create a per-pass handle (NCCL EP listing, Table II: handles) over a
@@ -211,10 +221,21 @@ ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
 ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
                              size_t workspace_bytes, ep_handle_t *out);
 ep_status_t ep_handle_destroy(ep_handle_t h);
+
+/* Device pointers to every table of the handle's last plan (counts, offsets,
+ * destinations, the static plan), the routing state that the forward and
+ * the backward pass share (NCCL EP listing, Figure 5: one handle for both).
+ * Host bookkeeping only; the tables hold valid data once the stream has run
+ * the plan.  Errors: EP_ERR_INVALID_ARG for a NULL argument. */
 ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *view);
 
 /* Wait for `stream`, then return the status word's EP_FLAG_* bits in *flags.
- * The only blocking call of the library; meant for tests and error checks. */
+ * The only blocking call of the library; meant for tests and error checks.
+ * Every other call sizes and checks its work on the device, so a pass needs
+ * no per-layer host synchronisation (MoonEP article, paragraph 4); data
+ * errors are latched in the status word and read here when the caller
+ * chooses.  Errors: EP_ERR_INVALID_ARG (NULL), EP_ERR_HIP (the copy or the
+ * wait failed). */
 ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags);
 
 /* Top-k routing, the gate step before ep_plan ("Ultra-Large MoE Models"

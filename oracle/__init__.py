@@ -21,7 +21,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
-_LIB = os.path.join(_HERE, "libep_oracle.so")
+# EP_ORACLE_SANITIZE=1: build and load an AddressSanitizer +
+# UndefinedBehaviorSanitizer build instead (the sanitizer runtimes must be
+# preloaded into the interpreter)
+_SANITIZE = os.environ.get("EP_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libep_oracle_san.so" if _SANITIZE else "libep_oracle.so")
 
 FLAG_INDEX_RANGE = 1
 FLAG_CAPACITY = 2
@@ -39,6 +43,9 @@ def build(force: bool = True) -> str:
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
                "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
                "-o", tmp, _SRC, "-lm"]
+        if _SANITIZE:
+            cmd[1:1] = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                        "-fno-omit-frame-pointer", "-g"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -715,7 +715,7 @@ void orc_route(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *id
   for (t = 0; t < T; ++t) {
     const float *l = logits + t * E;
     char *taken = (char *)calloc((size_t)(E > 0 ? E : 1), 1);
-    double z[64];
+    double *z = (double *)calloc((size_t)(k > 0 ? k : 1), sizeof(double));
     int32_t n = 0;
     for (int32_t j = 0; j < k; ++j) {
       int32_t best = -1;
@@ -736,6 +736,7 @@ void orc_route(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *id
       sum += z[j];
     }
     for (int32_t j = 0; j < k; ++j) w[t * k + j] = j < n ? (float)(z[j] / sum) : 0.0f;
+    free(z);
     free(taken);
   }
 }

@@ -388,6 +388,9 @@ def test_expert_gemm_fp8_argument_validation(lib):
     KB = (1 << 24) + 128                                                      # beyond 32-bit tile offsets
     assert G(h, T(FP8, TK, 128, KB), T(F32, SC, 128, KB // 128), T(FP8, W, 8, 32, KB),
              T(F32, SC, 8, 32, KB // 128), None, None, y, None) == 7
+    KM = 1 << 24                                                              # the largest K taken:
+    assert G(h, T(FP8, TK, 128, KM), T(F32, SC, 128, KM // 128), T(FP8, W, 8, 32, KM),
+             T(F32, SC, 8, 32, KM // 128), None, None, y, None) == 5          # passes the size check
     assert G(h, x, sx, w, T(F32, SC, 7, 32, 2), None, None, y, None) == 4
     assert G(h, x, sx, T(FP8, W, 7, 32, 256), sw, None, None, y, None) == 4   # not E matrices
     assert G(h, T(FP8, TK, 127, 256), sx, w, sw, None, None, y, None) == 4    # not recv_rows

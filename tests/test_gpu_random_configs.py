@@ -124,7 +124,7 @@ def draw_gemm(seed: int) -> dict:
     S = int(rng.integers(0, 3)) if kind == "static" else 0
     mode = str(rng.choice(["training", "inference"])) if kind == "static" else "training"
     K = 128 * int(rng.integers(1, 5))
-    N = int(rng.choice([1, 8, 37, 64, 128, 200, 257]))
+    N = int(rng.choice([1, 8, 37, 64, 128, 160, 200, 257, 272, 320]))
     return dict(R=R, E=E, k=k, kind=kind, T=T, cap=cap, S=S, mode=mode, K=K, N=N,
                 skew=float(rng.choice([0.0, 1.5])), slots=bool(kind == "static" and S > 0 and rng.random() < 0.7))
 

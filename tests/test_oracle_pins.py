@@ -636,6 +636,21 @@ def test_route_matches_numpy(T, E, k, std):
     assert np.allclose(w.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
 
 
+def test_route_with_more_choices_than_64():
+    # k = 100 over E = 130: every chosen logit keeps its own softmax term (no
+    # fixed-size buffer caps k); checked against a stable numpy argsort and
+    # numpy's softmax as above
+    rng = np.random.default_rng(7)
+    lg = rng.standard_normal((3, 130)).astype(np.float32)
+    idx, w = oracle.route(lg, 100)
+    want = np.argsort(-lg, axis=1, kind="stable")[:, :100]
+    assert np.array_equal(idx, want)
+    ch = np.take_along_axis(lg, want, axis=1).astype(np.float64)
+    z = np.exp(ch - ch.max(axis=1, keepdims=True))
+    ref = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    assert np.max(np.abs(w - ref) / ref) < 2.0 ** -23
+
+
 def test_route_feeds_the_workload_inputs():
     # the routing the workloads use to draw topk_idx / topk_w is the same rule
     inp = workloads.make_inputs("training", T=512)
