@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "EpError", "LAYOUT_LL", "LAYOUT_HT", "LAYOUT_STATIC", "FLAG_INDEX_RANGE", "FLAG_CAPACITY",
-    "FLAG_SLOT_BUDGET", "Group", "Handle", "Buffer", "library_path", "load_library",
+    "FLAG_SLOT_BUDGET", "FLAG_PLAN_STALL", "Group", "Handle", "Buffer", "library_path", "load_library",
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
@@ -39,7 +39,7 @@ _LIB_NAME = "libep_mi355x.so"
 
 LAYOUT_LL, LAYOUT_HT, LAYOUT_STATIC = 0, 1, 2
 _LAYOUTS = {"ll": LAYOUT_LL, "ht": LAYOUT_HT, "static": LAYOUT_STATIC}
-FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET = 1, 2, 4
+FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET, FLAG_PLAN_STALL = 1, 2, 4, 8
 TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0, 1, 2, 3, 4
 TAG_ROUTER_LOGITS, TAG_EXPERT_WEIGHTS = 5, 6
 SLOTS_TRAINING, SLOTS_INFERENCE = 0, 1

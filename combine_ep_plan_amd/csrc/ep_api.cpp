@@ -96,6 +96,20 @@ bool is_rows(const ep_tensor_t *t, int64_t rows, int64_t last, bool allow_1d = f
 
 ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
+// Compute units of the current device: a layout of at most that many tiles
+// runs as one launch with every tile resident.  0 when there is no device (the
+// layout then takes its two-launch form); a failed query's error is cleared
+// so no later launch reports it.
+int32_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cus;
+}
+
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -113,6 +127,9 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
   char *hdr = take(kAlign);
   w.status = reinterpret_cast<uint32_t *>(hdr);
   w.ticket = reinterpret_cast<uint32_t *>(hdr ? hdr + 4 : nullptr);
+  w.stall = reinterpret_cast<uint32_t *>(hdr ? hdr + 8 : nullptr);
+  w.done = reinterpret_cast<uint32_t *>(hdr ? hdr + 12 : nullptr);
+  w.arrive = reinterpret_cast<uint64_t *>(hdr ? hdr + 16 : nullptr);
   w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
   w.offsets = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (g.E + 1)));
   w.eidx = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.n));
@@ -120,6 +137,7 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
   w.dst = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.n));
   w.tile_hist = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)g.ntiles * g.E));
   w.tile_flags = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * g.ntiles));
+  w.tagged = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * (size_t)g.ntiles * (g.E + 1)));
   w.recv_src = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.rows));
   if (g.layout == kStatic) {
     w.keep = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
@@ -214,9 +232,10 @@ ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
   if (!g || !out || !workspace) return EP_ERR_INVALID_ARG;
   if (num_tokens < 0 || num_tokens > g->cfg.max_tokens) return EP_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return EP_ERR_INVALID_ARG;
-  const epk::Geometry geo = make_geometry(g, num_tokens);
+  epk::Geometry geo = make_geometry(g, num_tokens);
   const size_t need = epk::carve_workspace(geo, nullptr, nullptr);
   if (workspace_bytes < need) return EP_ERR_WORKSPACE_TOO_SMALL;
+  geo.cus = device_cus();
   ep_handle *h = new (std::nothrow) ep_handle;
   if (!h) return EP_ERR_INVALID_ARG;
   h->g = g;
@@ -267,10 +286,21 @@ ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *v) {
 
 ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags) {
   if (!h || !flags) return EP_ERR_INVALID_ARG;
-  uint32_t v = 0;
-  hipError_t e = hipMemcpyAsync(&v, h->ws.status, sizeof v, hipMemcpyDeviceToHost, as_stream(stream));
+  // header: status word, ticket, stall mark, done mark, arrival count
+  uint32_t hdr[6] = {0, 0, 0, 0, 0, 0};
+  hipError_t e = hipMemcpyAsync(hdr, h->ws.status, sizeof hdr, hipMemcpyDeviceToHost,
+                                as_stream(stream));
   if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return EP_ERR_HIP;
+  uint32_t v = hdr[0];
+  // resident-tiles layout: the last call's epoch mark is its calls so far
+  const epk::Geometry &g = h->geo;
+  if (g.ntiles > 1 && g.ntiles <= g.cus) {
+    uint64_t arrive;
+    std::memcpy(&arrive, hdr + 4, sizeof arrive);
+    const uint32_t last = (uint32_t)(arrive / (uint64_t)g.ntiles);
+    if (last != 0 && hdr[2] == last) v |= EP_FLAG_PLAN_STALL;
+  }
   *flags = v;
   return EP_OK;
 }

@@ -20,13 +20,20 @@ constexpr int kGemmBM = 128;  // rows of the smaller grouped-GEMM tile (sizes th
 constexpr uint32_t kFlagIndexRange = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
 constexpr uint32_t kFlagSlotBudget = 4u;
+constexpr uint32_t kFlagPlanStall = 8u;
 
 enum Layout : int32_t { kLL = 0, kHT = 1, kStatic = 2 };
 
 // Device tables carved out of the caller's workspace (each 256-byte aligned).
 struct Workspace {
   uint32_t *status;      // [1]  EP_FLAG_* bits
-  uint32_t *ticket;      // [1]  blocks of the layout kernel that finished
+  uint32_t *ticket;      // [1]  blocks of the layout kernel that finished (two-launch layout)
+  // resident-tiles layout handshake (see plan.hip): words only grow or carry
+  // the epoch mark of the call that wrote them, so no call resets them
+  uint64_t *arrive;      // [1]  tiles that published their histogram, over all calls
+  uint32_t *done;        // [1]  epoch mark: tile 0's static-plan tables are out
+  uint32_t *stall;       // [1]  epoch mark of the last call in which a tile's wait ran out
+  uint64_t *tagged;      // [ntiles][E] histograms, then [ntiles] flags: (mark << 32) | value
   int32_t *counts;       // [E]
   int32_t *offsets;      // [E+1]
   int32_t *eidx;         // [n]  validated expert id of each entry (-1 = skipped)
@@ -53,6 +60,7 @@ struct Geometry {
   int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
+  int32_t cus;      // compute units of the device (0 if unknown): the most tiles one launch finishes
   int32_t nbits;    // bits of an expert id, >= 1
   int64_t n;        // T*k
   int64_t rows;     // receive rows

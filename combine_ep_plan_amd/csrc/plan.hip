@@ -11,12 +11,21 @@
 //   and a per-wave LDS counter per expert carries ranks across chunks.  A
 //   per-expert scan over the 16 waves gives ranks inside the tile and the
 //   tile histogram.  No atomics touch the ranks, so every output is
-//   deterministic.  The last workgroup to finish (ticket counter) scans the
-//   tile histograms into per-tile bases, counts and offsets, raises the
-//   flags and, for the static layout, runs the planner.  A single tile keeps
-//   its histogram in LDS, needs no handshake and also writes the
-//   destinations, so small batches take one launch.
-// k_plan_dst: one thread per entry: dst from its tile base + tile rank.
+//   deterministic.  A single tile keeps its histogram in LDS, needs no
+//   handshake and also writes the destinations.
+//   Several tiles, all resident at once (no more tiles than compute units):
+//   every tile publishes its histogram, waits until all tiles have, and
+//   then computes its own per-expert base and the totals from all the
+//   histograms, so it writes its destinations in the same launch.  Counts,
+//   offsets, flags and (static layout) the planner's tables come from
+//   tile 0; for the static layout the other tiles wait for them before
+//   placing their entries.  The wait is bounded: a tile that runs out of it
+//   raises EP_FLAG_PLAN_STALL (the layout is then incomplete) instead of
+//   hanging.
+//   More tiles than that: the last workgroup to finish (ticket counter)
+//   scans the tile histograms into per-tile bases, counts and offsets,
+//   raises the flags and runs the planner; then k_plan_dst, one thread per
+//   entry, adds the tile base to the tile rank.
 // recv_src is written for the rows that hold an entry; which rows those are
 // follows from counts (LL), load (STATIC) or offsets[E] (HT).
 #include "device.h"
@@ -76,6 +85,19 @@ __device__ __forceinline__ int32_t last_le(const int32_t *a, int32_t n, int32_t 
 // barrier on gfx950 does not wait for them, so every wave does this before
 // the barrier that precedes a release by one wave of the workgroup.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Bounded wait until the 32-bit epoch mark at p reaches mark (compared modulo
+// 2^32): agent-scope loads (they see other XCDs' stores), a short sleep
+// between them, at most about half a second.  Returns false if it ran out.
+constexpr uint32_t kSpinLimit = 1u << 21;
+__device__ bool wait_mark(uint32_t *p, uint32_t mark) {
+  for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - mark) >= 0) return true;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  return false;
+}
 
 // Receive row of an entry of expert e at position pos among e's entries.
 __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace &ws,
@@ -261,15 +283,88 @@ __host__ __device__ inline int32_t plan_region_a(int32_t E, int32_t R) {
   return waves > planner ? waves : planner;
 }
 
+// Inclusive scan over the 64 lanes of a wave in six DPP steps: shifts by 1,
+// 2, 4 and 8 lanes inside each 16-lane row (lanes without a source add 0),
+// then lane 15 of each row added to the next row and lane 31 to the upper
+// half.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_add(int32_t v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, true);
+}
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+  v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Exclusive scan of cnt[0, E) into offs[0, E] (offs[E] = total) by the whole
+// workgroup, E <= its size: a DPP scan per wave, then the wave totals.
+// Callers make cnt complete (barrier) before; the scan ends with a barrier.
+__device__ void block_exclusive_scan(const int32_t *cnt, int32_t *offs, int32_t E,
+                                     int32_t *s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t v = tid < E ? cnt[tid] : 0;
+  const int32_t incl = wave_inclusive_scan(v);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int32_t pre = 0;
+#pragma unroll
+  for (int i = 0; i < kTileWaves; ++i) pre += i < w ? s_wsum[i] : 0;   // loads issued together
+  if (tid < E) offs[tid] = pre + incl - v;
+  if (tid == E - 1) offs[E] = pre + incl;
+  __syncthreads();
+}
+
+// Resident-tiles handshake words are 64-bit: (epoch mark << 32) | value.  A
+// reader polls each word until it carries this call's mark, so publishing and
+// waiting are one round trip and no cache write-back or invalidate is needed
+// (the words are written and read at agent scope, through to the point every
+// XCD sees).
+__device__ __forceinline__ uint64_t tagged(uint32_t mark, uint32_t v) {
+  return ((uint64_t)mark << 32) | v;
+}
+
+// Loads the words p[i * stride], i < n <= 16, into v, polling until every one
+// carries `mark`; each round re-issues all stale loads together, so a round
+// costs one memory latency however many are stale.  Bounded: returns false
+// once `spins` exceeds the limit (v then holds what was last read).
+template <int N>
+__device__ __forceinline__ bool load_tagged(const uint64_t *p, int64_t stride, int n,
+                                            uint32_t mark, uint64_t (&v)[N], uint32_t &spins) {
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    v[u] = u < n ? __hip_atomic_load(p + u * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : tagged(mark, 0u);
+  for (;;) {
+    bool stale = false;
+#pragma unroll
+    for (int u = 0; u < N; ++u) stale |= (uint32_t)(v[u] >> 32) != mark;
+    if (!stale) return true;
+    if (++spins > kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if ((uint32_t)(v[u] >> 32) != mark)
+        v[u] = __hip_atomic_load(p + u * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // RG > 0: the tile first routes the tokens its entries belong to (RG lanes
 // per token, RPER logits per lane; route_impl.h), writes their ids and
 // weights and ranks them from LDS: routing and the tile histogram in one
 // launch.  RG = 0: the ids come from a.idx.
-template <int RG, int RPER>
+// RES: several tiles, all resident at once; every tile finishes its own
+// entries after reading every tile's histogram (no second launch).
+template <int RG, int RPER, bool RES>
 __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   extern __shared__ int32_t lds[];
   __shared__ uint32_t s_flags;
-  __shared__ int32_t s_last;
+  __shared__ int32_t s_last;     // two-launch form: this workgroup finishes; RES: a wait ran out
+  __shared__ uint32_t s_mark;    // RES: this call's epoch mark
   __shared__ int32_t s_tmp[kTileWaves + 2];
   const Geometry &g = a.g;
   const Workspace &ws = a.ws;
@@ -282,9 +377,30 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   int32_t *offs = cnt + E;                               // [E+1]
   int32_t *s_idx = offs + E + 1;                         // RG > 0: the tile's routed ids
 
-  for (int i = tid; i < kTileWaves * E; i += kTileThreads) wcnt[i] = 0;
-  if (tid == 0) s_flags = 0;
   const int64_t f0 = (int64_t)blockIdx.x * kTileEntries;   // the tile's first entry
+  const int64_t wbase = f0 + (int64_t)w * (64 * kTileChunks);
+  int32_t ev[kTileChunks], rr[kTileChunks];
+  if constexpr (RG == 0) {   // the id loads are in flight while LDS is set up
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c) {
+      const int64_t f = wbase + c * 64 + lane;
+      ev[c] = f < g.n ? a.idx[f] : -1;
+    }
+  }
+  // Each wave zeroes and uses only its own counters, so ranking needs no
+  // workgroup barrier first (the waves of a 1024-thread workgroup start up
+  // to a microsecond apart); routing shares its ids through LDS and does.
+  for (int i = lane; i < E; i += 64) wcnt[w * E + i] = 0;
+  __builtin_amdgcn_wave_barrier();
+  if (tid == 0) {
+    s_flags = 0;
+    s_last = 0;
+    // This call's epoch: calls so far, from the arrival count (this tile has
+    // not arrived, so at most ntiles - 1 arrivals of this call are in it).
+    if constexpr (RES)
+      s_mark = (uint32_t)(__hip_atomic_load(ws.arrive, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) / gridDim.x) + 1u;
+  }
   if constexpr (RG > 0) {
     // The tokens whose entries fall in [f0, f1); a token split between two
     // tiles is routed by both (same result), each keeping its own entries.
@@ -305,18 +421,17 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
         s_idx[f - f0] = ri;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-
-  const int64_t wbase = f0 + (int64_t)w * (64 * kTileChunks);
-  int32_t ev[kTileChunks], rr[kTileChunks];
-  uint32_t flags = 0;
+  if constexpr (RG > 0) {
 #pragma unroll
-  for (int c = 0; c < kTileChunks; ++c) {   // all loads in flight before any ranking
-    const int64_t f = wbase + c * 64 + lane;
-    if constexpr (RG > 0) ev[c] = f < g.n ? s_idx[f - f0] : -1;
-    else ev[c] = f < g.n ? a.idx[f] : -1;
+    for (int c = 0; c < kTileChunks; ++c) {
+      const int64_t f = wbase + c * 64 + lane;
+      ev[c] = f < g.n ? s_idx[f - f0] : -1;
+    }
   }
+
+  uint32_t flags = 0;
 #pragma unroll
   for (int c = 0; c < kTileChunks; ++c) {
     const int64_t f = wbase + c * 64 + lane;
@@ -325,7 +440,7 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
       const int32_t raw = ev[c];
       if (raw >= 0 && raw < E) e = raw;
       else if (raw != -1) flags |= kFlagIndexRange;
-      if (!single) ws.eidx[f] = e;
+      if (!single && !RES) ws.eidx[f] = e;
     }
     const bool valid = e >= 0;
     uint64_t peers = __ballot(valid);
@@ -345,6 +460,8 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   }
   __syncthreads();
 
+  uint32_t mark = 0;
+  if constexpr (RES) mark = s_mark;
   for (int e = tid; e < E; e += kTileThreads) {
     int32_t v[kTileWaves];
 #pragma unroll
@@ -356,6 +473,9 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
       run += v[ww];
     }
     if (single) cnt[e] = run;                              // the tile is the whole layout
+    else if (RES)   // published with this call's mark
+      __hip_atomic_store(ws.tagged + (int64_t)blockIdx.x * E + e, tagged(mark, (uint32_t)run),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else ws.tile_hist[(int64_t)blockIdx.x * E + e] = run;
   }
   if (flags) atomicOr(&s_flags, flags);
@@ -364,11 +484,58 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   for (int c = 0; c < kTileChunks; ++c) {
     if (ev[c] >= 0) {
       rr[c] += wcnt[w * E + ev[c]];
-      if (!single) ws.lrank[wbase + c * 64 + lane] = rr[c];
+      if (!single && !RES) ws.lrank[wbase + c * 64 + lane] = rr[c];
     }
   }
 
-  if (!single) {
+  if constexpr (RES) {
+    const int32_t ntiles = gridDim.x;
+    uint64_t *tflags = ws.tagged + (int64_t)ntiles * E;   // [ntiles] flags words
+    if (tid == 0) {
+      __hip_atomic_store(tflags + blockIdx.x, tagged(mark, s_flags), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(ws.arrive, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();   // the per-wave counters are read; region A takes the bases
+    // This tile's base and every expert's total from all the histograms.
+    int32_t *sbase = lds;
+    uint32_t spins = 0;
+    bool ok = true;
+    for (int e = tid; e < E; e += kTileThreads) {
+      int32_t run = 0, base = 0;
+      for (int32_t t0 = 0; t0 < ntiles; t0 += 16) {
+        uint64_t v[16];
+        const int n = ntiles - t0 < 16 ? ntiles - t0 : 16;
+        ok = load_tagged(ws.tagged + (int64_t)t0 * E + e, E, n, mark, v, spins) && ok;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (u < n) {
+            if (t0 + u == (int32_t)blockIdx.x) base = run;
+            run += (int32_t)(uint32_t)v[u];
+          }
+        }
+      }
+      cnt[e] = run;
+      sbase[e] = base;
+    }
+    if (blockIdx.x == 0) {   // every tile's flags, for the status word
+      for (int32_t t = tid; t < ntiles; t += kTileThreads) {
+        uint64_t v[1];
+        ok = load_tagged(tflags + t, 0, 1, mark, v, spins) && ok;
+        const uint32_t fl = (uint32_t)v[0];
+        if (fl) atomicOr(&s_flags, fl);
+      }
+    }
+    if (!ok) s_last = 1;
+    __syncthreads();
+    // positions inside the expert, kept in registers so region A can hold
+    // the planner's tables next
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c)
+      if (ev[c] >= 0) rr[c] += sbase[ev[c]];
+  }
+
+  if (!single && !RES) {
     // Publish this tile; the last one to arrive finishes the layout.  Every
     // wave waits for its own stores to reach L2, the barrier joins them, then
     // a single wave makes them visible to the other XCDs (agent-scope release:
@@ -415,28 +582,50 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   // end, because every barrier waits for the wave's outstanding global
   // stores as well as its loads.
   __syncthreads();
-  for (int e = tid; e < E; e += kTileThreads) offs[e] = cnt[e];
-  __syncthreads();
-  if (w == 0) {
-    const int32_t tot = wave_exclusive_scan(offs, E);
-    if (lane == 0) offs[E] = tot;
-  }
-  __syncthreads();
+  block_exclusive_scan(cnt, offs, E, s_tmp);
   const int32_t total = offs[E];
-  if (g.layout == kLL) {
-    for (int e = tid; e < E; e += kTileThreads)
-      if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
-  } else if (g.layout == kStatic) {
-    plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
+  const bool writer = !RES || blockIdx.x == 0;   // the tile that writes the shared tables
+  if (writer) {
+    if (g.layout == kLL) {
+      for (int e = tid; e < E; e += kTileThreads)
+        if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
+    } else if (g.layout == kStatic) {
+      plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kTileThreads) {
+      ws.offsets[e] = offs[e];
+      if (e < E) ws.counts[e] = cnt[e];
+    }
+    if (tid == 0) *ws.status = s_flags;
   }
-  __syncthreads();
-  for (int e = tid; e <= E; e += kTileThreads) {
-    ws.offsets[e] = offs[e];
-    if (e < E) ws.counts[e] = cnt[e];
-  }
-  if (tid == 0) *ws.status = s_flags;
 
-  if (single) {
+  if constexpr (RES) {
+    // The static layout places entries through the planner's tables: tile 0
+    // releases them (epoch mark), the other tiles wait for the mark.  A tile
+    // whose wait ran out leaves this call's mark in the stall word, which
+    // ep_handle_status reports as EP_FLAG_PLAN_STALL.
+    if (g.layout == kStatic) {
+      if (blockIdx.x == 0) {
+        wait_stores();
+        __syncthreads();
+        if (tid == 0) {
+          __threadfence();
+          __hip_atomic_store(ws.done, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        if (tid == 0) {
+          if (!wait_mark(ws.done, mark)) s_last = 1;
+          __threadfence();
+        }
+        __syncthreads();
+      }
+    }
+    if (tid == 0 && s_last)
+      __hip_atomic_store(ws.stall, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (single || RES) {
 #pragma unroll
     for (int c = 0; c < kTileChunks; ++c) {
       const int64_t f = wbase + c * 64 + lane;
@@ -475,8 +664,12 @@ size_t plan_lds_bytes(int32_t E, int32_t R) {
   return (size_t)(plan_region_a(E, R) + 2 * E + 1) * sizeof(int32_t);
 }
 
+// All tiles in one launch when they can all be resident at once: one
+// 1024-thread workgroup per compute unit at most.
+static bool resident_tiles(const Geometry &g) { return g.ntiles > 1 && g.ntiles <= g.cus; }
+
 static hipError_t launch_plan_dst(const Geometry &g, const PlanArgs &a, hipStream_t s) {
-  if (g.ntiles > 1) {
+  if (g.ntiles > 1 && !resident_tiles(g)) {
     const int64_t blocks = (g.n + 255) / 256;
     hipLaunchKernelGGL(k_plan_dst, dim3((unsigned)blocks), dim3(256), 0, s, a);
   }
@@ -498,9 +691,14 @@ hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float
   PlanArgs a{g, ws, idx, logits, idx, w};
   const size_t lds =
       plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0) + (size_t)kTileEntries * sizeof(int32_t);
-#define L(P)                                                                                    \
-  hipLaunchKernelGGL((k_plan_tiles<kFusedRouteLanes, P>), dim3(g.ntiles), dim3(kTileThreads), \
-                     lds, s, a)
+#define L2(P, RES)                                                                              \
+  hipLaunchKernelGGL((k_plan_tiles<kFusedRouteLanes, P, RES>), dim3(g.ntiles),                \
+                     dim3(kTileThreads), lds, s, a)
+#define L(P)                          \
+  do {                                \
+    if (resident_tiles(g)) L2(P, true); \
+    else L2(P, false);                \
+  } while (0)
   if (per <= 1) L(1);
   else if (per <= 2) L(2);
   else if (per <= 4) L(4);
@@ -508,6 +706,7 @@ hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float
   else if (per <= 16) L(16);
   else L(32);
 #undef L
+#undef L2
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_plan_dst(g, a, s);
@@ -517,7 +716,10 @@ hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *to
                        hipStream_t s) {
   PlanArgs a{g, ws, topk_idx, nullptr, nullptr, nullptr};
   const size_t lds = plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0);
-  hipLaunchKernelGGL((k_plan_tiles<0, 0>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
+  if (resident_tiles(g))
+    hipLaunchKernelGGL((k_plan_tiles<0, 0, true>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_plan_tiles<0, 0, false>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_plan_dst(g, a, s);

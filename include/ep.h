@@ -73,6 +73,10 @@ typedef enum ep_status {
 #define EP_FLAG_CAPACITY 2u     /* LL: an expert got more than `capacity` entries; extra dropped */
 #define EP_FLAG_SLOT_BUDGET 4u  /* STATIC, training slot mode: a rank needs more replica slots
                                    than slots_per_rank (the plan is still complete) */
+#define EP_FLAG_PLAN_STALL 8u   /* the layout's workgroups, which wait for each other, could not
+                                   all run at once within about half a second (the GPU was held
+                                   by other work): the layout of that call is incomplete and must
+                                   be planned again */
 
 /* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS,
  * EP_TAG_ROUTER_LOGITS and EP_TAG_EXPERT_WEIGHTS are this library's additions
@@ -171,7 +175,8 @@ typedef struct ep_handle_view {
                               for rows that hold one: HT rows < offsets[E], LL slots
                               < min(counts[e], capacity) of expert e, STATIC rows
                               < load[r] of rank r.  Other rows are left unchanged. */
-  uint32_t *status;        /* [1]   EP_FLAG_* bits of the last ep_plan (+ dup reduce) */
+  uint32_t *status;        /* [1]   EP_FLAG_* bits of the last ep_plan (+ dup reduce);
+                              EP_FLAG_PLAN_STALL is reported by ep_handle_status only */
   /* STATIC only (NULL otherwise): */
   int32_t *keep;           /* [E] rows of e kept on its home rank */
   int32_t *native_row;     /* [E] first row of e's kept rows inside its home rank */
@@ -213,9 +218,10 @@ ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
 
 /* Create a per-pass handle (NCCL EP listing, Table II: handles) over a
  * caller-owned device workspace of `workspace_bytes` bytes, 256-byte
- * aligned, whose first 256 bytes are zero when the handle is created (the
- * status word then holds the EP_FLAG_* bits of each call; ep_plan returns
- * its workgroup ticket to zero).  Host bookkeeping only: nothing is
+ * aligned and zero-filled when the handle is created (the status word then
+ * holds the EP_FLAG_* bits of each call; the layout's handshake words start
+ * from zero and are kept consistent by every later call, so a workspace is
+ * zeroed once, not per call).  Host bookkeeping only: nothing is
  * enqueued.  Errors: EP_ERR_INVALID_ARG (NULL, misaligned, num_tokens < 0 or
  * > max_tokens), EP_ERR_WORKSPACE_TOO_SMALL. */
 ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
@@ -286,7 +292,11 @@ ep_status_t ep_route_plan(ep_handle_t h, const ep_tensor_t *logits, ep_tensor_t 
  *         (seg_slot -1), which sets EP_FLAG_SLOT_BUDGET in the training
  *         slot mode and is the direct-read overflow in the inference mode.
  * Entries equal to -1 are skipped; other ids outside [0, E) are skipped and
- * set EP_FLAG_INDEX_RANGE.  Enqueues one kernel if T*k <= 2048, else two.
+ * set EP_FLAG_INDEX_RANGE.
+ * Enqueues one kernel while ceil(T*k / 2048) tiles fit the device's compute
+ * units (T*k <= 524288 on MI355X): the tiles wait for each other inside it,
+ * a wait bounded so that it ends with EP_FLAG_PLAN_STALL rather than hangs
+ * when other work holds the GPU; above that, two kernels.
  * Re-planning a handle invalidates the layout every earlier output used. */
 ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream);
 
