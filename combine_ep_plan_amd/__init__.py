@@ -25,7 +25,8 @@ __all__ = [
     "EpError", "LAYOUT_LL", "LAYOUT_HT", "LAYOUT_STATIC", "FLAG_INDEX_RANGE", "FLAG_CAPACITY",
     "FLAG_SLOT_BUDGET", "FLAG_PLAN_STALL", "Group", "Handle", "Buffer", "library_path", "load_library",
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
-    "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_destroy", "ep_handle_query",
+    "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_create_static", "ep_handle_destroy",
+    "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
@@ -108,6 +109,7 @@ def load_library():
         "ep_group_recv_rows": (S, [c_void_p, c_int32, POINTER(c_int64)]),
         "ep_handle_workspace_bytes": (S, [c_void_p, c_int32, POINTER(c_size_t)]),
         "ep_handle_create": (S, [c_void_p, c_int32, c_void_p, c_size_t, POINTER(c_void_p)]),
+        "ep_handle_create_static": (S, [c_void_p, c_int32, c_void_p, POINTER(c_void_p)]),
         "ep_handle_destroy": (S, [c_void_p]),
         "ep_handle_query": (S, [c_void_p, POINTER(ep_handle_view_t)]),
         "ep_handle_status": (S, [c_void_p, c_void_p, POINTER(c_uint32)]),
@@ -213,6 +215,13 @@ def ep_handle_create(g: int, num_tokens: int, workspace_ptr: int, workspace_byte
     out = c_void_p()
     _check(load_library().ep_handle_create(c_void_p(g), num_tokens, c_void_p(workspace_ptr),
                                            workspace_bytes, ctypes.byref(out)), "ep_handle_create")
+    return out.value
+
+
+def ep_handle_create_static(g: int, num_tokens: int, stream=None) -> int:
+    out = c_void_p()
+    _check(load_library().ep_handle_create_static(c_void_p(g), num_tokens, _stream(stream),
+                                                  ctypes.byref(out)), "ep_handle_create_static")
     return out.value
 
 

@@ -24,7 +24,15 @@ struct ep_handle {
   char *base;
   size_t bytes;
   bool planned;
+  bool in_scratch;  // made by ep_handle_create_static: static storage, library scratch
 };
+
+namespace {
+// The handles ep_handle_create_static returns: one per device, in static
+// storage, so making one allocates nothing on the host either.
+constexpr int kMaxScratchHandles = 64;
+ep_handle g_scratch_handles[kMaxScratchHandles];
+}  // namespace
 
 namespace {
 
@@ -243,6 +251,36 @@ ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
   h->base = static_cast<char *>(workspace);
   h->bytes = workspace_bytes;
   h->planned = false;
+  h->in_scratch = false;
+  epk::carve_workspace(geo, h->base, &h->ws);
+  *out = h;
+  return EP_OK;
+}
+
+ep_status_t ep_handle_create_static(ep_group_t g, int32_t num_tokens, void *stream,
+                                    ep_handle_t *out) {
+  if (!g || !out) return EP_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_tokens > g->cfg.max_tokens) return EP_ERR_INVALID_ARG;
+  epk::Geometry geo = make_geometry(g, num_tokens);
+  const size_t need = epk::carve_workspace(geo, nullptr, nullptr);
+  if (need > epk::kScratchBytes) return EP_ERR_WORKSPACE_TOO_SMALL;
+  int dev = 0;
+  void *base = nullptr;
+  if (epk::scratch_base(&dev, &base) != hipSuccess) {
+    (void)hipGetLastError();
+    return EP_ERR_HIP;
+  }
+  if (dev >= kMaxScratchHandles) return EP_ERR_UNSUPPORTED;
+  // the workspace contract: zero-filled when the handle is made
+  if (epk::launch_zero(base, need, as_stream(stream)) != hipSuccess) return EP_ERR_HIP;
+  geo.cus = device_cus();
+  ep_handle *h = &g_scratch_handles[dev];
+  h->g = g;
+  h->geo = geo;
+  h->base = static_cast<char *>(base);
+  h->bytes = epk::kScratchBytes;
+  h->planned = false;
+  h->in_scratch = true;
   epk::carve_workspace(geo, h->base, &h->ws);
   *out = h;
   return EP_OK;
@@ -250,6 +288,7 @@ ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
 
 ep_status_t ep_handle_destroy(ep_handle_t h) {
   if (!h) return EP_ERR_INVALID_ARG;
+  if (h->in_scratch) return EP_OK;   // static storage: nothing to free
   delete h;
   return EP_OK;
 }

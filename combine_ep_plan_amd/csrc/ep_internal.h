@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ep.h"
+
 namespace epk {
 
 // Layout tile: 16 waves x 2 chunks x 64 lanes of flat entries t*k + j.
@@ -16,6 +18,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kLdsLimit = 65536;
 constexpr int kGemmBM = 128;  // rows of the smaller grouped-GEMM tile (sizes the tile table)
+constexpr size_t kScratchBytes = EP_SCRATCH_BYTES;  // the static scratch (scratch.hip)
 
 constexpr uint32_t kFlagIndexRange = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
@@ -105,6 +108,10 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
                                    const float *sx, const uint8_t *w, const float *sw,
                                    const uint8_t *wslot, const float *swslot, int32_t K, int32_t N,
                                    uint16_t *y, bool glu, hipStream_t s);
+// static scratch (scratch.hip): device address on the current device, and a
+// zero-filling kernel
+hipError_t scratch_base(int *dev, void **base);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_dup_reduce(const uint16_t *rep, const int32_t *rep_e, int32_t n, int64_t P,
                              int32_t E_owner, float *owner, uint32_t *status, hipStream_t s);
 

@@ -226,6 +226,27 @@ ep_status_t ep_group_recv_rows(ep_group_t g, int32_t num_tokens, int64_t *rows);
  * > max_tokens), EP_ERR_WORKSPACE_TOO_SMALL. */
 ep_status_t ep_handle_create(ep_group_t g, int32_t num_tokens, void *workspace,
                              size_t workspace_bytes, ep_handle_t *out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * handle as ep_handle_create, but its workspace is the library's static
+ * device scratch of 16 MiB (EP_SCRATCH_BYTES) on the current device, held by
+ * each GPU the library runs on until the process ends, and the handle itself
+ * lives in static storage.  Enqueues one zero-filling kernel on `stream`
+ * (the workspace contract); calls on the handle must follow it on that
+ * stream or after it.  Nothing is allocated, on the device or the host.
+ * The device has ONE such handle and ONE scratch: every call returns the
+ * same handle object, re-made for the new arguments, and the scratch keeps
+ * the last call's contents, so using two of these handles on one device at
+ * once, or a handle after the next ep_handle_create_static on that device,
+ * races.  ep_handle_destroy on it does nothing.
+ * Errors: EP_ERR_INVALID_ARG (NULL, num_tokens < 0 or > max_tokens),
+ * EP_ERR_WORKSPACE_TOO_SMALL (the workspace ep_handle_workspace_bytes gives
+ * for num_tokens exceeds EP_SCRATCH_BYTES), EP_ERR_HIP (no device, or the
+ * clearing kernel failed to launch). */
+#define EP_SCRATCH_BYTES ((size_t)16 << 20)
+ep_status_t ep_handle_create_static(ep_group_t g, int32_t num_tokens, void *stream,
+                                    ep_handle_t *out);
 ep_status_t ep_handle_destroy(ep_handle_t h);
 
 /* Device pointers to every table of the handle's last plan (counts, offsets,

@@ -141,6 +141,26 @@ def test_handle_create_validation(lib):
     lib.ep_group_destroy(g)
 
 
+def test_handle_create_static_validation(lib):
+    # argument checks of the scratch-backed handle run before any device call;
+    # a batch whose workspace exceeds the 16 MiB scratch is refused
+    rc, g = create(lib)
+    h = ctypes.c_void_p()
+    f = lib.ep_handle_create_static
+    assert f(None, 64, None, ctypes.byref(h)) == 1
+    assert f(g, 64, None, None) == 1
+    assert f(g, 65, None, ctypes.byref(h)) == 1       # > max_tokens
+    assert f(g, -1, None, ctypes.byref(h)) == 1
+    lib.ep_group_destroy(g)
+    rc, g = create(lib, num_experts=1024, num_ranks=1, top_k=16, max_tokens=65536)
+    assert rc == 0
+    b = ctypes.c_size_t()
+    lib.ep_handle_workspace_bytes(g, 65536, ctypes.byref(b))
+    assert b.value > (16 << 20)
+    assert f(g, 65536, None, ctypes.byref(h)) == 6    # EP_ERR_WORKSPACE_TOO_SMALL
+    lib.ep_group_destroy(g)
+
+
 def test_handle_view_points_into_workspace(lib):
     g, h, nbytes = make_handle(lib, layout=ep.LAYOUT_STATIC, slots_per_rank=2)
     v = ep.ep_handle_view_t()
