@@ -47,6 +47,9 @@ def parse():
                         "fp8 MFMA peak)")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
+    p.add_argument("--two-call-dispatch", action="store_true",
+                   help="time ep_plan + ep_dispatch as two calls even where ep_plan_dispatch "
+                        "runs them as one launch (LL / HT with T*k <= 2048: decode, tiny)")
     p.add_argument("--fused-route", action="store_true",
                    help="start the step from router logits with routing fused into the layout "
                         "launch (ep_route_plan instead of ep_route + ep_plan)")
@@ -109,6 +112,7 @@ def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P, slot_
         P = 4096 * 1536
         b["dup_reduce"] = 2 * P * 2 + P * 4 * 2                  # 2 bf16 replicas, one fp32 owner r/w
     b["route_plan"] = b["route"] + b["plan"]
+    b["plan_dispatch"] = b["plan"] + b["dispatch"]
     b["prefetch"] = filled_slots * slot_elems * slot_elem_bytes * 2   # each filled slot: owner row read, slot written
     b["prefetch_scales"] = filled_slots * (slot_elems // 128) * 4 * 2  # FP8 weights: their fp32 scales
     return b
@@ -124,7 +128,8 @@ def source_hash(files):
 
 KERNEL_SOURCES = {"dispatch": ["dispatch.hip", "device.h"], "combine": ["combine.hip", "device.h"],
                   "combine_bwd": ["combine.hip", "device.h"], "dispatch_bwd": ["combine.hip", "device.h"],
-                  "plan": ["plan.hip"], "dup_reduce": ["dup_reduce.hip", "device.h"]}
+                  "plan": ["plan.hip"], "dup_reduce": ["dup_reduce.hip", "device.h"],
+                  "plan_dispatch": ["dispatch.hip", "device.h"]}
 
 
 def traffic_for(workload, kernel):
@@ -441,12 +446,16 @@ def main():
     if a.route or a.fused_route:   # the pass starts from router logits: plan and combine use the routed outputs
         logits = torch.from_numpy(inp.logits).to(dev)
         idx, w = torch.empty_like(idx), torch.empty_like(w)
+    # small LL / HT batches: the layout runs inside the dispatch launch (ep_plan_dispatch)
+    fused_pd = (c.layout in ("ll", "ht") and c.T * c.k <= 2048 and not a.fused_route
+                and not a.two_call_dispatch)
     if a.fused_route:
         ops.append(("route_plan", lambda: ep.ep_route_plan(h.ptr, logits, idx, w, LS["s"])))
     else:
         if a.route:
             ops.append(("route", lambda: ep.ep_route(h.ptr, logits, idx, w, LS["s"])))
-        ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, LS["s"])))
+        if not fused_pd:
+            ops.append(("plan", lambda: ep.ep_plan(h.ptr, idx, LS["s"])))
     slot_elems = a.gemm * c.H if a.gemm else PREFETCH_P
     slots = None
     if a.gemm:   # one [N, H] projection per expert, the GEMM's weights
@@ -474,7 +483,14 @@ def main():
         # the experts' bf16 outputs (identity experts: the bf16 rows) feed combine
         ep.ep_plan(h.ptr, idx, stream)
         ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, stream)
-        ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, LS["s"])))
+        if fused_pd:
+            ops.append(("plan_dispatch", lambda: ep.ep_plan_dispatch(h.ptr, idx, x, None, rq, rs, None, None,
+                                                                     LS["s"])))
+        else:
+            ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, LS["s"])))
+    elif fused_pd:
+        ops.append(("plan_dispatch", lambda: ep.ep_plan_dispatch(h.ptr, idx, x, None, recv, None, None, None,
+                                                                 LS["s"])))
     else:
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, LS["s"])))
     if a.gemm:
@@ -612,7 +628,7 @@ def main():
                                      "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     chain_bytes = sum(ab[nm] for nm, _ in ops)
     step_s = step_ms / 1000.0
-    dom = max((nm for nm in ("dispatch", "combine", "combine_bwd") if nm in per_us),
+    dom = max((nm for nm in ("dispatch", "plan_dispatch", "combine", "combine_bwd") if nm in per_us),
               key=lambda nm: per_us[nm])
     dom_gbps = ab[dom] / (per_us[dom] * 1e-6) / 1e9
     traffic = traffic_for(f"{name}{'_fp8' if a.fp8 else ''}", dom)

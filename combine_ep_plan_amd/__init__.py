@@ -27,7 +27,8 @@ __all__ = [
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_create_static", "ep_handle_destroy",
     "ep_handle_query",
-    "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_bwd",
+    "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_plan_dispatch",
+    "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
     "SLOTS_TRAINING",
@@ -117,6 +118,7 @@ def load_library():
         "ep_route_plan": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_plan": (S, [c_void_p, _T, c_void_p]),
         "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_plan_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
@@ -272,6 +274,17 @@ def ep_dispatch(h: int, tokens: torch.Tensor, topk_weights: torch.Tensor | None,
         _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
         _tensor(recv_topk_idx, TAG_TOPK_IDX), _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS),
         _stream(stream)), "ep_dispatch")
+
+
+def ep_plan_dispatch(h: int, topk_idx: torch.Tensor, tokens: torch.Tensor,
+                     topk_weights: torch.Tensor | None, recv_tokens: torch.Tensor,
+                     recv_scales: torch.Tensor | None = None, recv_topk_idx: torch.Tensor | None = None,
+                     recv_topk_weights: torch.Tensor | None = None, stream=None) -> None:
+    _check(load_library().ep_plan_dispatch(
+        c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _tensor(tokens, TAG_TOKENS),
+        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(recv_tokens, TAG_TOKENS),
+        _tensor(recv_scales, TAG_FP8_SCALES), _tensor(recv_topk_idx, TAG_TOPK_IDX),
+        _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)), "ep_plan_dispatch")
 
 
 def ep_combine(h: int, expert_out: torch.Tensor, topk_weights: torch.Tensor | None,
@@ -487,9 +500,9 @@ class Buffer:
         Returns ``recv_x, recv_i, recv_w, handle, event`` (plus the FP8 scales
         as ``recv_x = (codes, scales)`` when ``fp8``)."""
         T = x.shape[0]
-        if handle is None:
+        plan = handle is None
+        if plan:
             handle = Handle(self.group, T, x.device)
-            handle.plan(topk_idx, stream)
         rows = handle.recv_rows
         shape = self.group.recv_shape(T)
         H = self.group.hidden
@@ -501,7 +514,10 @@ class Buffer:
             recv = out if out is not None else torch.empty(shape, dtype=torch.bfloat16, device=x.device)
         ri = torch.empty(rows, dtype=torch.int32, device=x.device) if recv_meta else None
         rw = torch.empty(rows, dtype=torch.float32, device=x.device) if (recv_meta and topk_weights is not None) else None
-        ep_dispatch(handle.ptr, x, topk_weights, recv, scales, ri, rw, stream)
+        if plan:   # the layout and the dispatch together (one launch for small batches)
+            ep_plan_dispatch(handle.ptr, topk_idx, x, topk_weights, recv, scales, ri, rw, stream)
+        else:
+            ep_dispatch(handle.ptr, x, topk_weights, recv, scales, ri, rw, stream)
         ev = torch.cuda.Event()
         ev.record(torch.cuda.current_stream() if stream is None else stream)
         recv_x = (recv, scales) if fp8 else recv

@@ -396,11 +396,12 @@ ep_status_t ep_plan(ep_handle_t h, const ep_tensor_t *topk_idx, void *stream) {
   return st;
 }
 
-ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens, const ep_tensor_t *topk_weights,
-                        ep_tensor_t *recv_tokens, ep_tensor_t *recv_scales,
-                        ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
-                        void *stream) {
-  if (!h) return EP_ERR_INVALID_ARG;
+// Argument checks of a dispatch (tokens, optional weights, receive rows and
+// scales, optional per-row outputs); EP_OK when all hold.
+static ep_status_t check_dispatch(const ep_handle *h, const ep_tensor_t *tokens,
+                                  const ep_tensor_t *topk_weights, const ep_tensor_t *recv_tokens,
+                                  const ep_tensor_t *recv_scales, const ep_tensor_t *recv_topk_idx,
+                                  const ep_tensor_t *recv_topk_weights) {
   const epk::Geometry &g = h->geo;
   const int32_t H = h->g->cfg.hidden;
   ep_status_t st = check_tensor(tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
@@ -433,22 +434,69 @@ ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens, const ep_tenso
     if (!(recv_topk_weights->ndim == 1 && recv_topk_weights->sizes[0] == g.rows))
       return EP_ERR_BAD_SHAPE;
   }
-  if (!h->planned) return EP_ERR_NOT_PLANNED;
-  hipStream_t s = as_stream(stream);
+  return EP_OK;
+}
+
+// Enqueue a checked dispatch; fused: the layout of topk_idx in the same launch.
+static ep_status_t run_dispatch(ep_handle *h, const ep_tensor_t *tokens,
+                                const ep_tensor_t *topk_weights, ep_tensor_t *recv_tokens,
+                                ep_tensor_t *recv_scales, ep_tensor_t *recv_topk_idx,
+                                ep_tensor_t *recv_topk_weights, hipStream_t s,
+                                const int32_t *topk_idx, bool fused) {
+  const epk::Geometry &g = h->geo;
+  const int32_t H = h->g->cfg.hidden;
   hipError_t e;
-  if (fp8)
+  if (recv_scales)
     e = epk::launch_dispatch_fp8(g, h->ws, static_cast<const uint16_t *>(tokens->data), H,
                                  static_cast<uint8_t *>(recv_tokens->data),
-                                 static_cast<float *>(recv_scales->data), s);
+                                 static_cast<float *>(recv_scales->data), s, topk_idx, fused);
   else
     e = epk::launch_dispatch_bf16(g, h->ws, static_cast<const uint16_t *>(tokens->data), H,
-                                  static_cast<uint16_t *>(recv_tokens->data), s);
+                                  static_cast<uint16_t *>(recv_tokens->data), s, topk_idx, fused);
   if (e == hipSuccess && (recv_topk_idx || recv_topk_weights))
     e = epk::launch_recv_meta(
         g, h->ws, topk_weights ? static_cast<const float *>(topk_weights->data) : nullptr,
         recv_topk_idx ? static_cast<int32_t *>(recv_topk_idx->data) : nullptr,
         recv_topk_weights ? static_cast<float *>(recv_topk_weights->data) : nullptr, s);
   return hip_status(e);
+}
+
+ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens, const ep_tensor_t *topk_weights,
+                        ep_tensor_t *recv_tokens, ep_tensor_t *recv_scales,
+                        ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
+                        void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  ep_status_t st = check_dispatch(h, tokens, topk_weights, recv_tokens, recv_scales,
+                                  recv_topk_idx, recv_topk_weights);
+  if (st != EP_OK) return st;
+  if (!h->planned) return EP_ERR_NOT_PLANNED;
+  return run_dispatch(h, tokens, topk_weights, recv_tokens, recv_scales, recv_topk_idx,
+                      recv_topk_weights, as_stream(stream), nullptr, false);
+}
+
+ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
+                             const ep_tensor_t *tokens, const ep_tensor_t *topk_weights,
+                             ep_tensor_t *recv_tokens, ep_tensor_t *recv_scales,
+                             ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
+                             void *stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const epk::Geometry &g = h->geo;
+  ep_status_t st = check_tensor(topk_idx, EP_TAG_TOPK_IDX, EP_DTYPE_INT32);
+  if (st != EP_OK) return st;
+  if (!is_2d(topk_idx, g.T, g.k)) return EP_ERR_BAD_SHAPE;
+  st = check_dispatch(h, tokens, topk_weights, recv_tokens, recv_scales, recv_topk_idx,
+                      recv_topk_weights);
+  if (st != EP_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const int32_t *idx = static_cast<const int32_t *>(topk_idx->data);
+  const bool fused = epk::fused_layout_fits(g);
+  if (!fused) {
+    st = hip_status(epk::launch_plan(g, h->ws, idx, s));
+    if (st != EP_OK) return st;
+  }
+  h->planned = true;
+  return run_dispatch(h, tokens, topk_weights, recv_tokens, recv_scales, recv_topk_idx,
+                      recv_topk_weights, s, idx, fused);
 }
 
 ep_status_t ep_combine(ep_handle_t h, const ep_tensor_t *expert_out,

@@ -84,10 +84,15 @@ hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *to
 // launch when E allows, else routing then layout
 hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float *logits,
                              int32_t *idx, float *w, hipStream_t s);
+// dispatch; with fused (fused_layout_fits(g)) the layout of idx is placed in
+// the same launch (the tables ep_plan would write)
+bool fused_layout_fits(const Geometry &g);
 hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const uint16_t *x,
-                                int32_t H, uint16_t *recv, hipStream_t s);
+                                int32_t H, uint16_t *recv, hipStream_t s,
+                                const int32_t *idx = nullptr, bool fused = false);
 hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uint16_t *x,
-                               int32_t H, uint8_t *recv_q, float *recv_scale, hipStream_t s);
+                               int32_t H, uint8_t *recv_q, float *recv_scale, hipStream_t s,
+                               const int32_t *idx = nullptr, bool fused = false);
 hipError_t launch_recv_meta(const Geometry &g, const Workspace &ws, const float *topk_w,
                             int32_t *recv_idx, float *recv_w, hipStream_t s);
 hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t *rows,

@@ -344,6 +344,23 @@ ep_status_t ep_dispatch(ep_handle_t h, const ep_tensor_t *tokens,
                         ep_tensor_t *recv_scales, ep_tensor_t *recv_topk_idx,
                         ep_tensor_t *recv_topk_weights, void *stream);
 
+/* ep_plan followed by ep_dispatch, as one call: the same tables and rows,
+ * bit for bit.  For the low-latency regime (NCCL EP listing, abstract and
+ * Table III: LL mode for small decode batches, where latency is the figure of
+ * merit) the layout runs inside the dispatch launch when the layout is LL or
+ * HT and T*k <= 2048: every token's workgroup places its own entries by
+ * counting, over all T*k ids, the earlier entries of its expert (and, HT,
+ * the entries of lower experts), and one more workgroup writes counts,
+ * offsets and flags; one launch instead of two (plus the per-row outputs'
+ * launch when asked for).  Otherwise it enqueues ep_plan's kernels, then
+ * the dispatch.  Arguments, outputs and errors: those of ep_plan (topk_idx)
+ * and ep_dispatch (the rest); afterwards the handle is planned. */
+ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
+                             const ep_tensor_t *tokens, const ep_tensor_t *topk_weights,
+                             ep_tensor_t *recv_tokens, ep_tensor_t *recv_scales,
+                             ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
+                             void *stream);
+
 /* Gather each token's expert outputs back to its place (NCCL EP listing,
  * Table II):  out[t, :] = sum_j w[t, j] * expert_out[dst[t*k+j], :], j
  * ascending, skipped entries contribute nothing, accumulated in fp32.
