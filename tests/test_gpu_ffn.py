@@ -67,7 +67,7 @@ BF16_GLU = ["ht_small", "ll_capacity", "static_slots", "static_inference_overflo
             "wide_ht_k384_n320", "wide_ll_k128_n256", "wide_static_inference_k192_n512",
             "wide_skewed_k192_n256"]
 FP8_GLU = ["ht_small", "ht_many_empty", "ll_capacity", "static_slots", "static_inference_overflow",
-           "empty"]
+           "empty", "wide_ll", "wide_static_slots", "wide_inference_overflow"]
 
 
 @pytest.mark.parametrize("name", BF16_GLU)

@@ -136,7 +136,24 @@ CASES = [
     ("ht_n_not_multiple_of_8", 300, 8, 4, "ht", 0, 1, 0, "training", 128, 37, 1.0, 0.0, 9, False),   # per-element epilogue
     ("static_slots_n_odd", 600, 32, 4, "static", 0, 8, 4, "training", 256, 131, 1.5, 0.02, 10, True),
     ("empty", 0, 8, 2, "ht", 0, 1, 0, "training", 128, 64, 0.0, 0.0, 8, False),
+    # large groups (hundreds of rows per expert): many full row tiles per
+    # weight matrix; K of 1 to 5 scale blocks, ragged N, every layout
+    ("wide_ht", 2000, 8, 4, "ht", 0, 1, 0, "training", 384, 200, 1.0, 0.0, 11, False),
+    ("wide_static_slots", 3000, 16, 4, "static", 0, 4, 2, "training", 256, 160, 1.5, 0.0, 12, True),
+    ("wide_ll", 2000, 8, 2, "ll", 600, 1, 0, "training", 640, 128, 0.8, 0.0, 13, False),
+    ("wide_n_odd_one_block", 1500, 4, 2, "ht", 0, 1, 0, "training", 128, 131, 0.5, 0.0, 14, False),
+    ("wide_inference_overflow", 2500, 16, 8, "static", 0, 8, 1, "inference", 512, 128, 1.8, 0.0, 15, True),
 ]
+
+
+def quantised_torch(gen, shape):
+    """Gaussian values quantised as the FP8 dispatch does: e4m3 codes and one
+    fp32 scale per 128 (amax / 448)."""
+    v = torch.randn(shape, generator=gen, device="cuda").view(*shape[:-1], shape[-1] // 128, 128)
+    amax = v.abs().amax(-1)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (v / sc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).view(shape), sc.contiguous()
 
 
 def _run(c, glu=None):
@@ -193,7 +210,7 @@ def test_grouped_gemm_fp8_parity(c):
     for r0, n, _ in groups:
         covered[r0:r0 + n] = True
     assert np.all(yb[~covered] == SENTINEL)
-    check_gemm_fp8(yb, ref, *ops, groups)
+    check_gemm_fp8(yb, ref, *ops, groups, separable=L.rows > 2048)
     if c[14]:
         assert np.any(groups[:, 2] >= c[2])
 
@@ -270,17 +287,8 @@ def test_grouped_gemm_fp8_training_shapes_sampled(use_slots):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(778)
 
-    def quantised(shape):
-        # Gaussian values quantised as the FP8 dispatch does: e4m3 codes and one
-        # fp32 scale per 128 (amax / 448)
-        v = torch.randn(shape, generator=gen, device="cuda").view(*shape[:-1], shape[-1] // 128, 128)
-        amax = v.abs().amax(-1)
-        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-        q = (v / sc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-        return q.view(torch.uint8).view(shape), sc.contiguous()
-
-    x, sx = quantised((L.rows, K))
-    w, sw = quantised((c.E, N, K))
+    x, sx = quantised_torch(gen, (L.rows, K))
+    w, sw = quantised_torch(gen, (c.E, N, K))
     buf = ep.Buffer(g)
     slots = slot_sc = None
     if use_slots:
@@ -333,15 +341,8 @@ def test_grouped_gemm_fp8_prefill_shapes_sampled():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(780)
 
-    def quantised(shape):
-        v = torch.randn(shape, generator=gen, device="cuda").view(*shape[:-1], shape[-1] // 128, 128)
-        amax = v.abs().amax(-1)
-        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-        q = (v / sc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-        return q.view(torch.uint8).view(shape), sc.contiguous()
-
-    x, sx = quantised((L.rows, K))
-    w, sw = quantised((c.E, N, K))
+    x, sx = quantised_torch(gen, (L.rows, K))
+    w, sw = quantised_torch(gen, (c.E, N, K))
     y = ep.Buffer(g).expert_gemm_fp8(x.view(torch.float8_e4m3fn), sx, w.view(torch.float8_e4m3fn), sw, h)
     torch.cuda.synchronize()
     groups = oracle.expert_groups(L, "ht", c.E)
