@@ -217,8 +217,10 @@ def run_microbatches(a):
     torch.cuda.set_device(dev)
     main_stream = torch.cuda.current_stream()
     c = workloads.get_config(name, a.rho)
+    # overlapped micro-batches are passes in flight together: the library's
+    # default store rule counts their receive rows together
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S,
-                 dispatch_stores=a.dispatch_stores)
+                 dispatch_stores=a.dispatch_stores, passes_in_flight=M if a.overlap else 1)
     streams = [torch.cuda.Stream() for _ in range(M)] if a.overlap else [main_stream] * M
     mbs = []
     for i in range(M):

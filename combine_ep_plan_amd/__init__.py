@@ -70,7 +70,7 @@ class ep_group_config_t(ctypes.Structure):
     _fields_ = [("num_experts", c_int32), ("num_ranks", c_int32), ("hidden", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
                 ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32),
-                ("dispatch_stores", c_int32)]
+                ("dispatch_stores", c_int32), ("passes_in_flight", c_int32)]
 
 
 class ep_handle_view_t(ctypes.Structure):
@@ -363,12 +363,13 @@ class Group:
     def __init__(self, num_experts: int, num_ranks: int, hidden: int, top_k: int,
                  max_tokens: int, layout: str | int = "ht", capacity: int = 0,
                  slots_per_rank: int = 0, slot_mode: str | int = "training",
-                 dispatch_stores: str | int = "auto"):
+                 dispatch_stores: str | int = "auto", passes_in_flight: int = 1):
         self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
         mode = _SLOT_MODES[slot_mode] if isinstance(slot_mode, str) else int(slot_mode)
         stores = _STORES[dispatch_stores] if isinstance(dispatch_stores, str) else int(dispatch_stores)
         self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
-                                     self.layout, capacity, slots_per_rank, mode, stores)
+                                     self.layout, capacity, slots_per_rank, mode, stores,
+                                     passes_in_flight)
         self.ptr = ep_group_create(self.cfg)
 
     @property

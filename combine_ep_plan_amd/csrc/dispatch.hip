@@ -35,10 +35,11 @@ constexpr int64_t kCachedStoreBytes = (int64_t)512 << 20;  // twice the Infinity
 constexpr int64_t kCachedStoreMin = (int64_t)64 << 20;     // below: latency-bound
 
 // The size rule of the default store choice: cached between 64 MiB and
-// 512 MiB of rows written.
-static bool streaming_stores(int32_t stores, int64_t bytes) {
+// 512 MiB of rows written by one dispatch, the rows of every pass in flight
+// counted against the upper bound (they share the cache).
+static bool streaming_stores(int32_t stores, int64_t bytes, int32_t in_flight) {
   if (stores != 0) return stores == 2;
-  return bytes <= kCachedStoreMin || bytes > kCachedStoreBytes;
+  return bytes <= kCachedStoreMin || bytes * (in_flight > 1 ? in_flight : 1) > kCachedStoreBytes;
 }
 
 // Pieces per row: small batches (decode) split each row over several
@@ -385,7 +386,7 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces_to(g.T, V, &chunk, fused ? kFusedSplitTarget : kSplitTarget);
-  const bool nt = streaming_stores(g.stores, g.n * H * 2);
+  const bool nt = streaming_stores(g.stores, g.n * H * 2, g.in_flight);
   const FusedLayout fl{idx, g, ws};
   const unsigned gx = (unsigned)g.T + (fused ? 1u : 0u);
 #define L3(KK, NT, FU)                                                                 \
@@ -416,7 +417,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
   const int32_t V = H / 8;
   int32_t chunk = V;
   const int32_t pieces = row_pieces_to(g.T, V, &chunk, fused ? kFusedSplitTarget : kSplitTarget);
-  const bool nt = streaming_stores(g.stores, g.n * (H + H / 128 * 4));
+  const bool nt = streaming_stores(g.stores, g.n * (H + H / 128 * 4), g.in_flight);
   const FusedLayout fl{idx, g, ws};
   const unsigned gx = (unsigned)g.T + (fused ? 1u : 0u);
 #define L3(KK, NT, FU)                                                                 \

@@ -51,6 +51,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.S = c.slots_per_rank;
   geo.slot_mode = c.slot_mode;
   geo.stores = c.dispatch_stores;
+  geo.in_flight = c.passes_in_flight > 1 ? c.passes_in_flight : 1;
   geo.layout = c.layout;
   geo.cap = c.capacity;
   geo.n = (int64_t)T * c.top_k;
@@ -202,6 +203,7 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
     return EP_ERR_INVALID_ARG;
   if (c.dispatch_stores < EP_STORES_AUTO || c.dispatch_stores > EP_STORES_STREAMING)
     return EP_ERR_INVALID_ARG;
+  if (c.passes_in_flight < 0 || c.passes_in_flight > 64) return EP_ERR_INVALID_ARG;
   if (c.slot_mode != EP_SLOTS_TRAINING &&
       !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))
     return EP_ERR_INVALID_ARG;

@@ -61,6 +61,7 @@ struct Geometry {
   int32_t T, k, E, R, S, layout, cap;
   int32_t slot_mode;  // 0 training (overflow flags SLOT_BUDGET), 1 inference
   int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
+  int32_t in_flight;  // passes of the group at once (>= 1): the size rule counts all their rows
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
   int32_t cus;      // compute units of the device (0 if unknown): the most tiles one launch finishes

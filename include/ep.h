@@ -119,9 +119,9 @@ typedef enum ep_slot_mode {
  * 256 MB Infinity Cache for the next kernel; past about twice its size they
  * only leave write-backs for that kernel to pay, and non-temporal stores
  * win; small dispatches are latency-bound and gain nothing.  AUTO picks
- * cached stores when one dispatch writes between 64 MiB and 512 MiB of rows.
- * A caller that keeps several passes in flight at once (their rows together
- * decide) can choose instead. */
+ * cached stores when one dispatch writes between 64 MiB and 512 MiB of rows,
+ * counting the rows of every pass in flight (passes_in_flight): several
+ * passes overlapped on their own streams share the cache. */
 typedef enum ep_dispatch_stores {
   EP_STORES_AUTO = 0,
   EP_STORES_CACHED = 1,
@@ -153,6 +153,9 @@ typedef struct ep_group_config {
   int32_t slots_per_rank;  /* STATIC only: replica slots S per rank, >= 0 */
   int32_t slot_mode;       /* ep_slot_mode_t (STATIC only; 0 otherwise) */
   int32_t dispatch_stores; /* ep_dispatch_stores_t */
+  int32_t passes_in_flight; /* passes of this group the caller runs at once (e.g. micro-batches
+                               on several streams); 0 or 1 = one.  EP_STORES_AUTO weighs the
+                               receive rows of all of them against the Infinity Cache. */
 } ep_group_config_t;
 
 typedef struct ep_group *ep_group_t;

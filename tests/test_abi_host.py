@@ -55,7 +55,8 @@ def test_status_strings(lib):
 
 def cfg(**kw):
     base = dict(num_experts=8, num_ranks=4, hidden=256, top_k=2, max_tokens=64,
-                layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0, slot_mode=0, dispatch_stores=0)
+                layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0, slot_mode=0, dispatch_stores=0,
+                passes_in_flight=0)
     base.update(kw)
     return ep.ep_group_config_t(*[base[f] for f, _ in ep.ep_group_config_t._fields_])
 
@@ -71,7 +72,8 @@ def create(lib, **kw):
     dict(hidden=12), dict(hidden=0), dict(top_k=0), dict(top_k=17), dict(max_tokens=-1),
     dict(layout=7), dict(layout=ep.LAYOUT_LL, capacity=0), dict(layout=ep.LAYOUT_STATIC, slots_per_rank=-1),
     dict(layout=ep.LAYOUT_STATIC, slot_mode=2), dict(layout=ep.LAYOUT_STATIC, slot_mode=-1),
-    dict(dispatch_stores=3), dict(dispatch_stores=-1),
+    dict(dispatch_stores=3), dict(dispatch_stores=-1), dict(passes_in_flight=-1),
+    dict(passes_in_flight=65),
     dict(slot_mode=ep.SLOTS_INFERENCE),               # the inference slot mode is STATIC only
     dict(layout=ep.LAYOUT_STATIC, num_experts=1024, num_ranks=1024, slots_per_rank=1 << 22),
 ])
