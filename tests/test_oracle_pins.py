@@ -938,3 +938,26 @@ def test_gemm_then_swiglu_equals_separate_gate_and_up_projections():
     hg = bf16_bits_to_f32(_round_bf16_f64(x @ wg.T)).astype(np.float64)
     hu = bf16_bits_to_f32(_round_bf16_f64(x @ wu.T)).astype(np.float64)
     np.testing.assert_array_equal(got, _round_bf16_f64(hg * expit(hg) * hu))
+
+
+def test_swiglu_then_fp8_quantiser_composed():
+    # The all-FP8 expert FFN's activation: SwiGLU rounded to bf16, then the
+    # rows quantised as the FP8 dispatch does (amax / 448 per 128, e4m3).
+    # Checked against an independent pipeline: scipy's logistic function in
+    # double, torch's bf16 cast, amax / 448 in fp32, torch's e4m3 cast.
+    from scipy.special import expit
+    rng = np.random.default_rng(77)
+    h = (rng.standard_normal((6, 512)) * np.array([[0.1], [1.0], [4.0], [30.0], [1.0], [1.0]])).astype(np.float32)
+    h[4, :] = 0.0                                  # an all-zero activation row: scale 1, codes 0
+    hb = workloads.f32_to_bf16_bits(h)
+    act = oracle.swiglu(hb)                        # [6, 256] bf16
+    q, s = oracle.quantize_rows_fp8(act)
+    hf = bf16_bits_to_f32(hb).astype(np.float64)
+    g, u = hf[:, 0::2], hf[:, 1::2]
+    a = torch.from_numpy(g * expit(g) * u).to(torch.bfloat16).float().view(6, 2, 128)
+    amax = a.abs().amax(-1, keepdim=True)
+    sc = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
+    qt = torch.clamp(a / sc, -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(q, qt.reshape(6, 256).numpy())
+    assert np.array_equal(s, sc.reshape(6, 2).numpy())
+    assert np.all(q[4] == 0) and np.all(s[4] == 1.0)
