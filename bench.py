@@ -71,6 +71,11 @@ def parse():
     p.add_argument("--swiglu", action="store_true",
                    help="with --gemm: the FFN's first GEMM with the SwiGLU store (weight rows "
                         "interleave gate and up; output N/2 columns of silu(gate) * up)")
+    p.add_argument("--ffn", action="store_true",
+                   help="with --gemm N --swiglu: the whole expert FFN, the second GEMM [E, H, N/2] "
+                        "back to H after the activation (with --fp8 the activation quantised by "
+                        "ep_quantize_fp8 first, both GEMMs on FP8 operands); combine then gathers "
+                        "the FFN output")
     p.add_argument("--microbatches", type=int, default=1, metavar="M",
                    help="one step = M independent micro-batches of the workload (forward chain "
                         "plan -> dispatch -> combine), each with its own inputs, handle, receive "
@@ -93,6 +98,30 @@ def parse():
 
 
 PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
+
+
+def gemm_report(ab, name, us, grows, mats, N, K, n_out, fp8, epilogue):
+    """Flops, algorithmic bytes (X, every weight matrix used and Y, once each;
+    stored in ab[name]) and the roofline of one grouped GEMM launch."""
+    flops = 2.0 * grows * N * K
+    if fp8:   # codes (1 byte) plus one fp32 scale per 128 of K, for rows and weights
+        el, sc, peak = 1, 4.0 / 128, MFMA_FP8_PEAK_TFLOPS
+    else:
+        el, sc, peak = 2, 0.0, MFMA_BF16_PEAK_TFLOPS
+    ab[name] = int(grows * K * (el + sc) + mats * N * K * (el + sc) + grows * n_out * 2)
+    tflops = flops / (us * 1e-6) / 1e12
+    info = {"N": N, "K": K, "dtype": "fp8-e4m3" if fp8 else "bf16", "epilogue": epilogue,
+            "rows": grows, "weight_matrices": mats, "flops": flops,
+            "avg_us": round(us, 2), "tflops": round(tflops, 1)}
+    # the binding resource: MFMA time of the flops or HBM time of the bytes
+    if flops / (peak * 1e12) >= ab[name] / (HBM_PEAK_GBPS * 1e9):
+        info["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak,
+                            "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}
+    else:
+        gbps = ab[name] / (us * 1e-6) / 1e9
+        info["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    return info
 
 
 def algorithmic_bytes(c, fp8=False, filled_slots=0, slot_elems=PREFETCH_P, slot_elem_bytes=2):
@@ -409,6 +438,10 @@ def main():
     if a.swiglu and (not a.gemm or a.gemm % 16):
         print("bench.py: --swiglu needs --gemm N with N a multiple of 16", file=sys.stderr)
         sys.exit(2)
+    if a.ffn and (not a.swiglu or (a.fp8 and a.gemm % 256)):
+        print("bench.py: --ffn needs --gemm N --swiglu (with --fp8: N a multiple of 256, so that "
+              "the activation is whole 128-blocks)", file=sys.stderr)
+        sys.exit(2)
     if (a.prefetch or a.slots is not None or a.slot_mode != "training") and c.layout != "static":
         print("bench.py: --prefetch, --slots and --slot-mode need a STATIC workload (sweep, training)",
               file=sys.stderr)
@@ -495,6 +528,7 @@ def main():
                                                                  LS["s"])))
     else:
         ops.append(("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, LS["s"])))
+    comb_in = recv
     if a.gemm:
         gy_out = torch.empty((h.recv_rows, a.gemm // 2 if a.swiglu else a.gemm), dtype=torch.bfloat16,
                              device=dev)
@@ -507,7 +541,25 @@ def main():
             recv2d = recv.view(h.recv_rows, c.H)
             ops.append(("gemm", lambda: ep.ep_expert_gemm(h.ptr, recv2d, wts, slots, gy_out, LS["s"],
                                                           swiglu=a.swiglu)))
-    ops.append(("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, LS["s"])))
+    if a.ffn:   # down projection [E, H, I] back to H; combine gathers its output
+        I = a.gemm // 2
+        gen2 = torch.Generator(device=dev)
+        gen2.manual_seed(1000 * 5 + 11)
+        w2 = (torch.randn((c.E, c.H, I), generator=gen2, device=dev) * I ** -0.5).to(torch.bfloat16)
+        ffn_out = torch.empty((h.recv_rows, c.H), dtype=torch.bfloat16, device=dev)
+        comb_in = ffn_out.view(shape)
+        if gemm_fp8:
+            w2c, w2s = ep.Buffer.quantize_fp8(w2)
+            aq = torch.empty((h.recv_rows, I), dtype=torch.float8_e4m3fn, device=dev)
+            asc = torch.empty((h.recv_rows, I // 128), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            del w2
+            ops.append(("quantize", lambda: ep.ep_quantize_fp8(gy_out, aq, asc, LS["s"])))
+            ops.append(("gemm2", lambda: ep.ep_expert_gemm_fp8(h.ptr, aq, asc, w2c, w2s, None, None,
+                                                               ffn_out, LS["s"])))
+        else:
+            ops.append(("gemm2", lambda: ep.ep_expert_gemm(h.ptr, gy_out, w2, None, ffn_out, LS["s"])))
+    ops.append(("combine", lambda: ep.ep_combine(h.ptr, comb_in, w, y, LS["s"])))
     if train:
         ops.append(("combine_bwd", lambda: ep.ep_combine_bwd(h.ptr, gy, recv, w, gout, gw, LS["s"])))
         ops.append(("dispatch_bwd", lambda: ep.ep_combine(h.ptr, gout, None, gx, LS["s"])))
@@ -594,40 +646,26 @@ def main():
 
     filled = int((h.tables()["replica"] >= 0).sum()) if c.layout == "static" and S > 0 else 0
     ab = algorithmic_bytes(c, a.fp8, filled, slot_elems, 1 if gemm_fp8 else 2)
-    gemm_info = None
+    gemm_info = gemm2_info = None
     if a.gemm:
         tb = h.tables()
         if c.layout == "ll":
             grows = int(torch.clamp(tb["counts"], max=c.cap).sum())
         else:
             grows = int(tb["offsets"][-1])   # every routed entry is one row of some group
-        flops = 2.0 * grows * a.gemm * c.H
-        # X, every weight matrix some row uses (experts with rows, plus the
-        # prefetch slots the segments read) and Y, once each
+        # every weight matrix some row uses (experts with rows, plus the
+        # prefetch slots the segments read)
         mats = int((tb["counts"] > 0).sum()) + (filled if a.prefetch else 0)
-        if gemm_fp8:   # codes (1 byte) plus one fp32 scale per 128 of K, for rows and weights
-            el, sc = 1, 4.0 / 128
-            peak = MFMA_FP8_PEAK_TFLOPS
-        else:
-            el, sc = 2, 0.0
-            peak = MFMA_BF16_PEAK_TFLOPS
         n_out = a.gemm // 2 if a.swiglu else a.gemm
-        ab["gemm"] = int(grows * c.H * (el + sc) + mats * a.gemm * c.H * (el + sc) + grows * n_out * 2)
-        tflops = flops / (per_us["gemm"] * 1e-6) / 1e12
-        gemm_info = {"N": a.gemm, "K": c.H, "dtype": "fp8-e4m3" if gemm_fp8 else "bf16",
-                     "epilogue": "swiglu" if a.swiglu else "plain",
-                     "rows": grows, "weight_matrices": mats, "flops": flops,
-                     "avg_us": round(per_us["gemm"], 2), "tflops": round(tflops, 1)}
-        # the binding resource: MFMA time of the flops or HBM time of the bytes
-        if flops / (peak * 1e12) >= ab["gemm"] / (HBM_PEAK_GBPS * 1e9):
-            gemm_info["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
-                                     "peak": peak, "unit": "TFLOP/s",
-                                     "frac": round(tflops / peak, 4)}
-        else:
-            gbps = ab["gemm"] / (per_us["gemm"] * 1e-6) / 1e9
-            gemm_info["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),
-                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                     "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        gemm_info = gemm_report(ab, "gemm", per_us["gemm"], grows, mats, a.gemm, c.H, n_out, gemm_fp8,
+                                "swiglu" if a.swiglu else "plain")
+        if a.ffn:   # the second GEMM reads no prefetch slots
+            I = a.gemm // 2
+            mats2 = int((tb["counts"] > 0).sum())
+            gemm2_info = gemm_report(ab, "gemm2", per_us["gemm2"], grows, mats2, c.H, I, c.H, gemm_fp8,
+                                     "plain")
+            if gemm_fp8:   # bf16 activation read, codes and scales written
+                ab["quantize"] = int(h.recv_rows * I * (2 + 1) + h.recv_rows * (I // 128) * 4)
     chain_bytes = sum(ab[nm] for nm, _ in ops)
     step_s = step_ms / 1000.0
     dom = max((nm for nm in ("dispatch", "plan_dispatch", "combine", "combine_bwd") if nm in per_us),
@@ -664,6 +702,7 @@ def main():
                    "hip_graph": a.graph},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
         **({"gemm": gemm_info} if gemm_info else {}),
+        **({"gemm2": gemm2_info} if gemm2_info else {}),
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": chain_bytes,

@@ -28,7 +28,7 @@ __all__ = [
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_create_static", "ep_handle_destroy",
     "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_plan_dispatch",
-    "ep_combine", "ep_combine_bwd",
+    "ep_quantize_fp8", "ep_combine", "ep_combine_bwd",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
     "SLOTS_TRAINING",
@@ -119,6 +119,7 @@ def load_library():
         "ep_plan": (S, [c_void_p, _T, c_void_p]),
         "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_plan_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_quantize_fp8": (S, [_T, _T, _T, c_void_p]),
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
@@ -285,6 +286,12 @@ def ep_plan_dispatch(h: int, topk_idx: torch.Tensor, tokens: torch.Tensor,
         _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(recv_tokens, TAG_TOKENS),
         _tensor(recv_scales, TAG_FP8_SCALES), _tensor(recv_topk_idx, TAG_TOPK_IDX),
         _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)), "ep_plan_dispatch")
+
+
+def ep_quantize_fp8(tokens: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    _check(load_library().ep_quantize_fp8(
+        _tensor(tokens, TAG_TOKENS), _tensor(codes, TAG_TOKENS), _tensor(scales, TAG_FP8_SCALES),
+        _stream(stream)), "ep_quantize_fp8")
 
 
 def ep_combine(h: int, expert_out: torch.Tensor, topk_weights: torch.Tensor | None,
@@ -589,6 +596,20 @@ class Buffer:
                            expert_weights, expert_scales, slots, slot_scales, out, stream,
                            swiglu=swiglu)
         return out
+
+    @staticmethod
+    def quantize_fp8(x: torch.Tensor, codes: torch.Tensor | None = None,
+                     scales: torch.Tensor | None = None, stream=None):
+        """bf16 rows [..., K] (K % 128 == 0) to e4m3 codes of the same shape
+        and fp32 scales [..., K/128], bit for bit the FP8 dispatch's
+        quantisation; for the activation between the two FFN GEMMs."""
+        K = x.shape[-1]
+        if codes is None:
+            codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+        if scales is None:
+            scales = torch.empty(tuple(x.shape[:-1]) + (K // 128,), dtype=torch.float32, device=x.device)
+        ep_quantize_fp8(x, codes, scales, stream)
+        return codes, scales
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,
                         handle: Handle, replica_expert: torch.Tensor | None = None,

@@ -288,10 +288,35 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__re
   }
 }
 
-// FP8: a 128-channel block is 16 lanes x 8 channels; amax is reduced over
-// those 16 lanes.  scale = amax / 448 and x / scale are IEEE fp32 divisions,
-// the quotient is clamped to +-448 and rounded to nearest even by
-// v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950).
+// FP8 quantisation of one 16-byte vector (8 bf16 channels) whose 128-channel
+// block spans 16 consecutive lanes: amax reduced over those lanes, scale =
+// amax / 448 and x / scale IEEE fp32 divisions, the quotient clamped to +-448
+// and rounded to nearest even by v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950).
+// Returns the 8 codes; *scale gets the block's scale.
+__device__ __forceinline__ u32x2 quantize_fp8_vec(u32x4 xv, float *scale) {
+  float f[8];
+  unpack8(xv, f);
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+  float q[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(f[c] / s, -448.0f), 448.0f);
+  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
+  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+  *scale = s;
+  return u32x2{w0, w1};
+}
+
+// FP8 dispatch: each token's row quantised once (quantize_fp8_vec) and the
+// codes and scales written to its k destinations.
 template <int K, bool NT, bool FUSED>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__restrict__ x,
                                                               const int32_t *__restrict__ dst,
@@ -319,25 +344,10 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
   int32_t d[KN];
   token_dst<K, FUSED>(dst, t, k, fl, d);
   for (int32_t v = lo + threadIdx.x; v < hi; v += kRowThreads) {
-    float f[8];
-    unpack8(xv, f);
+    const u32x4 cur = xv;
     if (v + kRowThreads < hi) xv = x[t * V + v + kRowThreads];
-    float amax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
-    amax = fmaxf(amax, __shfl_xor(amax, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
-    float q[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(f[c] / s, -448.0f), 448.0f);
-    uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
-    uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
-    const u32x2 packed = {w0, w1};
+    float s;
+    const u32x2 packed = quantize_fp8_vec(cur, &s);
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
       if (K == 0 && j >= k) break;
@@ -347,6 +357,36 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
       if ((v & 15) == 0) recv_s[(int64_t)d[j] * nb + (v >> 4)] = s;
     }
   }
+}
+
+// Rows of bf16 (K % 128 == 0) to e4m3 codes and one fp32 scale per 128, the
+// FP8 dispatch's recipe (quantize_fp8_vec), for rows that do not come from
+// a dispatch -- the activation between the expert FFN's two GEMMs.  A grid
+// stride over the 16-byte vectors; 16 consecutive vectors are one block, so
+// a block's lanes are all in or all out of a pass (the stride is a multiple
+// of 16 and the vector count is too).
+__global__ __launch_bounds__(256) void k_quantize_fp8(const u32x4 *__restrict__ x,
+                                                      u32x2 *__restrict__ q,
+                                                      float *__restrict__ scales, int64_t nvec) {
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * 256) {
+    float s;
+    const u32x2 codes = quantize_fp8_vec(x[v], &s);
+    q[v] = codes;
+    if ((v & 15) == 0) scales[v >> 4] = s;
+  }
+}
+
+hipError_t launch_quantize_fp8(const uint16_t *x, int64_t rows, int32_t K, uint8_t *q,
+                               float *scales, hipStream_t s) {
+  const int64_t nvec = rows * (K / 8);
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_quantize_fp8, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), scales,
+                     nvec);
+  return hipGetLastError();
 }
 
 // Per receive row: expert id and router weight of the entry it holds (-1 / 0

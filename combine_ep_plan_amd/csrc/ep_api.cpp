@@ -501,6 +501,25 @@ ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
                       recv_topk_weights, s, idx, fused);
 }
 
+ep_status_t ep_quantize_fp8(const ep_tensor_t *tokens, ep_tensor_t *codes, ep_tensor_t *scales,
+                            void *stream) {
+  ep_status_t st = check_tensor(tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
+  if (st != EP_OK) return st;
+  st = check_tensor(codes, EP_TAG_TOKENS, EP_DTYPE_FP8_E4M3);
+  if (st != EP_OK) return st;
+  st = check_tensor(scales, EP_TAG_FP8_SCALES, EP_DTYPE_FP32);
+  if (st != EP_OK) return st;
+  if (tokens->ndim < 2) return EP_ERR_BAD_SHAPE;
+  const int64_t K = tokens->sizes[tokens->ndim - 1];
+  const int64_t rows = numel(tokens) / (K > 0 ? K : 1);
+  if (K <= 0 || K % 128 != 0 || K > INT32_MAX) return EP_ERR_BAD_SHAPE;
+  if (!is_rows(codes, rows, K) || !is_rows(scales, rows, K / 128)) return EP_ERR_BAD_SHAPE;
+  return hip_status(epk::launch_quantize_fp8(static_cast<const uint16_t *>(tokens->data), rows,
+                                             (int32_t)K, static_cast<uint8_t *>(codes->data),
+                                             static_cast<float *>(scales->data),
+                                             as_stream(stream)));
+}
+
 ep_status_t ep_combine(ep_handle_t h, const ep_tensor_t *expert_out,
                        const ep_tensor_t *topk_weights, ep_tensor_t *out_tokens, void *stream) {
   if (!h) return EP_ERR_INVALID_ARG;

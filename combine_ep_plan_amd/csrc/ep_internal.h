@@ -94,6 +94,9 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const Workspace &ws, const ui
 hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                int32_t H, uint8_t *recv_q, float *recv_scale, hipStream_t s,
                                const int32_t *idx = nullptr, bool fused = false);
+// rows x K bf16 to e4m3 codes + fp32 scales per 128 (the FP8 dispatch's recipe)
+hipError_t launch_quantize_fp8(const uint16_t *x, int64_t rows, int32_t K, uint8_t *q,
+                               float *scales, hipStream_t s);
 hipError_t launch_recv_meta(const Geometry &g, const Workspace &ws, const float *topk_w,
                             int32_t *recv_idx, float *recv_w, hipStream_t s);
 hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t *rows,

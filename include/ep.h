@@ -364,6 +364,22 @@ ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
                              ep_tensor_t *recv_topk_idx, ep_tensor_t *recv_topk_weights,
                              void *stream);
 
+/* FP8 e4m3 quantisation of bf16 rows with the FP8 dispatch's recipe (NCCL EP
+ * listing, Table IV: FP8 codes travel with one fp32 scale per 128 channels):
+ * per row and 128-wide block, scale = amax/448 (fp32 division; 1 if amax ==
+ * 0), code = e4m3(clamp(x / scale, -448, 448)), round to nearest even --
+ * bit for bit what ep_dispatch writes for the same row.  For rows that do
+ * not come from a dispatch: the activation between the expert FFN's two
+ * grouped GEMMs ("Ultra-Large MoE Models" article, section 3.1), so that the
+ * second GEMM runs on FP8 operands (ep_expert_gemm_fp8).  Needs no handle.
+ * tokens: bf16 [rows, K] (any leading shape), tag TOKENS; K % 128 == 0.
+ * codes:  e4m3, the same shape, tag TOKENS.
+ * scales: fp32 [rows, K/128] (any leading shape), tag FP8_SCALES.
+ * Errors: EP_ERR_BAD_TAG / _BAD_DTYPE / _BAD_SHAPE / _INVALID_ARG.
+ * Enqueues one kernel. */
+ep_status_t ep_quantize_fp8(const ep_tensor_t *tokens, ep_tensor_t *codes, ep_tensor_t *scales,
+                            void *stream);
+
 /* Gather each token's expert outputs back to its place (NCCL EP listing,
  * Table II):  out[t, :] = sum_j w[t, j] * expert_out[dst[t*k+j], :], j
  * ascending, skipped entries contribute nothing, accumulated in fp32.

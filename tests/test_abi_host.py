@@ -453,3 +453,25 @@ def test_binding_refuses_host_tensors():
     # reach them
     with pytest.raises(ValueError, match="on the GPU"):
         ep._tensor(torch.zeros(4, 8), ep.TAG_TOKENS)
+
+
+def test_quantize_fp8_argument_validation(lib):
+    Q = lib.ep_quantize_fp8
+    TK, SC = ep.TAG_TOKENS, ep.TAG_FP8_SCALES
+    x, q, s = T(BF16, TK, 64, 256), T(FP8, TK, 64, 256), T(F32, SC, 64, 2)
+    assert Q(None, q, s, None) == 1
+    assert Q(x, q, None, None) == 1
+    assert Q(T(F32, TK, 64, 256), q, s, None) == 3            # rows are bf16
+    assert Q(x, T(BF16, TK, 64, 256), s, None) == 3           # codes are e4m3
+    assert Q(x, q, T(F32, TK, 64, 2), None) == 2              # scales tag
+    assert Q(T(BF16, TK, 64, 192), T(FP8, TK, 64, 192), T(F32, SC, 64, 1), None) == 4   # K % 128
+    assert Q(T(BF16, TK, 256), T(FP8, TK, 256), T(F32, SC, 2), None) == 4              # 1D rows
+    assert Q(x, T(FP8, TK, 63, 256), s, None) == 4            # codes not [rows, K]
+    assert Q(x, q, T(F32, SC, 64, 3), None) == 4              # scales not [rows, K/128]
+    assert Q(x, q, T(F32, SC, 64, 2, data=FAKE + 2), None) == 1
+    assert Q(T(BF16, TK, 64, 256, data=FAKE + 8), q, s, None) == 1
+    # zero rows, also under a leading shape, pass validation and enqueue nothing
+    assert Q(T(BF16, TK, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
+             T(F32, SC, 0, 2, data=None), None) == 0
+    assert Q(T(BF16, TK, 4, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
+             T(F32, SC, 0, 2, data=None), None) == 0
