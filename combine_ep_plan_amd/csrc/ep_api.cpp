@@ -160,7 +160,7 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
     w.seg_slot = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)(g.E + g.R)));
   }
   w.gemm_tiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * 4 * (size_t)gemm_max_tiles(g)));
-  w.gemm_ntiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t)));
+  w.gemm_ntiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * 2));
   if (ws) *ws = w;
   return off;
 }

@@ -53,8 +53,9 @@ struct Workspace {
   int32_t *replica;      // [R*S]
   int32_t *seg_slot;     // [E+R] slot of each segment on its rank, -1 if none
   // grouped GEMM
-  int32_t *gemm_tiles;   // [gemm_max_tiles][4] row0, rows, weight index, 0
-  int32_t *gemm_ntiles;  // [1]
+  int32_t *gemm_tiles;   // [gemm_max_tiles][4] row0, rows, weight index, 0 (full tiles
+                         // from the front, short ones from the back)
+  int32_t *gemm_ntiles;  // [2] all tiles, full tiles
 };
 
 struct Geometry {

@@ -48,10 +48,12 @@
 //    MFMAs: the main loop is compiled once per count of live blocks and each
 //    wave runs its own copy (all copies have the same barriers).  The wide
 //    and FP8 kernels do the same.
-//    Workgroup order: workgroup b runs on XCD b % 8; each XCD takes an equal,
-//    contiguous share of the valid (row tile, column tile) pairs, column tile
-//    fastest, so the column tiles of one row tile share its X rows in that
-//    XCD's L2 and no XCD idles on the grid's unused tail.
+//    Workgroup order (balanced_tile): workgroup b runs on XCD b % 8; every
+//    XCD takes the same share of the full row tiles (MFMA-bound) and of the
+//    short ones (bound by streaming their weight slice), merged, column tile
+//    fastest, so no XCD holds only one kind: with skewed routing the hot
+//    experts' full tiles would otherwise sit on the first XCDs and the cold
+//    experts' short tiles on the last ones, which then idle.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -111,37 +113,60 @@ __device__ __forceinline__ void group_of(const TileArgs &a, int32_t q, int32_t &
   }
 }
 
-template <int TM>
+// PART: row tiles come in two kinds, full ones (more than TM/2 rows), whose
+// time is MFMA work, and short ones (a group's tail or a small group), whose
+// time is streaming their weight slice.  The table then holds the full tiles
+// in group order from the front and the short ones in group order from the
+// back (entry max_tiles - 1 - j is short tile j), so the GEMM kernel can give
+// every XCD the same share of each kind (balanced_tile).  Without PART every
+// tile counts as full: the table is in group order, and each XCD takes a
+// contiguous eighth of it.
+// ntiles[0] = all tiles, ntiles[1] = full tiles.
+template <int TM, bool PART>
 __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_tiles) {
-  __shared__ int32_t s_wave[16];
-  __shared__ int32_t s_base;
+  __shared__ int32_t s_wave[2][16];
+  __shared__ int32_t s_base[2];
   const Geometry &g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int32_t ngroups = g.layout == kStatic ? g.E + *a.ws.n_segments : g.E;
-  if (tid == 0) s_base = 0;
+  if (tid < 2) s_base[tid] = 0;
   __syncthreads();
   for (int32_t q0 = 0; q0 < ngroups; q0 += 1024) {
     const int32_t q = q0 + tid;
     int32_t row0 = 0, rows = 0, widx = 0;
     if (q < ngroups) group_of(a, q, row0, rows, widx);
     const int32_t nt = rows > 0 ? (rows + TM - 1) / TM : 0;
-    // inclusive scan of nt over the workgroup: lanes, then waves
-    int32_t x = nt;
+    const int32_t tail = rows - (nt - 1) * TM;                 // rows of the last tile
+    const int32_t nshort = PART && nt > 0 && 2 * tail <= TM ? 1 : 0;   // the last may be short
+    const int32_t nfull = nt - nshort;
+    // inclusive scans of nfull and nshort over the workgroup: lanes, then waves
+    int32_t xf = nfull, xs = nshort;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int32_t y = __shfl_up(x, d);
-      if (lane >= d) x += y;
+      const int32_t yf = __shfl_up(xf, d), ys = __shfl_up(xs, d);
+      if (lane >= d) {
+        xf += yf;
+        xs += ys;
+      }
     }
-    if (lane == 63) s_wave[w] = x;
+    if (lane == 63) {
+      s_wave[0][w] = xf;
+      s_wave[1][w] = xs;
+    }
     __syncthreads();
-    int32_t before = s_base, total = 0;
+    int32_t bf = s_base[0], bs = s_base[1], tf = 0, ts = 0;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      before += v < w ? s_wave[v] : 0;
-      total += s_wave[v];
+      bf += v < w ? s_wave[0][v] : 0;
+      bs += v < w ? s_wave[1][v] : 0;
+      tf += s_wave[0][v];
+      ts += s_wave[1][v];
     }
-    int32_t t = before + x - nt;
-    for (int32_t i = 0; i < nt && t < max_tiles; ++i, ++t) {
+    bf += xf - nfull;   // full tiles before this group's
+    bs += xs - nshort;  // short tiles before this group's
+    for (int32_t i = 0; i < nt; ++i) {
+      const int32_t t = i < nfull ? bf + i : max_tiles - 1 - bs;
+      if (t < 0 || t >= max_tiles) continue;   // not reached: the table holds every tile
       int32_t *e = a.ws.gemm_tiles + (int64_t)t * 4;
       e[0] = row0 + i * TM;
       e[1] = rows - i * TM < TM ? rows - i * TM : TM;
@@ -149,10 +174,42 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
       e[3] = 0;
     }
     __syncthreads();
-    if (tid == 0) s_base += total;
+    if (tid == 0) {
+      s_base[0] += tf;
+      s_base[1] += ts;
+    }
     __syncthreads();
   }
-  if (tid == 0) *a.ws.gemm_ntiles = s_base < max_tiles ? s_base : max_tiles;
+  if (tid == 0) {
+    const int32_t nf = s_base[0], all = s_base[0] + s_base[1];
+    a.ws.gemm_ntiles[0] = all < max_tiles ? all : max_tiles;
+    a.ws.gemm_ntiles[1] = nf < max_tiles ? nf : max_tiles;
+  }
+}
+
+// Work of workgroup blockIdx.x: its row tile (an index into the table) and
+// column tile.  Workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of
+// the full tiles and the x-th eighth of the short tiles, each in group
+// order, merged in proportion (Bresenham), every row tile with its column
+// tiles one after another.  So every XCD gets the same MFMA-bound and
+// streaming-bound work and runs both kinds side by side, and the column
+// tiles of a row tile stay on one XCD (they share X rows in its L2).  The
+// grid holds at least (max_tiles / 8 + 2) * n_col_tiles workgroups per XCD
+// (gemm_grid).
+__device__ __forceinline__ bool balanced_tile(const int32_t *__restrict__ ntiles,
+                                              int32_t max_tiles, int32_t n_col_tiles,
+                                              int32_t &tile, int32_t &col) {
+  const int32_t nf = ntiles[1], ns = ntiles[0] - nf;
+  const int32_t x = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int32_t f0 = (int32_t)((int64_t)x * nf / kXcds), f1 = (int32_t)((int64_t)(x + 1) * nf / kXcds);
+  const int32_t s0 = (int32_t)((int64_t)x * ns / kXcds), s1 = (int32_t)((int64_t)(x + 1) * ns / kXcds);
+  const int32_t b = f1 - f0, n = b + (s1 - s0);
+  const int32_t p = slot / n_col_tiles;
+  if (p >= n) return false;
+  col = slot - p * n_col_tiles;
+  const int32_t before = (int32_t)((int64_t)p * b / n), upto = (int32_t)((int64_t)(p + 1) * b / n);
+  tile = upto > before ? f0 + before : max_tiles - 1 - (s0 + p - before);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -183,20 +240,17 @@ __device__ __forceinline__ uint2 swiglu4(u32x4 v) {
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
-    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t max_tiles,
+    int32_t K, int32_t N,
     int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
   __shared__ u32x4 sa[2][kTileM * kChunks];
   static_assert(kTileM * kChunks % kGemmThreads == 0 && kBN * kChunks % kGemmThreads == 0, "loader");
   __shared__ u32x4 sb[2][kBN * kChunks];
   // XCD-aware order over the valid work only (the grid is sized for the
   // largest possible tile count)
-  const int32_t valid = *ntiles * n_col_tiles;
-  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
-  const int32_t slot = blockIdx.x / kXcds;
-  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (slot >= per_xcd || lid >= valid) return;
-  const int32_t tile = lid / n_col_tiles;
-  const int32_t n0 = (lid - tile * n_col_tiles) * kBN;
+  int32_t tile, ctile;
+  if (!balanced_tile(ntiles, max_tiles, n_col_tiles, tile, ctile)) return;
+  const int32_t n0 = ctile * kBN;
   const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
   const int64_t KV = K / 8;  // 16-byte vectors per row
   const u32x4 *Wm = widx < E ? W + (int64_t)widx * N * KV : Wslot + (int64_t)(widx - E) * N * KV;
@@ -393,18 +447,15 @@ constexpr int kBufDword3 = 0x00020000;                    // buffer resource wor
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
-    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t K, int32_t N,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, int32_t max_tiles,
+    int32_t K, int32_t N,
     int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
   // two 64-deep slabs of X and W (128 KB), then the bf16 output tile
   __shared__ u32x4 lds[2 * kSlabA2 + 2 * kSlabB2];
   u32x4 *const sa = lds, *const sb = lds + 2 * kSlabA2;
-  const int32_t valid = *ntiles * n_col_tiles;
-  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
-  const int32_t slot = blockIdx.x / kXcds;
-  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (slot >= per_xcd || lid >= valid) return;
-  const int32_t tile = lid / n_col_tiles;
-  const int32_t n0 = (lid - tile * n_col_tiles) * kBN2;
+  int32_t tile, ctile;
+  if (!balanced_tile(ntiles, max_tiles, n_col_tiles, tile, ctile)) return;
+  const int32_t n0 = ctile * kBN2;
   const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
   const int64_t KV = K / 8;  // 16-byte vectors per row
   const u32x4 *Xt = X + (int64_t)row0 * KV;
@@ -642,19 +693,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
     const u32x4 *__restrict__ X, const float *__restrict__ SX, const u32x4 *__restrict__ W,
     const float *__restrict__ SW, const u32x4 *__restrict__ Wslot,
     const float *__restrict__ SWslot, const int32_t *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, int32_t K, int32_t N, int32_t E, int32_t n_col_tiles,
+    const int32_t *__restrict__ ntiles, int32_t max_tiles, int32_t K, int32_t N, int32_t E,
+    int32_t n_col_tiles,
     uint16_t *__restrict__ Y) {
   __shared__ u32x4 sa[2][kTileM * kChunks];
   __shared__ u32x4 sb[2][kBN * kChunks];
   __shared__ __attribute__((aligned(16))) float ssc[kScaleBufs][kTileM + kBN];  // row, then column scales
   static_assert(kTileM + kBN == kGemmThreads, "one scale per thread per slab");
-  const int32_t valid = *ntiles * n_col_tiles;
-  const int32_t per_xcd = (valid + kXcds - 1) / kXcds;
-  const int32_t slot = blockIdx.x / kXcds;
-  const int32_t lid = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (slot >= per_xcd || lid >= valid) return;
-  const int32_t tile = lid / n_col_tiles;
-  const int32_t n0 = (lid - tile * n_col_tiles) * kBN;
+  int32_t tile, ctile;
+  if (!balanced_tile(ntiles, max_tiles, n_col_tiles, tile, ctile)) return;
+  const int32_t n0 = ctile * kBN;
   const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
   const int64_t KV = K / 16;        // 16-byte vectors per row
   const int32_t NB = K / kF8Block;  // scales per row
@@ -903,6 +951,13 @@ int32_t gemm_max_tiles(const Geometry &g) {
     else hipLaunchKernelGGL(KERN<false>, __VA_ARGS__);        \
   } while (0)
 
+// Workgroups of a GEMM launch: per XCD, room for an eighth of each kind of
+// row tile rounded up (at most max_tiles / 8 + 2 row tiles), times the
+// column tiles (balanced_tile).
+static unsigned gemm_grid(int32_t max_tiles, int32_t ncol) {
+  return (unsigned)((int64_t)kXcds * (max_tiles / kXcds + 2) * ncol);
+}
+
 static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
   return N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E && (int64_t)kBM2 * K * 2 <= INT32_MAX;
 }
@@ -917,24 +972,20 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
     // at most as many 256-row tiles as the table holds 128-row ones
     const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
     const int32_t max2 = (int32_t)((g.n + kBM2 - 1) / kBM2 + groups);
-    hipLaunchKernelGGL(k_gemm_tiles<kBM2>, dim3(1), dim3(1024), 0, s, ta, max2);
+    hipLaunchKernelGGL((k_gemm_tiles<kBM2, true>), dim3(1), dim3(1024), 0, s, ta, max2);
     const int32_t ncol = (N + kBN2 - 1) / kBN2;
-    int64_t blocks = (int64_t)max2 * ncol;
-    blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-    GEMM_LAUNCH(k_grouped_gemm_256, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+    GEMM_LAUNCH(k_grouped_gemm_256, dim3(gemm_grid(max2, ncol)), dim3(kGemmThreads), 0, s,
                        reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
-                       reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
-                       g.E, ncol, y);
+                       reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, max2,
+                       K, N, g.E, ncol, y);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_gemm_tiles<kTileM>, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  hipLaunchKernelGGL((k_gemm_tiles<kTileM, false>), dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
-  int64_t blocks = (int64_t)max_tiles * ncol;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the XCD remap needs a multiple of 8
-  GEMM_LAUNCH(k_grouped_gemm, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+  GEMM_LAUNCH(k_grouped_gemm, dim3(gemm_grid(max_tiles, ncol)), dim3(kGemmThreads), 0, s,
                      reinterpret_cast<const u32x4 *>(x), reinterpret_cast<const u32x4 *>(w),
-                     reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles, K, N,
-                     g.E, ncol, y);
+                     reinterpret_cast<const u32x4 *>(wslot), ws.gemm_tiles, ws.gemm_ntiles,
+                     max_tiles, K, N, g.E, ncol, y);
   return hipGetLastError();
 }
 
@@ -945,14 +996,12 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
-  hipLaunchKernelGGL(k_gemm_tiles<kTileM>, dim3(1), dim3(1024), 0, s, ta, max_tiles);
+  hipLaunchKernelGGL((k_gemm_tiles<kTileM, false>), dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
-  int64_t blocks = (int64_t)max_tiles * ncol;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-  GEMM_LAUNCH(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s,
+  GEMM_LAUNCH(k_grouped_gemm_fp8, dim3(gemm_grid(max_tiles, ncol)), dim3(kGemmThreads), 0, s,
                      reinterpret_cast<const u32x4 *>(x), sx, reinterpret_cast<const u32x4 *>(w), sw,
                      reinterpret_cast<const u32x4 *>(wslot), swslot, ws.gemm_tiles,
-                     ws.gemm_ntiles, K, N, g.E, ncol, y);
+                     ws.gemm_ntiles, max_tiles, K, N, g.E, ncol, y);
   return hipGetLastError();
 }
 
