@@ -90,6 +90,9 @@ def parse():
     p.add_argument("--cold", action="store_true",
                    help="read a 512 MB buffer before every step (Infinity Cache evicted with "
                         "clean lines); steps are then timed one by one")
+    p.add_argument("--no-prepare", action="store_true",
+                   help="marshal every call's arguments in Python each time (by default each op is "
+                        "prepared once with ep.prepare and replays its C call)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -251,6 +254,7 @@ def run_microbatches(a):
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S,
                  dispatch_stores=a.dispatch_stores, passes_in_flight=M if a.overlap else 1)
     streams = [torch.cuda.Stream() for _ in range(M)] if a.overlap else [main_stream] * M
+    fused = c.layout in ("ll", "ht") and c.T * c.k <= 2048 and not a.two_call_dispatch
     mbs = []
     for i in range(M):
         inp = workloads.make_inputs(name, i, a.rho)
@@ -269,10 +273,15 @@ def run_microbatches(a):
         st = streams[i]
 
         def ops_for(h=h, x=x, idx=idx, w=w, recv=recv, y=y, rq=rq, rs=rs, st=st):
-            disp = ((lambda: ep.ep_dispatch(h.ptr, x, None, rq, rs, None, None, st)) if a.fp8 else
-                    (lambda: ep.ep_dispatch(h.ptr, x, None, recv, None, None, None, st)))
-            return [("plan", lambda: ep.ep_plan(h.ptr, idx, st)), ("dispatch", disp),
-                    ("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, st))]
+            out, out_s = (rq, rs) if a.fp8 else (recv, None)
+            if fused:   # layout and dispatch in one launch
+                lead = [("plan_dispatch",
+                         lambda: ep.ep_plan_dispatch(h.ptr, idx, x, None, out, out_s, None, None, st))]
+            else:
+                lead = [("plan", lambda: ep.ep_plan(h.ptr, idx, st)),
+                        ("dispatch", lambda: ep.ep_dispatch(h.ptr, x, None, out, out_s, None, None, st))]
+            ops = lead + [("combine", lambda: ep.ep_combine(h.ptr, recv, w, y, st))]
+            return ops if a.no_prepare else [(nm, ep.prepare(f)) for nm, f in ops]
         mbs.append((h, ops_for()))
     n_ops = len(mbs[0][1])
     start = torch.cuda.Event()
@@ -384,7 +393,8 @@ def run_microbatches(a):
                                f"{'overlapped on ' + str(M) + ' streams' if a.overlap else 'in turn on one stream'}",
                    "T": c.T, "H": c.H, "E": c.E, "top_k": c.k, "layout": c.layout,
                    "microbatches": M, "overlap": a.overlap, "dispatch_stores": a.dispatch_stores,
-                   "step": " -> ".join(nm for nm, _ in serial) + f" (x{M})"},
+                   "step": " -> ".join(nm for nm, _ in mbs[0][1]) + f" (x{M})",
+                   "prepared_calls": not a.no_prepare},
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(chain_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": chain_bytes,
@@ -565,6 +575,11 @@ def main():
         ops.append(("dispatch_bwd", lambda: ep.ep_combine(h.ptr, gout, None, gx, LS["s"])))
         ops.append(("dup_reduce", lambda: ep.ep_dup_grad_reduce(h.ptr, rep, rep_e, owner, LS["s"])))
 
+    if not a.graph and not a.no_prepare:
+        # each op's C call marshalled once (the library still validates and
+        # launches on every call); a graph capture needs the capture stream
+        ops = [(nm, ep.prepare(f)) for nm, f in ops]
+
     def step():
         for _, f in ops:
             f()
@@ -699,7 +714,7 @@ def main():
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
                    "dispatch_stores": a.dispatch_stores,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route or a.fused_route,
-                   "hip_graph": a.graph},
+                   "hip_graph": a.graph, "prepared_calls": not a.graph and not a.no_prepare},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
         **({"gemm": gemm_info} if gemm_info else {}),
         **({"gemm2": gemm2_info} if gemm2_info else {}),
@@ -708,7 +723,8 @@ def main():
         "step_algorithmic_bytes": chain_bytes,
         "kernels_us": {k: round(v, 2) for k, v in per_us.items()},
         "kernels_gbps": {k: round(ab[k] / (per_us[k] * 1e-6) / 1e9, 1) for k in per_us if k in ab},
-        "host_wall_s": round(t_host, 3),
+        "host_wall_s": round(t_host, 6),
+        "kernels_algorithmic_bytes": {k: int(ab[k]) for k in per_us if k in ab},
         "roofline": roof,
     }
     if name == "sweep":

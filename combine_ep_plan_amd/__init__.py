@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from ctypes import POINTER, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 import torch
@@ -28,7 +29,7 @@ __all__ = [
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_create_static", "ep_handle_destroy",
     "ep_handle_query",
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_plan_dispatch",
-    "ep_quantize_fp8", "ep_combine", "ep_combine_bwd",
+    "ep_quantize_fp8", "ep_combine", "ep_combine_bwd", "prepare", "Prepared",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
     "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
     "SLOTS_TRAINING",
@@ -144,6 +145,7 @@ def _check(code: int, what: str) -> None:
 
 _VIEWS: dict = {}
 _VIEWS_MAX = 4096
+_RECORDING = threading.local()   # prepare(): the calls being recorded and what they use
 
 
 def _tensor(t: torch.Tensor | None, tag: int):
@@ -153,6 +155,9 @@ def _tensor(t: torch.Tensor | None, tag: int):
     call that repeats its tensors costs a dictionary lookup."""
     if t is None:
         return None
+    keep = getattr(_RECORDING, "keep", None)
+    if keep is not None:   # a prepared call holds on to its tensors
+        keep.append(t)
     if not t.is_cuda:
         raise ValueError("tensors passed to the library must be on the GPU")
     if not t.is_contiguous():
@@ -177,9 +182,62 @@ def _tensor(t: torch.Tensor | None, tag: int):
 def _stream(stream) -> c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
+    keep = getattr(_RECORDING, "keep", None)
+    if keep is not None:
+        keep.append(stream)
     if isinstance(stream, torch.cuda.Stream):
         return c_void_p(stream.cuda_stream)
     return c_void_p(int(stream))
+
+
+# Compute entry points only enqueue work, so a call is fully described by the
+# C function and its marshalled arguments.  prepare() records them once; its
+# result makes the same C calls again without marshalling anything in Python
+# (each call still validates its arguments in the library and enqueues its
+# kernels).  For launch-bound loops such as low-latency decode, where the
+# marshalling costs about as much host time as the launch itself.
+
+
+def _enqueue(name: str, *args) -> None:
+    fn = getattr(load_library(), name)
+    calls = getattr(_RECORDING, "calls", None)
+    if calls is not None:
+        calls.append((fn, args, name))
+        return
+    _check(fn(*args), name)
+
+
+class Prepared:
+    """Library calls with their arguments marshalled once (see prepare).  It
+    holds references to the tensors and streams the calls name; their storage
+    must not be moved (no resize or reallocation) while it is in use."""
+
+    def __init__(self, calls, keep):
+        self.calls = tuple(calls)
+        self.names = tuple(n for _, _, n in self.calls)
+        self._keep = tuple(keep)
+
+    def __call__(self) -> None:
+        for fn, args, name in self.calls:
+            code = fn(*args)
+            if code != 0:
+                raise EpError(code, name)
+
+
+def prepare(fn) -> Prepared:
+    """Runs ``fn()`` -- a function making compute calls of this module (route,
+    plan, dispatch, combine, GEMMs, ...) -- with nothing enqueued, recording
+    each C call and its marshalled arguments, and returns a Prepared object
+    that repeats them.  Object-creating and querying calls are not recorded
+    and must not be made inside ``fn``."""
+    if getattr(_RECORDING, "calls", None) is not None:
+        raise RuntimeError("prepare() does not nest")
+    _RECORDING.calls, _RECORDING.keep = [], []
+    try:
+        fn()
+        return Prepared(_RECORDING.calls, _RECORDING.keep)
+    finally:
+        _RECORDING.calls = _RECORDING.keep = None
 
 
 # ---------------------------------------------------------------------------
@@ -247,92 +305,86 @@ def ep_handle_status(h: int, stream=None) -> int:
 
 def ep_route(h: int, logits: torch.Tensor, topk_idx: torch.Tensor,
              topk_weights: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_route(c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
-                                   _tensor(topk_idx, TAG_TOPK_IDX),
-                                   _tensor(topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)),
-           "ep_route")
+    _enqueue("ep_route", c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
+             _tensor(topk_idx, TAG_TOPK_IDX), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+             _stream(stream))
 
 
 def ep_route_plan(h: int, logits: torch.Tensor, topk_idx: torch.Tensor,
                   topk_weights: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_route_plan(c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
-                                        _tensor(topk_idx, TAG_TOPK_IDX),
-                                        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)),
-           "ep_route_plan")
+    _enqueue("ep_route_plan", c_void_p(h), _tensor(logits, TAG_ROUTER_LOGITS),
+             _tensor(topk_idx, TAG_TOPK_IDX), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+             _stream(stream))
 
 
 def ep_plan(h: int, topk_idx: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_plan(c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _stream(stream)),
-           "ep_plan")
+    _enqueue("ep_plan", c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _stream(stream))
 
 
 def ep_dispatch(h: int, tokens: torch.Tensor, topk_weights: torch.Tensor | None,
                 recv_tokens: torch.Tensor, recv_scales: torch.Tensor | None = None,
                 recv_topk_idx: torch.Tensor | None = None,
                 recv_topk_weights: torch.Tensor | None = None, stream=None) -> None:
-    _check(load_library().ep_dispatch(
-        c_void_p(h), _tensor(tokens, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
-        _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
-        _tensor(recv_topk_idx, TAG_TOPK_IDX), _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS),
-        _stream(stream)), "ep_dispatch")
+    _enqueue("ep_dispatch", c_void_p(h), _tensor(tokens, TAG_TOKENS),
+             _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(recv_tokens, TAG_TOKENS),
+             _tensor(recv_scales, TAG_FP8_SCALES), _tensor(recv_topk_idx, TAG_TOPK_IDX),
+             _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream))
 
 
 def ep_plan_dispatch(h: int, topk_idx: torch.Tensor, tokens: torch.Tensor,
                      topk_weights: torch.Tensor | None, recv_tokens: torch.Tensor,
                      recv_scales: torch.Tensor | None = None, recv_topk_idx: torch.Tensor | None = None,
                      recv_topk_weights: torch.Tensor | None = None, stream=None) -> None:
-    _check(load_library().ep_plan_dispatch(
-        c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX), _tensor(tokens, TAG_TOKENS),
-        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(recv_tokens, TAG_TOKENS),
-        _tensor(recv_scales, TAG_FP8_SCALES), _tensor(recv_topk_idx, TAG_TOPK_IDX),
-        _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)), "ep_plan_dispatch")
+    _enqueue("ep_plan_dispatch", c_void_p(h), _tensor(topk_idx, TAG_TOPK_IDX),
+             _tensor(tokens, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+             _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
+             _tensor(recv_topk_idx, TAG_TOPK_IDX), _tensor(recv_topk_weights, TAG_TOPK_WEIGHTS),
+             _stream(stream))
 
 
 def ep_quantize_fp8(tokens: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_quantize_fp8(
-        _tensor(tokens, TAG_TOKENS), _tensor(codes, TAG_TOKENS), _tensor(scales, TAG_FP8_SCALES),
-        _stream(stream)), "ep_quantize_fp8")
+    _enqueue("ep_quantize_fp8", _tensor(tokens, TAG_TOKENS), _tensor(codes, TAG_TOKENS),
+             _tensor(scales, TAG_FP8_SCALES), _stream(stream))
 
 
 def ep_combine(h: int, expert_out: torch.Tensor, topk_weights: torch.Tensor | None,
                out_tokens: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_combine(
-        c_void_p(h), _tensor(expert_out, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
-        _tensor(out_tokens, TAG_TOKENS), _stream(stream)), "ep_combine")
+    _enqueue("ep_combine", c_void_p(h), _tensor(expert_out, TAG_TOKENS),
+             _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(out_tokens, TAG_TOKENS),
+             _stream(stream))
 
 
 def ep_combine_bwd(h: int, grad_tokens: torch.Tensor, expert_out: torch.Tensor,
                    topk_weights: torch.Tensor, grad_expert_out: torch.Tensor,
                    grad_topk_weights: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_combine_bwd(
-        c_void_p(h), _tensor(grad_tokens, TAG_TOKENS), _tensor(expert_out, TAG_TOKENS),
-        _tensor(topk_weights, TAG_TOPK_WEIGHTS), _tensor(grad_expert_out, TAG_TOKENS),
-        _tensor(grad_topk_weights, TAG_TOPK_WEIGHTS), _stream(stream)), "ep_combine_bwd")
+    _enqueue("ep_combine_bwd", c_void_p(h), _tensor(grad_tokens, TAG_TOKENS),
+             _tensor(expert_out, TAG_TOKENS), _tensor(topk_weights, TAG_TOPK_WEIGHTS),
+             _tensor(grad_expert_out, TAG_TOKENS), _tensor(grad_topk_weights, TAG_TOPK_WEIGHTS),
+             _stream(stream))
 
 
 def ep_dup_grad_reduce(h: int, replica_grads: torch.Tensor, replica_expert: torch.Tensor | None,
                        owner_grads: torch.Tensor, stream=None) -> None:
-    _check(load_library().ep_dup_grad_reduce(
-        c_void_p(h), _tensor(replica_grads, TAG_EXPERT_GRADS), _tensor(replica_expert, TAG_TOPK_IDX),
-        _tensor(owner_grads, TAG_EXPERT_GRADS), _stream(stream)), "ep_dup_grad_reduce")
+    _enqueue("ep_dup_grad_reduce", c_void_p(h), _tensor(replica_grads, TAG_EXPERT_GRADS),
+             _tensor(replica_expert, TAG_TOPK_IDX), _tensor(owner_grads, TAG_EXPERT_GRADS),
+             _stream(stream))
 
 
 def ep_prefetch_replicas(h: int, expert_weights: torch.Tensor, slot_weights: torch.Tensor,
                          stream=None, scales: bool = False) -> None:
     """``scales``: the tensors are the fp32 scales of FP8 weights (tag FP8_SCALES)."""
     tag = TAG_FP8_SCALES if scales else TAG_EXPERT_WEIGHTS
-    _check(load_library().ep_prefetch_replicas(
-        c_void_p(h), _tensor(expert_weights, tag), _tensor(slot_weights, tag), _stream(stream)),
-        "ep_prefetch_replicas")
+    _enqueue("ep_prefetch_replicas", c_void_p(h), _tensor(expert_weights, tag),
+             _tensor(slot_weights, tag), _stream(stream))
 
 
 def ep_expert_gemm(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
                    slot_weights: torch.Tensor | None, out: torch.Tensor, stream=None,
                    swiglu: bool = False) -> None:
     name = "ep_expert_gemm_swiglu" if swiglu else "ep_expert_gemm"
-    _check(getattr(load_library(), name)(
-        c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
-        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream)), name)
+    _enqueue(name, c_void_p(h), _tensor(recv_tokens, TAG_TOKENS),
+             _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
+             _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(out, TAG_TOKENS), _stream(stream))
 
 
 def ep_expert_gemm_swiglu(h: int, recv_tokens: torch.Tensor, expert_weights: torch.Tensor,
@@ -345,11 +397,10 @@ def ep_expert_gemm_fp8(h: int, recv_tokens: torch.Tensor, recv_scales: torch.Ten
                        slot_weights: torch.Tensor | None, slot_scales: torch.Tensor | None,
                        out: torch.Tensor, stream=None, swiglu: bool = False) -> None:
     name = "ep_expert_gemm_fp8_swiglu" if swiglu else "ep_expert_gemm_fp8"
-    _check(getattr(load_library(), name)(
-        c_void_p(h), _tensor(recv_tokens, TAG_TOKENS), _tensor(recv_scales, TAG_FP8_SCALES),
-        _tensor(expert_weights, TAG_EXPERT_WEIGHTS), _tensor(expert_scales, TAG_FP8_SCALES),
-        _tensor(slot_weights, TAG_EXPERT_WEIGHTS), _tensor(slot_scales, TAG_FP8_SCALES),
-        _tensor(out, TAG_TOKENS), _stream(stream)), name)
+    _enqueue(name, c_void_p(h), _tensor(recv_tokens, TAG_TOKENS),
+             _tensor(recv_scales, TAG_FP8_SCALES), _tensor(expert_weights, TAG_EXPERT_WEIGHTS),
+             _tensor(expert_scales, TAG_FP8_SCALES), _tensor(slot_weights, TAG_EXPERT_WEIGHTS),
+             _tensor(slot_scales, TAG_FP8_SCALES), _tensor(out, TAG_TOKENS), _stream(stream))
 
 
 def ep_expert_gemm_fp8_swiglu(h: int, recv_tokens: torch.Tensor, recv_scales: torch.Tensor,

@@ -475,3 +475,15 @@ def test_quantize_fp8_argument_validation(lib):
              T(F32, SC, 0, 2, data=None), None) == 0
     assert Q(T(BF16, TK, 4, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
              T(F32, SC, 0, 2, data=None), None) == 0
+
+
+def test_prepare_records_without_enqueueing():
+    # nothing recorded: an empty call list; prepare does not nest; the
+    # recording state is cleared even when the recorded function raises
+    p = ep.prepare(lambda: None)
+    assert p.names == () and p() is None
+    with pytest.raises(RuntimeError, match="nest"):
+        ep.prepare(lambda: ep.prepare(lambda: None))
+    with pytest.raises(ValueError, match="on the GPU"):
+        ep.prepare(lambda: ep.ep_plan(1, torch.zeros(4, 2, dtype=torch.int32)))
+    assert getattr(ep._RECORDING, "calls", None) is None
