@@ -77,7 +77,9 @@ def _L():
             "orc_dispatch": (None, [i32, i32, i32, P, P, P]),
             "orc_recv_meta": (None, [i32, i32, i64, P, P, P, P, P, P]),
             "orc_quantize_row_fp8": (None, [i32, P, P, P]),
+            "orc_quantize_row_fp8_pow2": (None, [i32, P, P, P]),
             "orc_dispatch_fp8": (None, [i32, i32, i32, P, P, P, P]),
+            "orc_dispatch_fp8_pow2": (None, [i32, i32, i32, P, P, P, P]),
             "orc_combine": (None, [i32, i32, i32, P, P, P, i32, P]),
             "orc_combine_bwd": (None, [i32, i32, i32, P, P, P, P, P, P]),
             "orc_dup_reduce": (None, [i32, i64, P, P, i32, P]),
@@ -252,23 +254,27 @@ def recv_meta(topk_idx, topk_w, dst, rows: int):
     return src, ridx, rw
 
 
-def quantize_row_fp8(x_bits: np.ndarray):
+def quantize_row_fp8(x_bits: np.ndarray, pow2: bool = False):
+    """One bf16 row to e4m3 codes and one fp32 scale per 128 channels
+    (amax / 448, or with ``pow2`` the power of two at or above it)."""
     x = _c(x_bits, np.uint16).reshape(-1)
     H = x.shape[0]
     q = np.zeros(H, np.uint8)
     s = np.zeros(max(H // 128, 1), np.float32)
-    _L().orc_quantize_row_fp8(H, _p(x), _p(q), _p(s))
+    fn = _L().orc_quantize_row_fp8_pow2 if pow2 else _L().orc_quantize_row_fp8
+    fn(H, _p(x), _p(q), _p(s))
     return q, s[: H // 128]
 
 
-def dispatch_fp8(x_bits: np.ndarray, dst: np.ndarray, rows: int):
+def dispatch_fp8(x_bits: np.ndarray, dst: np.ndarray, rows: int, pow2: bool = False):
     x = _c(x_bits, np.uint16)
     T, H = x.shape
     d = _c(dst, np.int32)
     k = d.shape[1]
     q = np.zeros((rows, H), np.uint8)
     s = np.zeros((rows, H // 128), np.float32)
-    _L().orc_dispatch_fp8(T, k, H, _p(x), _p(d), _p(q), _p(s))
+    fn = _L().orc_dispatch_fp8_pow2 if pow2 else _L().orc_dispatch_fp8
+    fn(T, k, H, _p(x), _p(d), _p(q), _p(s))
     return q, s
 
 
@@ -395,16 +401,17 @@ def swiglu(h_bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize_rows_fp8(bits: np.ndarray):
+def quantize_rows_fp8(bits: np.ndarray, pow2: bool = False):
     """Every row of a bf16 matrix (last axis a multiple of 128) quantised as
-    ep_dispatch's FP8 path does: e4m3 codes and one fp32 scale per 128."""
+    ep_dispatch's FP8 path does: e4m3 codes and one fp32 scale per 128
+    (``pow2``: power-of-two scales)."""
     b = _c(bits, np.uint16)
     H = b.shape[-1]
     flat = b.reshape(-1, H)
     q = np.zeros(flat.shape, np.uint8)
     s = np.zeros((flat.shape[0], H // 128), np.float32)
     for r in range(flat.shape[0]):
-        q[r], s[r] = quantize_row_fp8(flat[r])
+        q[r], s[r] = quantize_row_fp8(flat[r], pow2)
     return q.reshape(b.shape), s.reshape(b.shape[:-1] + (H // 128,))
 
 

@@ -45,6 +45,7 @@
  * that the planner's *rule* is a reading (the pages give its contract, not
  * its algorithm); its outputs are pinned by invariants and hand-worked cases.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -486,15 +487,30 @@ void orc_recv_meta(int32_t T, int32_t k, int64_t rows, const int32_t *idx,
  *   amax = max |x| over the block (exact),  s = amax / 448 in fp32 (1 if 0),
  *   q    = E4M3(clamp(x / s, -448, 448)),   x / s an fp32 division.
  * The dequantised value is q * s.
+ *
+ * Power-of-two scales (READING, a second format a group can choose; the
+ * pages fix none): s is the smallest power of two not below the fp32
+ * quotient amax / 448, and not below 2^-126, the smallest normal fp32, so
+ * that its exponent is a valid 8-bit block exponent; 1 if amax is 0.  The
+ * codes are decided as above; x / s is then a power-of-two division.
  */
-void orc_quantize_row_fp8(int32_t H, const uint16_t *x, uint8_t *q, float *scale) {
+static float pow2_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float t = amax / 448.0f;
+  int e;
+  float m = frexpf(t, &e); /* t = m * 2^e, 0.5 <= m < 1 */
+  float s = (m == 0.5f) ? t : ldexpf(1.0f, e);
+  return s < FLT_MIN ? FLT_MIN : s;
+}
+
+static void quantize_row(int32_t H, const uint16_t *x, uint8_t *q, float *scale, int pow2) {
   for (int32_t b = 0; b < H / 128; ++b) {
     float amax = 0.0f;
     for (int32_t c = 0; c < 128; ++c) {
       float v = (float)fabs(orc_bf16_to_double(x[b * 128 + c]));
       if (v > amax) amax = v;
     }
-    float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    float s = pow2 ? pow2_scale(amax) : (amax == 0.0f) ? 1.0f : amax / 448.0f;
     scale[b] = s;
     for (int32_t c = 0; c < 128; ++c) {
       float v = (float)orc_bf16_to_double(x[b * 128 + c]) / s;
@@ -505,15 +521,23 @@ void orc_quantize_row_fp8(int32_t H, const uint16_t *x, uint8_t *q, float *scale
   }
 }
 
-void orc_dispatch_fp8(int32_t T, int32_t k, int32_t H, const uint16_t *x,
-                      const int32_t *dst, uint8_t *recv_q, float *recv_scale) {
+void orc_quantize_row_fp8(int32_t H, const uint16_t *x, uint8_t *q, float *scale) {
+  quantize_row(H, x, q, scale, 0);
+}
+
+void orc_quantize_row_fp8_pow2(int32_t H, const uint16_t *x, uint8_t *q, float *scale) {
+  quantize_row(H, x, q, scale, 1);
+}
+
+static void dispatch_fp8(int32_t T, int32_t k, int32_t H, const uint16_t *x, const int32_t *dst,
+                         uint8_t *recv_q, float *recv_scale, int pow2) {
   int32_t nb = H / 128;
   int64_t t;
 #pragma omp parallel for schedule(static)
   for (t = 0; t < T; ++t) {
     uint8_t *q = (uint8_t *)malloc((size_t)H);
     float *s = (float *)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1));
-    orc_quantize_row_fp8(H, x + (int64_t)t * H, q, s);
+    quantize_row(H, x + (int64_t)t * H, q, s, pow2);
     for (int32_t j = 0; j < k; ++j) {
       int32_t d = dst[t * k + j];
       if (d < 0) continue;
@@ -523,6 +547,16 @@ void orc_dispatch_fp8(int32_t T, int32_t k, int32_t H, const uint16_t *x,
     free(q);
     free(s);
   }
+}
+
+void orc_dispatch_fp8(int32_t T, int32_t k, int32_t H, const uint16_t *x,
+                      const int32_t *dst, uint8_t *recv_q, float *recv_scale) {
+  dispatch_fp8(T, k, H, x, dst, recv_q, recv_scale, 0);
+}
+
+void orc_dispatch_fp8_pow2(int32_t T, int32_t k, int32_t H, const uint16_t *x,
+                           const int32_t *dst, uint8_t *recv_q, float *recv_scale) {
+  dispatch_fp8(T, k, H, x, dst, recv_q, recv_scale, 1);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -961,3 +961,54 @@ def test_swiglu_then_fp8_quantiser_composed():
     assert np.array_equal(q, qt.reshape(6, 256).numpy())
     assert np.array_equal(s, sc.reshape(6, 2).numpy())
     assert np.all(q[4] == 0) and np.all(s[4] == 1.0)
+
+
+def test_fp8_pow2_quantiser_scales_and_codes():
+    # Power-of-two scales: every scale is an exact power of two, the smallest
+    # one at or above the fp32 quotient amax / 448 (one half of it is below),
+    # never below 2^-126 and 1 for an all-zero block; the codes are torch's
+    # e4m3 cast of x / s (a power-of-two division, exact in double); the
+    # dequantised values are within half an e4m3 step of x.
+    rng = np.random.default_rng(91)
+    mags = np.array([[0.0], [1e-40], [3e-39], [1e-3], [1.0], [3.0], [300.0], [1e36]])
+    v = rng.standard_normal((8, 384)) * mags
+    v[:, 7] = mags[:, 0] * 448.0 * 2.0 ** -3     # some blocks with amax/448 a power of two
+    x = workloads.f32_to_bf16_bits(v.astype(np.float32))
+    q, s = oracle.quantize_rows_fp8(x, pow2=True)
+    xf = bf16_bits_to_f32(x).astype(np.float64).reshape(8, 3, 128)
+    amax = np.abs(xf).max(axis=-1)
+    t = (amax.astype(np.float32) / np.float32(448.0)).astype(np.float64)
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)                                      # powers of two
+    zero = amax == 0
+    assert np.all(s[zero] == 1.0)
+    nz = ~zero
+    assert np.all(s[nz] >= np.maximum(t[nz], 2.0 ** -126))
+    assert np.all((s[nz] / 2 < t[nz]) | (s[nz] == np.float32(2.0 ** -126)))
+    want = torch.from_numpy(np.clip(xf / s[..., None].astype(np.float64), -448, 448)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(8, 384)
+    assert np.array_equal(q, want)
+    deq = torch.from_numpy(q.reshape(8, 3, 128)).view(torch.float8_e4m3fn).double().numpy() * s[..., None]
+    # e4m3: 3 mantissa bits, subnormal step 2^-9 (in units of the scale)
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(xf / s[..., None]), 2.0 ** -6))) - 3),
+                      2.0 ** -9) * s[..., None]
+    assert np.all(np.abs(deq - xf) <= step / 2 * (1 + 1e-12))
+    # where amax / 448 is already a power of two (at or above 2^-126) the two
+    # formats agree code for code
+    q0, s0 = oracle.quantize_rows_fp8(x)
+    same = (s0 == s)
+    assert same.any()
+    assert np.array_equal(q.reshape(8, 3, 128)[same], q0.reshape(8, 3, 128)[same])
+
+
+def test_fp8_pow2_dispatch_is_the_row_quantiser():
+    T, E, k, H = 40, 8, 3, 256
+    idx, _, x = workloads.random_case(92, T, H, E, k, mask_frac=0.1)
+    L = oracle.layout(idx, E, "ht")
+    q, s = oracle.dispatch_fp8(x, L.dst, L.rows, pow2=True)
+    rq, rs = oracle.quantize_rows_fp8(x, pow2=True)
+    for t in range(T):
+        for j in range(k):
+            d = L.dst[t, j]
+            if d >= 0:
+                assert np.array_equal(q[d], rq[t]) and np.array_equal(s[d], rs[t])
