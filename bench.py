@@ -45,6 +45,10 @@ def parse():
                    help="FP8 e4m3 dispatch (one fp32 scale per 128 channels); with --gemm the "
                         "grouped GEMM takes the FP8 rows and FP8 weights (roofline against the "
                         "fp8 MFMA peak)")
+    p.add_argument("--fp8-scales", choices=("amax", "pow2"), default="amax",
+                   help="format of the FP8 scales (the group's fp8_scales): amax/448, or the power "
+                        "of two at or above it (then the FP8 GEMM of large groups runs on the "
+                        "256 x 256 kernel with the scales applied by the matrix cores)")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
     p.add_argument("--two-call-dispatch", action="store_true",
@@ -457,7 +461,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=S,
-                 slot_mode=a.slot_mode, dispatch_stores=a.dispatch_stores)
+                 slot_mode=a.slot_mode, dispatch_stores=a.dispatch_stores, fp8_scales=a.fp8_scales)
     h = ep.Handle(g, c.T)
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(inp.topk_idx).to(dev)
@@ -510,12 +514,10 @@ def main():
     elif a.prefetch:
         wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
     gemm_fp8 = bool(a.gemm and a.fp8)
-    if gemm_fp8:   # the weights quantised like the rows: e4m3 codes, one scale per 128 of K
-        wf = wts.float().view(c.E, a.gemm, c.H // 128, 128)
-        amax = wf.abs().amax(-1)
-        wsc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).contiguous()
-        wts = (wf / wsc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(c.E, a.gemm, c.H)
-        del wf, amax
+    pow2 = a.fp8_scales == "pow2"
+    if gemm_fp8:   # the weights quantised like the rows (the library's quantiser, the group's format)
+        wts, wsc = ep.Buffer.quantize_fp8(wts, pow2=pow2)
+        torch.cuda.synchronize()
     if a.prefetch:
         slots = torch.empty((c.R, S) + tuple(wts.shape[1:]), dtype=wts.dtype, device=dev)
         ops.append(("prefetch", lambda: ep.ep_prefetch_replicas(h.ptr, wts, slots, LS["s"])))
@@ -559,12 +561,12 @@ def main():
         ffn_out = torch.empty((h.recv_rows, c.H), dtype=torch.bfloat16, device=dev)
         comb_in = ffn_out.view(shape)
         if gemm_fp8:
-            w2c, w2s = ep.Buffer.quantize_fp8(w2)
+            w2c, w2s = ep.Buffer.quantize_fp8(w2, pow2=pow2)
             aq = torch.empty((h.recv_rows, I), dtype=torch.float8_e4m3fn, device=dev)
             asc = torch.empty((h.recv_rows, I // 128), dtype=torch.float32, device=dev)
             torch.cuda.synchronize()
             del w2
-            ops.append(("quantize", lambda: ep.ep_quantize_fp8(gy_out, aq, asc, LS["s"])))
+            ops.append(("quantize", lambda: ep.ep_quantize_fp8(gy_out, aq, asc, LS["s"], pow2=pow2)))
             ops.append(("gemm2", lambda: ep.ep_expert_gemm_fp8(h.ptr, aq, asc, w2c, w2s, None, None,
                                                                ffn_out, LS["s"])))
         else:
@@ -714,7 +716,8 @@ def main():
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
                    "dispatch_stores": a.dispatch_stores,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route or a.fused_route,
-                   "hip_graph": a.graph, "prepared_calls": not a.graph and not a.no_prepare},
+                   "hip_graph": a.graph, "prepared_calls": not a.graph and not a.no_prepare,
+                   "fp8_scales": a.fp8_scales if a.fp8 else None},
         **({"prefetch": {"filled_slots": filled, "slot_bytes": slot_elems * 2}} if a.prefetch else {}),
         **({"gemm": gemm_info} if gemm_info else {}),
         **({"gemm2": gemm2_info} if gemm2_info else {}),

@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "EpError", "LAYOUT_LL", "LAYOUT_HT", "LAYOUT_STATIC", "FLAG_INDEX_RANGE", "FLAG_CAPACITY",
-    "FLAG_SLOT_BUDGET", "FLAG_PLAN_STALL", "Group", "Handle", "Buffer", "library_path", "load_library",
+    "FLAG_SLOT_BUDGET", "FLAG_PLAN_STALL", "FLAG_SCALE_FORMAT", "Group", "Handle", "Buffer", "library_path", "load_library",
     "ep_status_string", "ep_group_create", "ep_group_destroy", "ep_group_recv_rows",
     "ep_handle_workspace_bytes", "ep_handle_create", "ep_handle_create_static", "ep_handle_destroy",
     "ep_handle_query",
@@ -34,7 +34,7 @@ __all__ = [
     "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
     "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
-    "STORES_AUTO", "STORES_CACHED", "STORES_STREAMING",
+    "STORES_AUTO", "STORES_CACHED", "STORES_STREAMING", "FP8_SCALES_AMAX", "FP8_SCALES_POW2",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,13 +42,15 @@ _LIB_NAME = "libep_mi355x.so"
 
 LAYOUT_LL, LAYOUT_HT, LAYOUT_STATIC = 0, 1, 2
 _LAYOUTS = {"ll": LAYOUT_LL, "ht": LAYOUT_HT, "static": LAYOUT_STATIC}
-FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET, FLAG_PLAN_STALL = 1, 2, 4, 8
+FLAG_INDEX_RANGE, FLAG_CAPACITY, FLAG_SLOT_BUDGET, FLAG_PLAN_STALL, FLAG_SCALE_FORMAT = 1, 2, 4, 8, 16
 TAG_TOKENS, TAG_TOPK_IDX, TAG_TOPK_WEIGHTS, TAG_FP8_SCALES, TAG_EXPERT_GRADS = 0, 1, 2, 3, 4
 TAG_ROUTER_LOGITS, TAG_EXPERT_WEIGHTS = 5, 6
 SLOTS_TRAINING, SLOTS_INFERENCE = 0, 1
 _SLOT_MODES = {"training": SLOTS_TRAINING, "inference": SLOTS_INFERENCE}
 STORES_AUTO, STORES_CACHED, STORES_STREAMING = 0, 1, 2
 _STORES = {"auto": STORES_AUTO, "cached": STORES_CACHED, "streaming": STORES_STREAMING}
+FP8_SCALES_AMAX, FP8_SCALES_POW2 = 0, 1
+_FP8_SCALES = {"amax": FP8_SCALES_AMAX, "pow2": FP8_SCALES_POW2}
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
 _STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
            "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",
@@ -71,7 +73,8 @@ class ep_group_config_t(ctypes.Structure):
     _fields_ = [("num_experts", c_int32), ("num_ranks", c_int32), ("hidden", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
                 ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32),
-                ("dispatch_stores", c_int32), ("passes_in_flight", c_int32)]
+                ("dispatch_stores", c_int32), ("passes_in_flight", c_int32),
+                ("fp8_scales", c_int32)]
 
 
 class ep_handle_view_t(ctypes.Structure):
@@ -120,7 +123,7 @@ def load_library():
         "ep_plan": (S, [c_void_p, _T, c_void_p]),
         "ep_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_plan_dispatch": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
-        "ep_quantize_fp8": (S, [_T, _T, _T, c_void_p]),
+        "ep_quantize_fp8": (S, [_T, _T, _T, c_int32, c_void_p]),
         "ep_combine": (S, [c_void_p, _T, _T, _T, c_void_p]),
         "ep_combine_bwd": (S, [c_void_p, _T, _T, _T, _T, _T, c_void_p]),
         "ep_dup_grad_reduce": (S, [c_void_p, _T, _T, _T, c_void_p]),
@@ -342,9 +345,11 @@ def ep_plan_dispatch(h: int, topk_idx: torch.Tensor, tokens: torch.Tensor,
              _stream(stream))
 
 
-def ep_quantize_fp8(tokens: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+def ep_quantize_fp8(tokens: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None,
+                    pow2: bool = False) -> None:
     _enqueue("ep_quantize_fp8", _tensor(tokens, TAG_TOKENS), _tensor(codes, TAG_TOKENS),
-             _tensor(scales, TAG_FP8_SCALES), _stream(stream))
+             _tensor(scales, TAG_FP8_SCALES), FP8_SCALES_POW2 if pow2 else FP8_SCALES_AMAX,
+             _stream(stream))
 
 
 def ep_combine(h: int, expert_out: torch.Tensor, topk_weights: torch.Tensor | None,
@@ -421,13 +426,15 @@ class Group:
     def __init__(self, num_experts: int, num_ranks: int, hidden: int, top_k: int,
                  max_tokens: int, layout: str | int = "ht", capacity: int = 0,
                  slots_per_rank: int = 0, slot_mode: str | int = "training",
-                 dispatch_stores: str | int = "auto", passes_in_flight: int = 1):
+                 dispatch_stores: str | int = "auto", passes_in_flight: int = 1,
+                 fp8_scales: str | int = "amax"):
         self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
         mode = _SLOT_MODES[slot_mode] if isinstance(slot_mode, str) else int(slot_mode)
         stores = _STORES[dispatch_stores] if isinstance(dispatch_stores, str) else int(dispatch_stores)
+        f8 = _FP8_SCALES[fp8_scales] if isinstance(fp8_scales, str) else int(fp8_scales)
         self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
                                      self.layout, capacity, slots_per_rank, mode, stores,
-                                     passes_in_flight)
+                                     passes_in_flight, f8)
         self.ptr = ep_group_create(self.cfg)
 
     @property
@@ -650,16 +657,18 @@ class Buffer:
 
     @staticmethod
     def quantize_fp8(x: torch.Tensor, codes: torch.Tensor | None = None,
-                     scales: torch.Tensor | None = None, stream=None):
+                     scales: torch.Tensor | None = None, stream=None, pow2: bool = False):
         """bf16 rows [..., K] (K % 128 == 0) to e4m3 codes of the same shape
         and fp32 scales [..., K/128], bit for bit the FP8 dispatch's
-        quantisation; for the activation between the two FFN GEMMs."""
+        quantisation (``pow2``: power-of-two scales, as a group with
+        fp8_scales="pow2"); for the activation between the two FFN GEMMs,
+        or for FP8 weights."""
         K = x.shape[-1]
         if codes is None:
             codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
         if scales is None:
             scales = torch.empty(tuple(x.shape[:-1]) + (K // 128,), dtype=torch.float32, device=x.device)
-        ep_quantize_fp8(x, codes, scales, stream)
+        ep_quantize_fp8(x, codes, scales, stream, pow2=pow2)
         return codes, scales
 
     def dup_grad_reduce(self, replica_grads: torch.Tensor, owner_grads: torch.Tensor,

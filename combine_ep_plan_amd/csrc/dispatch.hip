@@ -292,8 +292,10 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(const u32x4 *__re
 // block spans 16 consecutive lanes: amax reduced over those lanes, scale =
 // amax / 448 and x / scale IEEE fp32 divisions, the quotient clamped to +-448
 // and rounded to nearest even by v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950).
+// pow2: the scale is rounded up to a power of two (at least 2^-126), so that
+// it is an 8-bit exponent the grouped GEMM's matrix cores can apply.
 // Returns the 8 codes; *scale gets the block's scale.
-__device__ __forceinline__ u32x2 quantize_fp8_vec(u32x4 xv, float *scale) {
+__device__ __forceinline__ u32x2 quantize_fp8_vec(u32x4 xv, float *scale, bool pow2) {
   float f[8];
   unpack8(xv, f);
   float amax = 0.0f;
@@ -303,7 +305,13 @@ __device__ __forceinline__ u32x2 quantize_fp8_vec(u32x4 xv, float *scale) {
   amax = fmaxf(amax, __shfl_xor(amax, 4));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
-  const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+  float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+  if (pow2 && amax != 0.0f) {
+    uint32_t b = __float_as_uint(s);
+    if (b < 0x00800000u) b = 0x00800000u;                                  // 2^-126
+    else if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;         // next power of two
+    s = __uint_as_float(b);
+  }
   float q[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(f[c] / s, -448.0f), 448.0f);
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
     const u32x4 cur = xv;
     if (v + kRowThreads < hi) xv = x[t * V + v + kRowThreads];
     float s;
-    const u32x2 packed = quantize_fp8_vec(cur, &s);
+    const u32x2 packed = quantize_fp8_vec(cur, &s, fl.g.fp8_pow2 != 0);
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
       if (K == 0 && j >= k) break;
@@ -367,25 +375,26 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
 // of 16 and the vector count is too).
 __global__ __launch_bounds__(256) void k_quantize_fp8(const u32x4 *__restrict__ x,
                                                       u32x2 *__restrict__ q,
-                                                      float *__restrict__ scales, int64_t nvec) {
+                                                      float *__restrict__ scales, int64_t nvec,
+                                                      bool pow2) {
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec;
        v += (int64_t)gridDim.x * 256) {
     float s;
-    const u32x2 codes = quantize_fp8_vec(x[v], &s);
+    const u32x2 codes = quantize_fp8_vec(x[v], &s, pow2);
     q[v] = codes;
     if ((v & 15) == 0) scales[v >> 4] = s;
   }
 }
 
 hipError_t launch_quantize_fp8(const uint16_t *x, int64_t rows, int32_t K, uint8_t *q,
-                               float *scales, hipStream_t s) {
+                               float *scales, bool pow2, hipStream_t s) {
   const int64_t nvec = rows * (K / 8);
   if (nvec == 0) return hipSuccess;
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(k_quantize_fp8, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), scales,
-                     nvec);
+                     nvec, pow2);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.slot_mode = c.slot_mode;
   geo.stores = c.dispatch_stores;
   geo.in_flight = c.passes_in_flight > 1 ? c.passes_in_flight : 1;
+  geo.fp8_pow2 = c.fp8_scales == EP_FP8_SCALES_POW2 ? 1 : 0;
   geo.layout = c.layout;
   geo.cap = c.capacity;
   geo.n = (int64_t)T * c.top_k;
@@ -204,6 +205,7 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
   if (c.dispatch_stores < EP_STORES_AUTO || c.dispatch_stores > EP_STORES_STREAMING)
     return EP_ERR_INVALID_ARG;
   if (c.passes_in_flight < 0 || c.passes_in_flight > 64) return EP_ERR_INVALID_ARG;
+  if (c.fp8_scales != EP_FP8_SCALES_AMAX && c.fp8_scales != EP_FP8_SCALES_POW2) return EP_ERR_INVALID_ARG;
   if (c.slot_mode != EP_SLOTS_TRAINING &&
       !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))
     return EP_ERR_INVALID_ARG;
@@ -502,7 +504,8 @@ ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
 }
 
 ep_status_t ep_quantize_fp8(const ep_tensor_t *tokens, ep_tensor_t *codes, ep_tensor_t *scales,
-                            void *stream) {
+                            int32_t fp8_scales, void *stream) {
+  if (fp8_scales != EP_FP8_SCALES_AMAX && fp8_scales != EP_FP8_SCALES_POW2) return EP_ERR_INVALID_ARG;
   ep_status_t st = check_tensor(tokens, EP_TAG_TOKENS, EP_DTYPE_BF16);
   if (st != EP_OK) return st;
   st = check_tensor(codes, EP_TAG_TOKENS, EP_DTYPE_FP8_E4M3);
@@ -517,7 +520,7 @@ ep_status_t ep_quantize_fp8(const ep_tensor_t *tokens, ep_tensor_t *codes, ep_te
   return hip_status(epk::launch_quantize_fp8(static_cast<const uint16_t *>(tokens->data), rows,
                                              (int32_t)K, static_cast<uint8_t *>(codes->data),
                                              static_cast<float *>(scales->data),
-                                             as_stream(stream)));
+                                             fp8_scales == EP_FP8_SCALES_POW2, as_stream(stream)));
 }
 
 ep_status_t ep_combine(ep_handle_t h, const ep_tensor_t *expert_out,

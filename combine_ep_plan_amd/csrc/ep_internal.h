@@ -24,6 +24,7 @@ constexpr uint32_t kFlagIndexRange = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
 constexpr uint32_t kFlagSlotBudget = 4u;
 constexpr uint32_t kFlagPlanStall = 8u;
+constexpr uint32_t kFlagScaleFormat = 16u;
 
 enum Layout : int32_t { kLL = 0, kHT = 1, kStatic = 2 };
 
@@ -63,6 +64,7 @@ struct Geometry {
   int32_t slot_mode;  // 0 training (overflow flags SLOT_BUDGET), 1 inference
   int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
   int32_t in_flight;  // passes of the group at once (>= 1): the size rule counts all their rows
+  int32_t fp8_pow2;   // FP8 scales are powers of two (EP_FP8_SCALES_POW2)
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
   int32_t cus;      // compute units of the device (0 if unknown): the most tiles one launch finishes
@@ -97,7 +99,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const Workspace &ws, const uin
                                const int32_t *idx = nullptr, bool fused = false);
 // rows x K bf16 to e4m3 codes + fp32 scales per 128 (the FP8 dispatch's recipe)
 hipError_t launch_quantize_fp8(const uint16_t *x, int64_t rows, int32_t K, uint8_t *q,
-                               float *scales, hipStream_t s);
+                               float *scales, bool pow2, hipStream_t s);
 hipError_t launch_recv_meta(const Geometry &g, const Workspace &ws, const float *topk_w,
                             int32_t *recv_idx, float *recv_w, hipStream_t s);
 hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t *rows,

@@ -444,6 +444,66 @@ constexpr int kLoadsB2 = kBN2 * kChunks / kGemmThreads;   // ... and of W
 constexpr int kSlabA2 = kBM2 * kChunks, kSlabB2 = kBN2 * kChunks;
 constexpr int kBufDword3 = 0x00020000;                    // buffer resource word 3 (raw, 32-bit data)
 
+// Epilogue of the 256 x 256 kernels: the fp32 tile (a wave's 4 x 4 blocks of
+// 32 x 32) to bf16 rows of Y (plain, or SwiGLU pairs).  N % 8 == 0: through
+// LDS (the slab buffers, free by now) as bf16 rows of 256 with the 128 x 128
+// kernel's chunk swizzle, then 16-byte row stores; otherwise 2-byte stores.
+template <bool GLU>
+__device__ __forceinline__ void wide_epilogue(f32x16 (&acc)[kFM2][kFN2], u32x4 *lds, int32_t rows,
+                                              int32_t row0, int32_t n0, int32_t N,
+                                              uint16_t *__restrict__ Y, int wm, int wn, int lane,
+                                              int tid) {
+  if (GLU || (N & 7) == 0) {   // a SwiGLU launch has N % 16 == 0
+    __syncthreads();
+    uint16_t *so = reinterpret_cast<uint16_t *>(lds);
+#define OSW(r_, cv_) ((r_) * kBN2 + (((cv_) ^ ((((r_) >> 2) & 3) << 2)) << 3))
+#pragma unroll
+    for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN2; ++j) {
+        const int c = wn * kWTN2 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int rr = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+          so[OSW(rr, c >> 3) + (c & 7)] = (uint16_t)(p & 0xFFFFu);
+          so[OSW(rr + 1, c >> 3) + (c & 7)] = (uint16_t)(p >> 16);
+        }
+      }
+    __syncthreads();
+    constexpr int kVecs = kBM2 * kBN2 / 8;
+#pragma unroll 4
+    for (int q = 0; q < kVecs / kGemmThreads; ++q) {
+      const int idx = tid + q * kGemmThreads;
+      const int rr = idx / (kBN2 / 8), cv = idx % (kBN2 / 8);
+      const int col = n0 + cv * 8;
+      if (rr < rows && col < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
+        if constexpr (GLU)   // columns col .. col + 7 give outputs col / 2 .. col / 2 + 3
+          *reinterpret_cast<uint2 *>(Y + (int64_t)(row0 + rr) * (N / 2) + col / 2) = swiglu4(v);
+        else
+          *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) = v;
+      }
+    }
+#undef OSW
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN2; ++j) {
+      const int col = n0 + wn * kWTN2 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+        if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
+        if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
+      }
+    }
+}
+
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
     const u32x4 *__restrict__ X, const u32x4 *__restrict__ W, const u32x4 *__restrict__ Wslot,
@@ -452,6 +512,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
     int32_t E, int32_t n_col_tiles, uint16_t *__restrict__ Y) {
   // two 64-deep slabs of X and W (128 KB), then the bf16 output tile
   __shared__ u32x4 lds[2 * kSlabA2 + 2 * kSlabB2];
+  static_assert(kBM2 * kBN2 * 2 <= (int)sizeof(lds), "output tile fits the slab buffers");
   u32x4 *const sa = lds, *const sb = lds + 2 * kSlabA2;
   int32_t tile, ctile;
   if (!balanced_tile(ntiles, max_tiles, n_col_tiles, tile, ctile)) return;
@@ -611,58 +672,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_256(
 #undef GLOAD_B
 #undef GLOAD_A
 
-  if (GLU || (N & 7) == 0) {   // a SwiGLU launch has N % 16 == 0
-    // through LDS as bf16 rows of 256 (same chunk swizzle as the 128 x 128
-    // kernel's epilogue), then 16-byte row stores
-    __syncthreads();
-    uint16_t *so = reinterpret_cast<uint16_t *>(lds);
-    static_assert(kBM2 * kBN2 * 2 <= (int)sizeof(lds), "output tile fits the slab buffers");
-#define OSW(r_, cv_) ((r_) * kBN2 + (((cv_) ^ ((((r_) >> 2) & 3) << 2)) << 3))
-#pragma unroll
-    for (int i = 0; i < kFM2; ++i)
-#pragma unroll
-      for (int j = 0; j < kFN2; ++j) {
-        const int c = wn * kWTN2 + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const int rr = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
-          so[OSW(rr, c >> 3) + (c & 7)] = (uint16_t)(p & 0xFFFFu);
-          so[OSW(rr + 1, c >> 3) + (c & 7)] = (uint16_t)(p >> 16);
-        }
-      }
-    __syncthreads();
-    constexpr int kVecs = kBM2 * kBN2 / 8;
-#pragma unroll 4
-    for (int q = 0; q < kVecs / kGemmThreads; ++q) {
-      const int idx = tid + q * kGemmThreads;
-      const int rr = idx / (kBN2 / 8), cv = idx % (kBN2 / 8);
-      const int col = n0 + cv * 8;
-      if (rr < rows && col < N) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + OSW(rr, cv));
-        if constexpr (GLU)   // columns col .. col + 7 give outputs col / 2 .. col / 2 + 3
-          *reinterpret_cast<uint2 *>(Y + (int64_t)(row0 + rr) * (N / 2) + col / 2) = swiglu4(v);
-        else
-          *reinterpret_cast<u32x4 *>(Y + (int64_t)(row0 + rr) * N + col) = v;
-      }
-    }
-#undef OSW
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < kFM2; ++i)
-#pragma unroll
-    for (int j = 0; j < kFN2; ++j) {
-      const int col = n0 + wn * kWTN2 + j * 32 + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int row = wm * kWTM2 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
-        if (row < rows) Y[(int64_t)(row0 + row) * N + col] = (uint16_t)(p & 0xFFFFu);
-        if (row + 1 < rows) Y[(int64_t)(row0 + row + 1) * N + col] = (uint16_t)(p >> 16);
-      }
-    }
+  wide_epilogue<GLU>(acc, lds, rows, row0, n0, N, Y, wm, wn, lane, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -935,6 +945,218 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
     }
 }
 
+// ---------------------------------------------------------------------------
+// grouped GEMM on FP8 operands with power-of-two scales, 256 x 256 tiles
+//
+// When every scale is a power of two (the group's fp8_scales = POW2: the FP8
+// dispatch and ep_quantize_fp8 then write such scales, and the caller's
+// weight scales are such too), the matrix cores apply them:
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes one E8M0 exponent per lane for the
+// 32 K-values the lane holds (A: the lane's row, B: its column), and both
+// 64-deep steps of a 128-deep slab lie in one scale block, so
+// SX[row][b] * SW[col][b] is applied exactly inside the MFMA and the
+// accumulators run over the whole of K with no vector-ALU fold.  What is left
+// is the bf16 wide kernel's loop: the same tiles, waves, LDS geometry (a
+// 128-deep slab of codes is 128 bytes per row, as a 64-deep bf16 slab) and
+// pipelining, with two 64-deep steps per slab instead of four 16-deep ones,
+// so half as many slabs for the same K.  The slab's exponents (one byte per
+// tile row and per tile column) go through LDS beside the codes, packed so a
+// lane reads the exponents of its four row blocks, and of its four column
+// blocks, as one word each; the MFMA's byte select (op_sel) picks them.
+// A scale that is not a positive normal power of two raises
+// EP_FLAG_SCALE_FORMAT (its block is then computed at the scale's exponent).
+
+constexpr int kF8KV = kF8Block / 16;   // 16-byte chunks per row of a slab (= kChunks)
+static_assert(kF8KV == kChunks, "an FP8 slab row is 128 bytes, as a bf16 one");
+
+// One step's 16 (or fewer) MFMAs of a wave: rows blocks I < NB, all column
+// blocks; byte I of ea and byte J of eb are the blocks' scale exponents.
+template <int I, int NB>
+__device__ __forceinline__ void mfma8_rows(f32x16 (&acc)[kFM2][kFN2], const i32x8 (&fa)[kFM2],
+                                           const i32x8 (&fb)[kFN2], int ea, int eb) {
+  if constexpr (I < NB) {
+    acc[I][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[0], acc[I][0], 0, 0, I, ea, 0, eb);
+    acc[I][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[1], acc[I][1], 0, 0, I, ea, 1, eb);
+    acc[I][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[2], acc[I][2], 0, 0, I, ea, 2, eb);
+    acc[I][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[3], acc[I][3], 0, 0, I, ea, 3, eb);
+    mfma8_rows<I + 1, NB>(acc, fa, fb, ea, eb);
+  }
+}
+static_assert(kFN2 == 4, "mfma8_rows writes four column blocks");
+
+// E8M0 exponent of a power-of-two fp32 scale; *bad is set if it is not one.
+__device__ __forceinline__ uint32_t scale_exponent(float s, uint32_t *bad) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t e = (b >> 23) & 0xFFu;
+  if ((b & 0x807FFFFFu) != 0u || e == 0u || e == 0xFFu) *bad = 1u;
+  return e;
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <bool GLU>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
+    const u32x4 *__restrict__ X, const float *__restrict__ SX, const u32x4 *__restrict__ W,
+    const float *__restrict__ SW, const u32x4 *__restrict__ Wslot,
+    const float *__restrict__ SWslot, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, int32_t max_tiles, int32_t K, int32_t N, int32_t E,
+    int32_t n_col_tiles, uint16_t *__restrict__ Y, uint32_t *__restrict__ status) {
+  // two 128-deep slabs of X and W codes (128 KB), later the bf16 output tile;
+  // the slabs' fp32 scales: [buffer][256 row scales, 256 column scales]
+  __shared__ u32x4 lds[2 * kSlabA2 + 2 * kSlabB2];
+  __shared__ float ssc[2][2 * kBM2];
+  static_assert(kBM2 * kBN2 * 2 <= (int)sizeof(lds), "output tile fits the slab buffers");
+  static_assert(kBM2 == kBN2 && kBM2 == kGemmThreads, "one row and one column scale per thread");
+  u32x4 *const sa = lds, *const sb = lds + 2 * kSlabA2;
+  int32_t tile, ctile;
+  if (!balanced_tile(ntiles, max_tiles, n_col_tiles, tile, ctile)) return;
+  const int32_t n0 = ctile * kBN2;
+  const int32_t row0 = tiles[tile * 4 + 0], rows = tiles[tile * 4 + 1], widx = tiles[tile * 4 + 2];
+  const int32_t KV = K / 16;        // 16-byte vectors per row of codes
+  const int32_t NB = K / kF8Block;  // scales per row
+  const bool own = widx < E;
+  const int64_t wsel = own ? widx : widx - E;
+  const int32_t wrows = N - n0 < kBN2 ? N - n0 : kBN2;
+  // buffer resources over the tile's rows of codes and of scales (every
+  // offset in range by construction: rows past the end read the last row)
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(X + (int64_t)row0 * KV), (short)0, rows * K, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((own ? W : Wslot) + wsel * N * KV + (int64_t)n0 * KV), (short)0, wrows * K,
+      kBufDword3);
+  const __amdgpu_buffer_rsrc_t rSX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(SX + (int64_t)row0 * NB), (short)0, rows * NB * 4, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rSW = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((own ? SW : SWslot) + wsel * N * NB + (int64_t)n0 * NB), (short)0, wrows * NB * 4,
+      kBufDword3);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wv >> 1, wn = wv & 1;
+  // The loads go straight into LDS: load i of wave wv fills the 64 16-byte
+  // slots i*256 + wv*64 + lane, slot q holding chunk (q % 8) ^ ((r / 2) % 8)
+  // of row r = q / 8 -- the chunk swizzle the fragment reads expect.
+  uint32_t oa[kLoads2], ob[kLoadsB2];
+#pragma unroll
+  for (int i = 0; i < kLoads2; ++i) {
+    const int q = i * kGemmThreads + tid, r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    oa[i] = (uint32_t)(((r < rows ? r : rows - 1) * KV + c) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsB2; ++i) {
+    const int q = i * kGemmThreads + tid, r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    ob[i] = (uint32_t)(((r < wrows ? r : wrows - 1) * KV + c) * 16);
+  }
+  const uint32_t osx = (uint32_t)((tid < rows ? tid : rows - 1) * NB * 4);
+  const uint32_t osw = (uint32_t)((tid < wrows ? tid : wrows - 1) * NB * 4);
+  // The compiler does not count these loads: the waits before the barriers
+  // that publish a slab are explicit (s_waitcnt vmcnt, then s_barrier).
+#define F8W_ISSUE(kt, buf)                                                                     \
+  {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kLoads2; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
+        rX, LDS_PTR(&sa[(buf) * kSlabA2 + i * kGemmThreads + wv * 64]), 16, oa[i], (kt) * 128, 0, 0); \
+    _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
+        rW, LDS_PTR(&sb[(buf) * kSlabB2 + i * kGemmThreads + wv * 64]), 16, ob[i], (kt) * 128, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSX, LDS_PTR(&ssc[buf][wv * 64]), 4, osx, (kt) * 4, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSW, LDS_PTR(&ssc[buf][kBM2 + wv * 64]), 4, osw,  \
+                                             (kt) * 4, 0, 0);                                  \
+  }
+  static_assert(kLoads2 + kLoadsB2 + 2 == 18, "the waits below count 18 loads per slab");
+// step h (0 or 1) of a slab: the lane's 32 K-values of its row (A) or column
+// (B) are chunks h*4 + (lane/32)*2 and the next one
+#define READK8(FA, FB, buf, h, NBK)                                                            \
+  {                                                                                            \
+    const int c_ = (h) * 4 + (lane >> 5) * 2;                                                  \
+    _Pragma("unroll") for (int i = 0; i < (NBK); ++i) {                                        \
+      const int r_ = wm * kWTM2 + i * 32 + (lane & 31);                                        \
+      const u32x4 lo = sa[(buf) * kSlabA2 + swz(r_, c_)];                                      \
+      const u32x4 hi = sa[(buf) * kSlabA2 + swz(r_, c_ + 1)];                                  \
+      FA[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,                                \
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};                               \
+    }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < kFN2; ++j) {                                         \
+      const int r_ = wn * kWTN2 + j * 32 + (lane & 31);                                        \
+      const u32x4 lo = sb[(buf) * kSlabB2 + swz(r_, c_)];                                      \
+      const u32x4 hi = sb[(buf) * kSlabB2 + swz(r_, c_ + 1)];                                  \
+      FB[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,                                \
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};                               \
+    }                                                                                          \
+  }
+// the exponents of the lane's four row blocks (byte i: row wm*128 + i*32 +
+// lane%32) and of its four column blocks
+#define READE(EA, EB, buf)                                                                     \
+  {                                                                                            \
+    uint32_t ea_ = 0u, eb_ = 0u;                                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+      ea_ |= scale_exponent(ssc[buf][wm * kWTM2 + i * 32 + (lane & 31)], &bad) << (8 * i);     \
+      eb_ |= scale_exponent(ssc[buf][kBM2 + wn * kWTN2 + i * 32 + (lane & 31)], &bad) << (8 * i); \
+    }                                                                                          \
+    EA = (int)ea_;                                                                             \
+    EB = (int)eb_;                                                                             \
+  }
+
+  f32x16 acc[kFM2][kFN2];
+#pragma unroll
+  for (int i = 0; i < kFM2; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int KT = K / kF8Block;
+  uint32_t bad = 0u;
+  i32x8 fa0[kFM2], fb0[kFN2], fa1[kFM2], fb1[kFN2];
+  int ea, eb, ea_n = 0, eb_n = 0;
+  F8W_ISSUE(0, 0);
+  if (KT > 1) {
+    F8W_ISSUE(1, 1);
+    asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");   // slab 0 landed
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  // Slab kt is in buffer kt & 1 and slab kt + 1 on its way into the other;
+  // step 0's fragments and the slab's exponents were read after the barrier
+  // that published slab kt.  Step 1's reads go under step 0's MFMAs; then
+  // the barrier (slab kt + 1 landed, slab kt read by every wave), the loads
+  // of slab kt + 2 into the buffer just freed, and the reads of slab kt + 1's
+  // step 0 under step 1's MFMAs.  (Half-slabs in four buffers, loaded three
+  // ahead, measured 1.6 times slower: twice the barriers.)  Compiled once
+  // per count of the wave's live 32-row blocks (same barriers in every copy).
+#define F8W_LOOP(NBK)                                                                          \
+  {                                                                                            \
+    READK8(fa0, fb0, 0, 0, NBK);                                                               \
+    READE(ea, eb, 0);                                                                          \
+    for (int kt = 0; kt < KT; ++kt) {                                                          \
+      const int buf = kt & 1;                                                                  \
+      READK8(fa1, fb1, buf, 1, NBK);                                                           \
+      mfma8_rows<0, NBK>(acc, fa0, fb0, ea, eb);                                               \
+      if (kt + 1 < KT) {                                                                       \
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");               \
+        if (kt + 2 < KT) F8W_ISSUE(kt + 2, buf);                                               \
+        READK8(fa0, fb0, buf ^ 1, 0, NBK);                                                     \
+        READE(ea_n, eb_n, buf ^ 1);                                                            \
+      }                                                                                        \
+      mfma8_rows<0, NBK>(acc, fa1, fb1, ea, eb);                                               \
+      ea = ea_n;                                                                               \
+      eb = eb_n;                                                                               \
+    }                                                                                          \
+  }
+  const int live = (rows - wm * kWTM2 + 31) / 32;  // wave-uniform
+  if (live >= kFM2) F8W_LOOP(kFM2)
+  else if (live == 3) F8W_LOOP(3)
+  else if (live == 2) F8W_LOOP(2)
+  else if (live == 1) F8W_LOOP(1)
+  else F8W_LOOP(0)
+#undef F8W_LOOP
+#undef READE
+#undef READK8
+#undef F8W_ISSUE
+  const uint64_t any_bad = __ballot(bad != 0u);
+  if (any_bad != 0u && lane == 0) atomicOr(status, kFlagScaleFormat);
+  wide_epilogue<GLU>(acc, lds, rows, row0, n0, N, Y, wm, wn, lane, tid);
+}
+#undef LDS_PTR
+
 // Row tiles of kTileM rows the plan can produce; the 256-row tiling needs no more.
 int32_t gemm_max_tiles(const Geometry &g) {
   const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
@@ -962,6 +1184,21 @@ static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
   return N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E && (int64_t)kBM2 * K * 2 <= INT32_MAX;
 }
 
+// The FP8 256 x 256 kernel needs power-of-two scales (the group's format)
+// and pays off from about 512 rows per expert on average (with fewer, the
+// 128 x 128 kernel's two workgroups per CU stream short groups' weights
+// faster); its buffer offsets over a tile's codes are 32-bit as well.
+static bool gemm_fp8_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
+  return g.fp8_pow2 && N >= kBN2 && g.n >= (int64_t)(2 * kBM2) * g.E &&
+         (int64_t)kBM2 * K <= INT32_MAX;
+}
+
+// At most as many 256-row tiles as the table holds 128-row ones.
+static int32_t wide_max_tiles(const Geometry &g) {
+  const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
+  return (int32_t)((g.n + kBM2 - 1) / kBM2 + groups);
+}
+
 hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uint16_t *x,
                                const uint16_t *w, const uint16_t *wslot, int32_t K, int32_t N,
                                uint16_t *y, bool glu, hipStream_t s) {
@@ -969,9 +1206,7 @@ hipError_t launch_grouped_gemm(const Geometry &g, const Workspace &ws, const uin
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
   if (gemm_uses_wide_tiles(g, K, N)) {
-    // at most as many 256-row tiles as the table holds 128-row ones
-    const int64_t groups = g.layout == kStatic ? 2 * (int64_t)g.E + g.R : g.E;
-    const int32_t max2 = (int32_t)((g.n + kBM2 - 1) / kBM2 + groups);
+    const int32_t max2 = wide_max_tiles(g);
     hipLaunchKernelGGL((k_gemm_tiles<kBM2, true>), dim3(1), dim3(1024), 0, s, ta, max2);
     const int32_t ncol = (N + kBN2 - 1) / kBN2;
     GEMM_LAUNCH(k_grouped_gemm_256, dim3(gemm_grid(max2, ncol)), dim3(kGemmThreads), 0, s,
@@ -996,6 +1231,16 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
   const int32_t max_tiles = gemm_max_tiles(g);
   if (max_tiles == 0 || N == 0) return hipSuccess;
   TileArgs ta{g, ws, wslot != nullptr ? 1 : 0};
+  if (gemm_fp8_uses_wide_tiles(g, K, N)) {
+    const int32_t max2 = wide_max_tiles(g);
+    hipLaunchKernelGGL((k_gemm_tiles<kBM2, true>), dim3(1), dim3(1024), 0, s, ta, max2);
+    const int32_t ncol = (N + kBN2 - 1) / kBN2;
+    GEMM_LAUNCH(k_grouped_gemm_fp8_256, dim3(gemm_grid(max2, ncol)), dim3(kGemmThreads), 0, s,
+                reinterpret_cast<const u32x4 *>(x), sx, reinterpret_cast<const u32x4 *>(w), sw,
+                reinterpret_cast<const u32x4 *>(wslot), swslot, ws.gemm_tiles, ws.gemm_ntiles,
+                max2, K, N, g.E, ncol, y, ws.status);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_gemm_tiles<kTileM, false>), dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
   GEMM_LAUNCH(k_grouped_gemm_fp8, dim3(gemm_grid(max_tiles, ncol)), dim3(kGemmThreads), 0, s,

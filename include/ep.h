@@ -77,6 +77,9 @@ typedef enum ep_status {
                                    all run at once within about half a second (the GPU was held
                                    by other work): the layout of that call is incomplete and must
                                    be planned again */
+#define EP_FLAG_SCALE_FORMAT 16u /* a group with EP_FP8_SCALES_POW2: an FP8 scale handed to the
+                                    grouped GEMM was not a positive normal power of two (its
+                                    block was taken at the scale's exponent) */
 
 /* Tensor roles (NCCL EP paper listing, Table IV).  EP_TAG_EXPERT_GRADS,
  * EP_TAG_ROUTER_LOGITS and EP_TAG_EXPERT_WEIGHTS are this library's additions
@@ -128,6 +131,20 @@ typedef enum ep_dispatch_stores {
   EP_STORES_STREAMING = 2  /* non-temporal */
 } ep_dispatch_stores_t;
 
+/* Format of the fp32 scales of FP8 rows (one per row and 128 channels).
+ * The pages fix only that FP8 rows travel with scales (NCCL EP listing,
+ * Table IV); both formats are readings.  AMAX: scale = amax / 448, the
+ * block's largest value lands on the largest e4m3 code.  POW2: the smallest
+ * power of two at or above amax / 448 (at least 2^-126; 1 for an all-zero
+ * block), so a scale is an 8-bit exponent and the grouped GEMM's matrix
+ * cores apply it themselves: with POW2 the FP8 GEMM of large groups takes
+ * the 256 x 256 kernel with no per-block rescaling, and the weights' scales
+ * must be powers of two too (ep_quantize_fp8 with POW2 makes such). */
+typedef enum ep_fp8_scales {
+  EP_FP8_SCALES_AMAX = 0,
+  EP_FP8_SCALES_POW2 = 1
+} ep_fp8_scales_t;
+
 /* Non-owning view of a contiguous row-major device tensor.  data must be
  * 16-byte aligned for the tags TOKENS, EXPERT_WEIGHTS and EXPERT_GRADS (rows
  * move as 16-byte vectors) and 4-byte aligned for the others; a misaligned
@@ -156,6 +173,7 @@ typedef struct ep_group_config {
   int32_t passes_in_flight; /* passes of this group the caller runs at once (e.g. micro-batches
                                on several streams); 0 or 1 = one.  EP_STORES_AUTO weighs the
                                receive rows of all of them against the Infinity Cache. */
+  int32_t fp8_scales;      /* ep_fp8_scales_t: FP8 dispatch scales and the FP8 GEMM's path */
 } ep_group_config_t;
 
 typedef struct ep_group *ep_group_t;
@@ -375,10 +393,12 @@ ep_status_t ep_plan_dispatch(ep_handle_t h, const ep_tensor_t *topk_idx,
  * tokens: bf16 [rows, K] (any leading shape), tag TOKENS; K % 128 == 0.
  * codes:  e4m3, the same shape, tag TOKENS.
  * scales: fp32 [rows, K/128] (any leading shape), tag FP8_SCALES.
+ * fp8_scales: ep_fp8_scales_t, the scale format (AMAX as above; POW2 the
+ *             power of two at or above amax/448, as a POW2 group's dispatch).
  * Errors: EP_ERR_BAD_TAG / _BAD_DTYPE / _BAD_SHAPE / _INVALID_ARG.
  * Enqueues one kernel. */
 ep_status_t ep_quantize_fp8(const ep_tensor_t *tokens, ep_tensor_t *codes, ep_tensor_t *scales,
-                            void *stream);
+                            int32_t fp8_scales, void *stream);
 
 /* Gather each token's expert outputs back to its place (NCCL EP listing,
  * Table II):  out[t, :] = sum_j w[t, j] * expert_out[dst[t*k+j], :], j

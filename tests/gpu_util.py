@@ -31,8 +31,9 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
-def make_group(E, R, H, k, T, kind, cap=0, S=0, mode="training") -> ep.Group:
-    return ep.Group(E, R, H, k, max(T, 1), kind, capacity=cap, slots_per_rank=S, slot_mode=mode)
+def make_group(E, R, H, k, T, kind, cap=0, S=0, mode="training", fp8_scales="amax") -> ep.Group:
+    return ep.Group(E, R, H, k, max(T, 1), kind, capacity=cap, slots_per_rank=S, slot_mode=mode,
+                    fp8_scales=fp8_scales)
 
 
 def check_layout(h: ep.Handle, L: "oracle.Layout", kind: str, idx: np.ndarray, w: np.ndarray | None):

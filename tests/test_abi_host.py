@@ -56,7 +56,7 @@ def test_status_strings(lib):
 def cfg(**kw):
     base = dict(num_experts=8, num_ranks=4, hidden=256, top_k=2, max_tokens=64,
                 layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0, slot_mode=0, dispatch_stores=0,
-                passes_in_flight=0)
+                passes_in_flight=0, fp8_scales=0)
     base.update(kw)
     return ep.ep_group_config_t(*[base[f] for f, _ in ep.ep_group_config_t._fields_])
 
@@ -73,7 +73,7 @@ def create(lib, **kw):
     dict(layout=7), dict(layout=ep.LAYOUT_LL, capacity=0), dict(layout=ep.LAYOUT_STATIC, slots_per_rank=-1),
     dict(layout=ep.LAYOUT_STATIC, slot_mode=2), dict(layout=ep.LAYOUT_STATIC, slot_mode=-1),
     dict(dispatch_stores=3), dict(dispatch_stores=-1), dict(passes_in_flight=-1),
-    dict(passes_in_flight=65),
+    dict(passes_in_flight=65), dict(fp8_scales=2), dict(fp8_scales=-1),
     dict(slot_mode=ep.SLOTS_INFERENCE),               # the inference slot mode is STATIC only
     dict(layout=ep.LAYOUT_STATIC, num_experts=1024, num_ranks=1024, slots_per_rank=1 << 22),
 ])
@@ -85,6 +85,13 @@ def test_group_config_validation(lib, bad):
 @pytest.mark.parametrize("stores", [ep.STORES_AUTO, ep.STORES_CACHED, ep.STORES_STREAMING])
 def test_group_accepts_each_dispatch_store_kind(lib, stores):
     rc, g = create(lib, dispatch_stores=stores)
+    assert rc == 0
+    lib.ep_group_destroy(g)
+
+
+@pytest.mark.parametrize("f8", [ep.FP8_SCALES_AMAX, ep.FP8_SCALES_POW2])
+def test_group_accepts_each_fp8_scale_format(lib, f8):
+    rc, g = create(lib, fp8_scales=f8)
     assert rc == 0
     lib.ep_group_destroy(g)
 
@@ -456,7 +463,8 @@ def test_binding_refuses_host_tensors():
 
 
 def test_quantize_fp8_argument_validation(lib):
-    Q = lib.ep_quantize_fp8
+    def Q(x, q, s, stream, fmt=0):
+        return lib.ep_quantize_fp8(x, q, s, fmt, stream)
     TK, SC = ep.TAG_TOKENS, ep.TAG_FP8_SCALES
     x, q, s = T(BF16, TK, 64, 256), T(FP8, TK, 64, 256), T(F32, SC, 64, 2)
     assert Q(None, q, s, None) == 1
@@ -470,11 +478,15 @@ def test_quantize_fp8_argument_validation(lib):
     assert Q(x, q, T(F32, SC, 64, 3), None) == 4              # scales not [rows, K/128]
     assert Q(x, q, T(F32, SC, 64, 2, data=FAKE + 2), None) == 1
     assert Q(T(BF16, TK, 64, 256, data=FAKE + 8), q, s, None) == 1
+    assert Q(x, q, s, None, fmt=2) == 1                      # no such scale format
+    assert Q(x, q, s, None, fmt=-1) == 1
     # zero rows, also under a leading shape, pass validation and enqueue nothing
     assert Q(T(BF16, TK, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
              T(F32, SC, 0, 2, data=None), None) == 0
     assert Q(T(BF16, TK, 4, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
              T(F32, SC, 0, 2, data=None), None) == 0
+    assert Q(T(BF16, TK, 0, 256, data=None), T(FP8, TK, 0, 256, data=None),
+             T(F32, SC, 0, 2, data=None), None, fmt=1) == 0
 
 
 def test_prepare_records_without_enqueueing():
