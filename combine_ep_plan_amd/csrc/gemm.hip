@@ -987,12 +987,33 @@ static_assert(kFN2 == 4, "mfma8_rows writes four column blocks");
 // E8M0 exponent of a power-of-two fp32 scale; *bad is set if it is not one.
 __device__ __forceinline__ uint32_t scale_exponent(float s, uint32_t *bad) {
   const uint32_t b = __float_as_uint(s);
-  const uint32_t e = (b >> 23) & 0xFFu;
-  if ((b & 0x807FFFFFu) != 0u || e == 0u || e == 0xFFu) *bad = 1u;
-  return e;
+  const uint32_t e = b >> 23;  // a set sign bit makes it 256 or more
+  // no branch: a mantissa bit, a sign, a zero or an all-ones exponent
+  *bad |= (b & 0x007FFFFFu) | (uint32_t)(e - 1u > 0xFDu);
+  return e & 0xFFu;
 }
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// A buffer load whose lanes' 16 (or 4) bytes land in LDS at m0 + lane * 16
+// (or 4), m0 being the wave's LDS base.  Written in asm on purpose: the
+// compiler tracks its own form of this load and, unable to tell which part
+// of LDS it writes, makes every later LDS read wait until it has landed --
+// which would let no slab load run under the MFMAs of the previous slab.
+// Here the caller owns the waits (s_waitcnt vmcnt before the barrier that
+// publishes the data).  No result register: nothing the compiler allocates
+// is written late.  The s_nop is the wait state the hardware needs between
+// the write of m0 and the load that reads it.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base,
+                                           uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base,
+                                          uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base) : "memory");
+}
 
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
@@ -1049,17 +1070,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
   }
   const uint32_t osx = (uint32_t)((tid < rows ? tid : rows - 1) * NB * 4);
   const uint32_t osw = (uint32_t)((tid < wrows ? tid : wrows - 1) * NB * 4);
-  // The compiler does not count these loads: the waits before the barriers
-  // that publish a slab are explicit (s_waitcnt vmcnt, then s_barrier).
+  // The waits before the barriers that publish a slab are explicit
+  // (s_waitcnt vmcnt, then s_barrier): the loads are issued from asm (see
+  // lds_load16), so the compiler neither counts nor waits for them.
+#define LDS_ADDR(p) ((uint32_t)(size_t)LDS_PTR(p))
 #define F8W_ISSUE(kt, buf)                                                                     \
   {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < kLoads2; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
-        rX, LDS_PTR(&sa[(buf) * kSlabA2 + i * kGemmThreads + wv * 64]), 16, oa[i], (kt) * 128, 0, 0); \
-    _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
-        rW, LDS_PTR(&sb[(buf) * kSlabB2 + i * kGemmThreads + wv * 64]), 16, ob[i], (kt) * 128, 0, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSX, LDS_PTR(&ssc[buf][wv * 64]), 4, osx, (kt) * 4, 0, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSW, LDS_PTR(&ssc[buf][kBM2 + wv * 64]), 4, osw,  \
-                                             (kt) * 4, 0, 0);                                  \
+    _Pragma("unroll") for (int i = 0; i < kLoads2; ++i) lds_load16(                            \
+        rX, LDS_ADDR(&sa[(buf) * kSlabA2 + i * kGemmThreads + wv * 64]), oa[i], (kt) * 128);   \
+    _Pragma("unroll") for (int i = 0; i < kLoadsB2; ++i) lds_load16(                           \
+        rW, LDS_ADDR(&sb[(buf) * kSlabB2 + i * kGemmThreads + wv * 64]), ob[i], (kt) * 128);   \
+    lds_load4(rSX, LDS_ADDR(&ssc[buf][wv * 64]), osx, (kt) * 4);                               \
+    lds_load4(rSW, LDS_ADDR(&ssc[buf][kBM2 + wv * 64]), osw, (kt) * 4);                        \
   }
   static_assert(kLoads2 + kLoadsB2 + 2 == 18, "the waits below count 18 loads per slab");
 // step h (0 or 1) of a slab: the lane's 32 K-values of its row (A) or column
@@ -1107,39 +1129,61 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
   uint32_t bad = 0u;
   i32x8 fa0[kFM2], fb0[kFN2], fa1[kFM2], fb1[kFN2];
   int ea, eb, ea_n = 0, eb_n = 0;
+  // Each wave waits for its own loads, then the barrier publishes every
+  // wave's share.  The asm reads one element of each accumulator: the MFMAs
+  // touch no memory, and without that data dependence the compiler moves
+  // most of a step's MFMAs past the wait they are meant to hide.
+#define F8W_SYNC(VM)                                                                           \
+  asm volatile("s_waitcnt vmcnt(" #VM ") lgkmcnt(0)\n\ts_barrier"                             \
+               :: "a"(acc[0][0][0]), "a"(acc[0][1][0]), "a"(acc[0][2][0]), "a"(acc[0][3][0]),  \
+                  "a"(acc[1][0][0]), "a"(acc[1][1][0]), "a"(acc[1][2][0]), "a"(acc[1][3][0]),  \
+                  "a"(acc[2][0][0]), "a"(acc[2][1][0]), "a"(acc[2][2][0]), "a"(acc[2][3][0]),  \
+                  "a"(acc[3][0][0]), "a"(acc[3][1][0]), "a"(acc[3][2][0]), "a"(acc[3][3][0])   \
+               : "memory")
+  static_assert(kFM2 == 4 && kFN2 == 4, "the barrier names each of the 16 accumulators");
   F8W_ISSUE(0, 0);
   if (KT > 1) {
     F8W_ISSUE(1, 1);
-    asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");   // slab 0 landed
+    F8W_SYNC(18);   // slab 0 landed
   } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    F8W_SYNC(0);
   }
   // Slab kt is in buffer kt & 1 and slab kt + 1 on its way into the other;
   // step 0's fragments and the slab's exponents were read after the barrier
-  // that published slab kt.  Step 1's reads go under step 0's MFMAs; then
-  // the barrier (slab kt + 1 landed, slab kt read by every wave), the loads
-  // of slab kt + 2 into the buffer just freed, and the reads of slab kt + 1's
-  // step 0 under step 1's MFMAs.  (Half-slabs in four buffers, loaded three
-  // ahead, measured 1.6 times slower: twice the barriers.)  Compiled once
-  // per count of the wave's live 32-row blocks (same barriers in every copy).
+  // that published slab kt.  Step 1's reads go out, then step 0's MFMAs;
+  // then the barrier (slab kt + 1 landed, slab kt read by every wave), the
+  // loads of slab kt + 2 into the buffer just freed, the reads of slab
+  // kt + 1's step 0 and step 1's MFMAs.  The last two slabs are peeled off,
+  // so the body has no branch the compiler could move MFMAs across.
+  // (Half-slabs in four buffers, loaded three ahead, measured 1.6 times
+  // slower.)  Compiled once per count of the wave's live 32-row blocks (the
+  // same barriers in every copy).
+#define F8W_SLAB(NBK, ISSUE)                                                                   \
+  {                                                                                            \
+    const int buf = kt & 1;                                                                    \
+    READK8(fa1, fb1, buf, 1, NBK);                                                             \
+    mfma8_rows<0, NBK>(acc, fa0, fb0, ea, eb);                                                 \
+    F8W_SYNC(0);                                                                               \
+    if (ISSUE) F8W_ISSUE(kt + 2, buf);                                                         \
+    READK8(fa0, fb0, buf ^ 1, 0, NBK);                                                         \
+    READE(ea_n, eb_n, buf ^ 1);                                                                \
+    mfma8_rows<0, NBK>(acc, fa1, fb1, ea, eb);                                                 \
+    ea = ea_n;                                                                                 \
+    eb = eb_n;                                                                                 \
+  }
 #define F8W_LOOP(NBK)                                                                          \
   {                                                                                            \
     READK8(fa0, fb0, 0, 0, NBK);                                                               \
     READE(ea, eb, 0);                                                                          \
-    for (int kt = 0; kt < KT; ++kt) {                                                          \
-      const int buf = kt & 1;                                                                  \
-      READK8(fa1, fb1, buf, 1, NBK);                                                           \
-      mfma8_rows<0, NBK>(acc, fa0, fb0, ea, eb);                                               \
-      if (kt + 1 < KT) {                                                                       \
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");               \
-        if (kt + 2 < KT) F8W_ISSUE(kt + 2, buf);                                               \
-        READK8(fa0, fb0, buf ^ 1, 0, NBK);                                                     \
-        READE(ea_n, eb_n, buf ^ 1);                                                            \
-      }                                                                                        \
-      mfma8_rows<0, NBK>(acc, fa1, fb1, ea, eb);                                               \
-      ea = ea_n;                                                                               \
-      eb = eb_n;                                                                               \
+    int kt = 0;                                                                                \
+    for (; kt + 2 < KT; ++kt) F8W_SLAB(NBK, true)                                              \
+    if (kt + 1 < KT) {                                                                         \
+      F8W_SLAB(NBK, false)                                                                     \
+      ++kt;                                                                                    \
     }                                                                                          \
+    READK8(fa1, fb1, kt & 1, 1, NBK);                                                          \
+    mfma8_rows<0, NBK>(acc, fa0, fb0, ea, eb);                                                 \
+    mfma8_rows<0, NBK>(acc, fa1, fb1, ea, eb);                                                 \
   }
   const int live = (rows - wm * kWTM2 + 31) / 32;  // wave-uniform
   if (live >= kFM2) F8W_LOOP(kFM2)
@@ -1148,9 +1192,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
   else if (live == 1) F8W_LOOP(1)
   else F8W_LOOP(0)
 #undef F8W_LOOP
+#undef F8W_SLAB
+#undef F8W_SYNC
 #undef READE
 #undef READK8
 #undef F8W_ISSUE
+#undef LDS_ADDR
   const uint64_t any_bad = __ballot(bad != 0u);
   if (any_bad != 0u && lane == 0) atomicOr(status, kFlagScaleFormat);
   wide_epilogue<GLU>(acc, lds, rows, row0, n0, N, Y, wm, wn, lane, tid);
