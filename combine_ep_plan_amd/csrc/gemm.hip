@@ -1158,16 +1158,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
   // (Half-slabs in four buffers, loaded three ahead, measured 1.6 times
   // slower.)  Compiled once per count of the wave's live 32-row blocks (the
   // same barriers in every copy).
+#define SGB8(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
+// before the barrier: one LDS read after each MFMA
+#define F8W_INTERLEAVE_A(NBK)                                                                  \
+  if constexpr ((NBK) == kFM2) {                                                               \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) { SGB8(0x008, 1); SGB8(0x100, 1); }      \
+  }
+// after it: three LDS reads after each of the first 8 MFMAs, then the
+// exponent arithmetic spread over the last 8
+#define F8W_INTERLEAVE_B(NBK)                                                                  \
+  if constexpr ((NBK) == kFM2) {                                                               \
+    _Pragma("unroll") for (int q_ = 0; q_ < 8; ++q_) { SGB8(0x008, 1); SGB8(0x100, 3); }       \
+    _Pragma("unroll") for (int q_ = 0; q_ < 8; ++q_) { SGB8(0x008, 1); SGB8(0x002, 6); }       \
+  }
 #define F8W_SLAB(NBK, ISSUE)                                                                   \
   {                                                                                            \
     const int buf = kt & 1;                                                                    \
     READK8(fa1, fb1, buf, 1, NBK);                                                             \
     mfma8_rows<0, NBK>(acc, fa0, fb0, ea, eb);                                                 \
+    F8W_INTERLEAVE_A(NBK);                                                                     \
     F8W_SYNC(0);                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
     if (ISSUE) F8W_ISSUE(kt + 2, buf);                                                         \
     READK8(fa0, fb0, buf ^ 1, 0, NBK);                                                         \
     READE(ea_n, eb_n, buf ^ 1);                                                                \
     mfma8_rows<0, NBK>(acc, fa1, fb1, ea, eb);                                                 \
+    F8W_INTERLEAVE_B(NBK);                                                                     \
     ea = ea_n;                                                                                 \
     eb = eb_n;                                                                                 \
   }
@@ -1193,6 +1209,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_256(
   else F8W_LOOP(0)
 #undef F8W_LOOP
 #undef F8W_SLAB
+#undef F8W_INTERLEAVE_A
+#undef F8W_INTERLEAVE_B
+#undef SGB8
 #undef F8W_SYNC
 #undef READE
 #undef READK8
@@ -1232,11 +1251,10 @@ static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
 }
 
 // The FP8 256 x 256 kernel needs power-of-two scales (the group's format)
-// and pays off from about 512 rows per expert on average (with fewer, the
-// 128 x 128 kernel's two workgroups per CU stream short groups' weights
-// faster); its buffer offsets over a tile's codes are 32-bit as well.
+// and at least 128 rows per expert on average; its buffer offsets over a
+// tile's codes are 32-bit as well.
 static bool gemm_fp8_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
-  return g.fp8_pow2 && N >= kBN2 && g.n >= (int64_t)(2 * kBM2) * g.E &&
+  return g.fp8_pow2 && N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E &&
          (int64_t)kBM2 * K <= INT32_MAX;
 }
 

@@ -40,7 +40,7 @@ def pow2_scales(rng, shape, lo, hi):
 
 
 # name, T, E, k, layout, cap, R, S, mode, K, N, skew, seed, use_slots
-# (the first ones have at least 512 rows per expert on average and N >= 256:
+# (the first ones have at least 128 rows per expert on average and N >= 256:
 # the 256 x 256 kernel; the last two the 128 x 128 kernel in the same format)
 CASES = [
     ("wide_ht", 2000, 8, 4, "ht", 0, 1, 0, "training", 384, 320, 1.0, 31, False),
