@@ -129,16 +129,19 @@ def draw_gemm(seed: int) -> dict:
                 skew=float(rng.choice([0.0, 1.5])), slots=bool(kind == "static" and S > 0 and rng.random() < 0.7))
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fp8", [False, True, "pow2"], ids=["bf16", "fp8", "fp8_pow2"])
 @pytest.mark.parametrize("seed", range(N_GEMM))
 def test_random_grouped_gemm(seed, fp8):
+    """bf16, FP8 with any fp32 scales, and FP8 in the power-of-two scale
+    format (groups with enough rows per expert and N >= 256 run the 256 x 256
+    kernel whose matrix cores apply the scales)."""
     from tests.test_gpu_gemm import check_gemm
     from tests.test_gpu_gemm_fp8 import check_gemm_fp8, dev_u8, finite_codes, host_u8
     c = draw_gemm(seed)
     print(f"[random gemm] fp8={fp8} {c}", flush=True)
     E, R, k, kind, T, cap, S, K, N = c["E"], c["R"], c["k"], c["kind"], c["T"], c["cap"], c["S"], c["K"], c["N"]
     idx, _, _ = workloads.random_case(6000 + seed, T, 8, E, k, skew=c["skew"])
-    g = make_group(E, R, 8, k, T, kind, cap, S, c["mode"])
+    g = make_group(E, R, 8, k, T, kind, cap, S, c["mode"], fp8_scales="pow2" if fp8 == "pow2" else "amax")
     h = ep.Handle(g, T)
     h.plan(dev_i32(idx))
     slot_mode = oracle.SLOTS_INFERENCE if c["mode"] == "inference" else oracle.SLOTS_TRAINING
@@ -164,9 +167,15 @@ def test_random_grouped_gemm(seed, fp8):
     else:
         NB = K // 128
         x = finite_codes(rng, (L.rows, K))
-        sx = (rng.random((L.rows, NB)) * 2.0 ** -3).astype(np.float32)
+        if fp8 == "pow2":
+            sx = np.ldexp(1.0, rng.integers(-9, -2, (L.rows, NB))).astype(np.float32)
+        else:
+            sx = (rng.random((L.rows, NB)) * 2.0 ** -3).astype(np.float32)
         w = finite_codes(rng, (E, N, K))
-        sw = (rng.random((E, N, NB)) * 2.0 ** -8).astype(np.float32)
+        if fp8 == "pow2":
+            sw = np.ldexp(1.0, rng.integers(-12, -7, (E, N, NB))).astype(np.float32)
+        else:
+            sw = (rng.random((E, N, NB)) * 2.0 ** -8).astype(np.float32)
         wt, swt = dev_u8(w), dev_f32(sw)
         slots = slot_sc = None
         if c["slots"]:
@@ -182,6 +191,7 @@ def test_random_grouped_gemm(seed, fp8):
             sw_all = np.concatenate([sw, host(slot_sc).reshape(R * S, N, NB)])
         ref = oracle.grouped_gemm_fp8(x, sx, w_all, sw_all, groups, np.full((L.rows, N), SENT, np.uint16))
         check_gemm_fp8(host_bits(y), ref, x, sx, w_all, sw_all, groups)
+        assert h.status() == L.flags, "only the layout's own flags: no scale-format flag"
     covered = np.zeros(L.rows, bool)
     for r0, n, _ in groups:
         covered[r0:r0 + n] = True
