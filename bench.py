@@ -107,6 +107,23 @@ def parse():
 PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
 
 
+def median_step_ms(run_step, K, stream):
+    """Median of K more steps, each bracketed by events.  An event record
+    costs host time (about 3 us here), which a launch-bound step would pay
+    inside its own time, so this pass gives the median only; ms_per_step comes
+    from K steps back to back between two events."""
+    import torch
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for i in range(K):
+        run_step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    lst = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(K))
+    return lst[K // 2] if K % 2 else 0.5 * (lst[K // 2 - 1] + lst[K // 2])
+
+
 def gemm_report(ab, name, us, grows, mats, N, K, n_out, fp8, epilogue):
     """Flops, algorithmic bytes (X, every weight matrix used and Y, once each;
     stored in ab[name]) and the roofline of one grouped GEMM launch."""
@@ -325,15 +342,12 @@ def run_microbatches(a):
         assert h.status() == 0, "device flags raised on the benchmark input"
     K = a.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]
     torch.cuda.synchronize()
     e0.record(main_stream)
     if a.overlap:
         fork()
     for i in range(K):
         step()
-        if i < K - 1 and not a.overlap:
-            marks[i].record(main_stream)
     if a.overlap:
         join()
     e1.record(main_stream)
@@ -342,9 +356,7 @@ def run_microbatches(a):
     if a.overlap:
         median_ms = None   # the streams run free between the fork and the join
     else:
-        bounds = [e0] + marks + [e1]
-        step_list = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(K))
-        median_ms = step_list[K // 2] if K % 2 else 0.5 * (step_list[K // 2 - 1] + step_list[K // 2])
+        median_ms = median_step_ms(step, K, main_stream)
 
     # per-kernel durations: micro-batch 0's launches one by one on the main
     # stream (nothing beside them), for the roofline of the dominant kernel
@@ -615,19 +627,14 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_host = time.perf_counter()
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]
         e0.record(stream)
         for i in range(K):
             run_step()
-            if i < K - 1:
-                marks[i].record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
         t_host = time.perf_counter() - t_host
         step_ms = e0.elapsed_time(e1) / K
-        bounds = [e0] + marks + [e1]
-        step_list = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(K))
-        median_ms = step_list[K // 2] if K % 2 else 0.5 * (step_list[K // 2 - 1] + step_list[K // 2])
+        median_ms = median_step_ms(run_step, K, stream)
     else:
         tot = 0.0
         steps_cold = []
