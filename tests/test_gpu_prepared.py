@@ -63,7 +63,11 @@ def test_prepared_chain_matches_plain_calls_and_follows_new_data(c):
     p()   # twice: the handshake words of the layout carry no state between calls
     torch.cuda.synchronize()
     assert h.status() == 0
-    assert np.array_equal(host_bits(recv), recv_plain)
+    # receive rows no entry uses (LL capacity rows) are never written: the
+    # plain run left whatever the allocation held there, so compare used rows
+    L1 = oracle.layout(idx1, E, kind, cap=cap, R=R, S=S)
+    used1 = L1.dst[L1.dst >= 0]
+    assert np.array_equal(host_bits(recv).reshape(L1.rows, H)[used1], recv_plain.reshape(L1.rows, H)[used1])
     assert np.array_equal(host_bits(y), y_plain)
     # a new batch written in place into the same tensors
     idx.copy_(dev_i32(idx2))
