@@ -31,7 +31,7 @@ __all__ = [
     "ep_handle_status", "ep_route", "ep_route_plan", "ep_plan", "ep_dispatch", "ep_plan_dispatch",
     "ep_quantize_fp8", "ep_combine", "ep_combine_bwd", "prepare", "Prepared",
     "ep_dup_grad_reduce", "ep_prefetch_replicas", "ep_expert_gemm", "ep_expert_gemm_fp8",
-    "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu",
+    "ep_expert_gemm_swiglu", "ep_expert_gemm_fp8_swiglu", "ep_run_calls", "ep_call_t",
     "SLOTS_TRAINING",
     "SLOTS_INFERENCE",
     "STORES_AUTO", "STORES_CACHED", "STORES_STREAMING", "FP8_SCALES_AMAX", "FP8_SCALES_POW2",
@@ -75,6 +75,17 @@ class ep_group_config_t(ctypes.Structure):
                 ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32),
                 ("dispatch_stores", c_int32), ("passes_in_flight", c_int32),
                 ("fp8_scales", c_int32)]
+
+
+class ep_call_t(ctypes.Structure):
+    """One recorded call for ep_run_calls: op, integer argument, pointers."""
+    _fields_ = [("op", c_int32), ("i0", c_int32), ("p", c_void_p * 9)]
+
+
+_OPS = {"ep_route": 1, "ep_route_plan": 2, "ep_plan": 3, "ep_dispatch": 4, "ep_plan_dispatch": 5,
+        "ep_quantize_fp8": 6, "ep_combine": 7, "ep_combine_bwd": 8, "ep_dup_grad_reduce": 9,
+        "ep_prefetch_replicas": 10, "ep_expert_gemm": 11, "ep_expert_gemm_swiglu": 12,
+        "ep_expert_gemm_fp8": 13, "ep_expert_gemm_fp8_swiglu": 14}
 
 
 class ep_handle_view_t(ctypes.Structure):
@@ -132,6 +143,7 @@ def load_library():
         "ep_expert_gemm_fp8": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
         "ep_expert_gemm_swiglu": (S, [c_void_p, _T, _T, _T, _T, c_void_p]),
         "ep_expert_gemm_fp8_swiglu": (S, [c_void_p, _T, _T, _T, _T, _T, _T, _T, c_void_p]),
+        "ep_run_calls": (S, [POINTER(ep_call_t), c_int32, POINTER(c_int32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -211,20 +223,36 @@ def _enqueue(name: str, *args) -> None:
 
 
 class Prepared:
-    """Library calls with their arguments marshalled once (see prepare).  It
-    holds references to the tensors and streams the calls name; their storage
-    must not be moved (no resize or reallocation) while it is in use."""
+    """Library calls with their arguments marshalled once (see prepare),
+    replayed by one ep_run_calls call.  It holds references to the tensors,
+    views and streams the calls name; the tensors' storage must not be moved
+    (no resize or reallocation) while it is in use."""
 
     def __init__(self, calls, keep):
         self.calls = tuple(calls)
         self.names = tuple(n for _, _, n in self.calls)
         self._keep = tuple(keep)
+        n = len(self.calls)
+        self._arr = (ep_call_t * max(n, 1))()
+        for k, (_, args, name) in enumerate(self.calls):
+            c = self._arr[k]
+            c.op = _OPS[name]
+            m = 0
+            for a in args:
+                if isinstance(a, (c_int32, int)):   # ep_quantize_fp8's scale format
+                    c.i0 = a.value if isinstance(a, c_int32) else int(a)
+                    continue
+                c.p[m] = None if a is None else ctypes.cast(a, c_void_p).value
+                m += 1
+        self._n = c_int32(n)
+        self._failed = c_int32(0)
+        self._run = load_library().ep_run_calls
 
     def __call__(self) -> None:
-        for fn, args, name in self.calls:
-            code = fn(*args)
-            if code != 0:
-                raise EpError(code, name)
+        code = self._run(self._arr, self._n, ctypes.byref(self._failed))
+        if code != 0:
+            raise EpError(code, self.names[self._failed.value] if self._failed.value < len(self.names)
+                          else "ep_run_calls")
 
 
 def prepare(fn) -> Prepared:
@@ -246,6 +274,16 @@ def prepare(fn) -> Prepared:
 # ---------------------------------------------------------------------------
 # one-to-one wrappers of the C entry points
 # ---------------------------------------------------------------------------
+
+def ep_run_calls(calls, n: int) -> int:
+    """Makes n recorded calls (a ctypes array of ep_call_t) in one entry into
+    the library; raises at the first that fails and returns n otherwise."""
+    failed = c_int32(0)
+    code = load_library().ep_run_calls(calls, int(n), ctypes.byref(failed))
+    if code != 0:
+        raise EpError(code, f"ep_run_calls (call {failed.value})")
+    return failed.value
+
 
 def ep_status_string(code: int) -> str:
     return load_library().ep_status_string(int(code)).decode()
@@ -348,7 +386,7 @@ def ep_plan_dispatch(h: int, topk_idx: torch.Tensor, tokens: torch.Tensor,
 def ep_quantize_fp8(tokens: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None,
                     pow2: bool = False) -> None:
     _enqueue("ep_quantize_fp8", _tensor(tokens, TAG_TOKENS), _tensor(codes, TAG_TOKENS),
-             _tensor(scales, TAG_FP8_SCALES), FP8_SCALES_POW2 if pow2 else FP8_SCALES_AMAX,
+             _tensor(scales, TAG_FP8_SCALES), c_int32(FP8_SCALES_POW2 if pow2 else FP8_SCALES_AMAX),
              _stream(stream))
 
 

@@ -784,4 +784,46 @@ ep_status_t ep_expert_gemm_fp8_swiglu(ep_handle_t h, const ep_tensor_t *recv_tok
                          slot_scales, out, stream, true);
 }
 
+ep_status_t ep_run_calls(const ep_call_t *calls, int32_t n, int32_t *failed) {
+  if (failed != nullptr) *failed = 0;
+  if (n < 0 || (n > 0 && calls == nullptr)) return EP_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const ep_call_t &c = calls[i];
+    const auto h = static_cast<ep_handle_t>(c.p[0]);
+    const auto t = [&c](int k) { return static_cast<ep_tensor_t *>(c.p[k]); };
+    ep_status_t st;
+    switch (c.op) {
+      case EP_OP_ROUTE: st = ep_route(h, t(1), t(2), t(3), c.p[4]); break;
+      case EP_OP_ROUTE_PLAN: st = ep_route_plan(h, t(1), t(2), t(3), c.p[4]); break;
+      case EP_OP_PLAN: st = ep_plan(h, t(1), c.p[2]); break;
+      case EP_OP_DISPATCH: st = ep_dispatch(h, t(1), t(2), t(3), t(4), t(5), t(6), c.p[7]); break;
+      case EP_OP_PLAN_DISPATCH:
+        st = ep_plan_dispatch(h, t(1), t(2), t(3), t(4), t(5), t(6), t(7), c.p[8]);
+        break;
+      case EP_OP_QUANTIZE_FP8: st = ep_quantize_fp8(t(0), t(1), t(2), c.i0, c.p[3]); break;
+      case EP_OP_COMBINE: st = ep_combine(h, t(1), t(2), t(3), c.p[4]); break;
+      case EP_OP_COMBINE_BWD: st = ep_combine_bwd(h, t(1), t(2), t(3), t(4), t(5), c.p[6]); break;
+      case EP_OP_DUP_GRAD_REDUCE: st = ep_dup_grad_reduce(h, t(1), t(2), t(3), c.p[4]); break;
+      case EP_OP_PREFETCH_REPLICAS: st = ep_prefetch_replicas(h, t(1), t(2), c.p[3]); break;
+      case EP_OP_EXPERT_GEMM: st = ep_expert_gemm(h, t(1), t(2), t(3), t(4), c.p[5]); break;
+      case EP_OP_EXPERT_GEMM_SWIGLU:
+        st = ep_expert_gemm_swiglu(h, t(1), t(2), t(3), t(4), c.p[5]);
+        break;
+      case EP_OP_EXPERT_GEMM_FP8:
+        st = ep_expert_gemm_fp8(h, t(1), t(2), t(3), t(4), t(5), t(6), t(7), c.p[8]);
+        break;
+      case EP_OP_EXPERT_GEMM_FP8_SWIGLU:
+        st = ep_expert_gemm_fp8_swiglu(h, t(1), t(2), t(3), t(4), t(5), t(6), t(7), c.p[8]);
+        break;
+      default: st = EP_ERR_INVALID_ARG; break;
+    }
+    if (st != EP_OK) {
+      if (failed != nullptr) *failed = i;
+      return st;
+    }
+  }
+  if (failed != nullptr) *failed = n;
+  return EP_OK;
+}
+
 }  // extern "C"

@@ -548,6 +548,55 @@ ep_status_t ep_expert_gemm_fp8_swiglu(ep_handle_t h, const ep_tensor_t *recv_tok
                                       const ep_tensor_t *slot_scales, ep_tensor_t *out,
                                       void *stream);
 
+/* ------------------------------------------------------------------------
+ * Recorded calls.  A launch-bound loop -- a low-latency decode step, a few
+ * kernels of a few microseconds each (NCCL EP listing, Table III: the LL
+ * mode for batches of 1 to 128 tokens) -- spends about as much host time
+ * entering the library once per operation as the GPU spends on the
+ * operations.  A caller can describe the step's calls once and pass the
+ * whole list to ep_run_calls every step: one entry into the library, the
+ * same work. */
+
+/* The entry point a recorded call makes. */
+typedef enum ep_op {
+  EP_OP_ROUTE = 1,
+  EP_OP_ROUTE_PLAN = 2,
+  EP_OP_PLAN = 3,
+  EP_OP_DISPATCH = 4,
+  EP_OP_PLAN_DISPATCH = 5,
+  EP_OP_QUANTIZE_FP8 = 6,
+  EP_OP_COMBINE = 7,
+  EP_OP_COMBINE_BWD = 8,
+  EP_OP_DUP_GRAD_REDUCE = 9,
+  EP_OP_PREFETCH_REPLICAS = 10,
+  EP_OP_EXPERT_GEMM = 11,
+  EP_OP_EXPERT_GEMM_SWIGLU = 12,
+  EP_OP_EXPERT_GEMM_FP8 = 13,
+  EP_OP_EXPERT_GEMM_FP8_SWIGLU = 14
+} ep_op_t;
+
+/* One recorded call.  p holds the entry point's pointer arguments in its
+ * own order -- the handle first where it takes one, the tensor views (NULL
+ * where the entry point accepts NULL), the stream last; i0 holds its one
+ * integer argument (ep_quantize_fp8's fp8_scales; p is then tokens, codes,
+ * scales, stream).  Slots past the entry point's arguments are ignored. */
+typedef struct ep_call {
+  int32_t op; /* ep_op_t */
+  int32_t i0;
+  void *p[9];
+} ep_call_t;
+
+/* Makes calls[0 .. n-1] in order, each exactly as its entry point would be
+ * called with those arguments (the same checks, kernels and streams), and
+ * stops at the first one that does not return EP_OK.
+ * failed: if not NULL, receives the index of that call, or n.
+ * Returns the failing call's status, or EP_OK.  EP_ERR_INVALID_ARG for
+ * n < 0, for calls == NULL with n > 0, and for a call with an unknown op
+ * (its index in *failed).  The list and everything it points to stay the
+ * caller's and must stay valid during the call; the kernels it enqueues
+ * read the tensors later, as with the entry points themselves. */
+ep_status_t ep_run_calls(const ep_call_t *calls, int32_t n, int32_t *failed);
+
 #ifdef __cplusplus
 }
 #endif

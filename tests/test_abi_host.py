@@ -499,3 +499,43 @@ def test_prepare_records_without_enqueueing():
     with pytest.raises(ValueError, match="on the GPU"):
         ep.prepare(lambda: ep.ep_plan(1, torch.zeros(4, 2, dtype=torch.int32)))
     assert getattr(ep._RECORDING, "calls", None) is None
+
+
+def _calls(*specs):
+    """ep_call_t array from (op, i0, [pointer args]) triples."""
+    arr = (ep.ep_call_t * max(len(specs), 1))()
+    for k, (op, i0, ptrs) in enumerate(specs):
+        arr[k].op, arr[k].i0 = op, i0
+        for m, a in enumerate(ptrs):
+            arr[k].p[m] = None if a is None else ctypes.cast(a, ctypes.c_void_p).value
+    return arr
+
+
+def test_run_calls_validation(lib):
+    failed = ctypes.c_int32(-7)
+    R = lib.ep_run_calls
+    assert R(_calls(), 0, ctypes.byref(failed)) == 0 and failed.value == 0   # nothing to do
+    assert R(None, 0, None) == 0
+    assert R(_calls(), -1, ctypes.byref(failed)) == 1
+    assert R(None, 2, ctypes.byref(failed)) == 1
+    g, h, _ = make_handle(lib)
+    hp = h   # already a c_void_p
+    # an unknown op stops the list at its index
+    assert R(_calls((99, 0, [hp])), 1, ctypes.byref(failed)) == 1 and failed.value == 0
+    # each call returns exactly what its entry point returns: the second call
+    # here is an ep_plan with the wrong tag (EP_ERR_BAD_TAG), so the list
+    # stops there; the first (wrong shape, EP_ERR_BAD_SHAPE) stops it sooner
+    bad_tag = T(I32, ep.TAG_TOKENS, 64, 2)
+    bad_shape = T(I32, ep.TAG_TOPK_IDX, 64, 3)
+    assert lib.ep_plan(h, bad_tag, None) == 2 and lib.ep_plan(h, bad_shape, None) == 4
+    assert R(_calls((3, 0, [hp, bad_tag, None])), 1, ctypes.byref(failed)) == 2 and failed.value == 0
+    assert R(_calls((3, 0, [hp, bad_shape, None]), (3, 0, [hp, bad_tag, None])), 2,
+             ctypes.byref(failed)) == 4 and failed.value == 0
+    # ep_quantize_fp8 takes its scale format from i0: 2 is not a format
+    x = T(BF16, ep.TAG_TOKENS, 4, 256)
+    q = T(FP8, ep.TAG_TOKENS, 4, 256)
+    s = T(F32, ep.TAG_FP8_SCALES, 4, 2)
+    assert R(_calls((6, 2, [x, q, s, None])), 1, ctypes.byref(failed)) == \
+        lib.ep_quantize_fp8(x, q, s, 2, None) == 1
+    lib.ep_handle_destroy(h)
+    lib.ep_group_destroy(g)
