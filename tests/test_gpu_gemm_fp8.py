@@ -146,12 +146,17 @@ CASES = [
 ]
 
 
-def quantised_torch(gen, shape):
+def quantised_torch(gen, shape, pow2=False):
     """Gaussian values quantised as the FP8 dispatch does: e4m3 codes and one
-    fp32 scale per 128 (amax / 448)."""
+    fp32 scale per 128 (amax / 448; with pow2, the smallest power of two at
+    or above it, as a group in the power-of-two format quantises)."""
     v = torch.randn(shape, generator=gen, device="cuda").view(*shape[:-1], shape[-1] // 128, 128)
     amax = v.abs().amax(-1)
     sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    if pow2:
+        b = sc.view(torch.int32)
+        up = torch.where((b & 0x007FFFFF) != 0, (b & 0x7F800000) + 0x00800000, b)
+        sc = torch.where(b < 0x00800000, torch.full_like(b, 0x00800000), up).view(torch.float32)
     q = (v / sc[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).view(shape), sc.contiguous()
 
@@ -273,22 +278,25 @@ def test_grouped_gemm_fp8_repeat_is_deterministic():
 
 
 @pytest.mark.parametrize("use_slots", [False, True])
-def test_grouped_gemm_fp8_training_shapes_sampled(use_slots):
+@pytest.mark.parametrize("fmt", ["amax", "pow2"])
+def test_grouped_gemm_fp8_training_shapes_sampled(use_slots, fmt):
     # training shapes: 16 ranks x 8 experts, [16, 8192, 4096] STATIC rows, one
     # [1536, 4096] projection per expert in FP8 (quantised Gaussian rows and
-    # weights); sampled rows against the oracle
+    # weights); sampled rows against the oracle.  In the power-of-two format
+    # these shapes run the 256 x 256 kernel whose matrix cores apply the scales.
+    print(f"[gemm_fp8] training shapes, slots={use_slots}, scales={fmt}", flush=True)
     inp = workloads.make_inputs("training")
     c = inp.cfg
     K, N, NB = c.H, 1536, c.H // 128
-    g = make_group(c.E, c.R, c.H, c.k, c.T, "static", 0, c.S)
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "static", 0, c.S, fp8_scales=fmt)
     h = ep.Handle(g, c.T)
     h.plan(dev_i32(inp.topk_idx))
     L = oracle.layout(inp.topk_idx, c.E, "static", R=c.R, S=c.S)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(778)
 
-    x, sx = quantised_torch(gen, (L.rows, K))
-    w, sw = quantised_torch(gen, (c.E, N, K))
+    x, sx = quantised_torch(gen, (L.rows, K), pow2=fmt == "pow2")
+    w, sw = quantised_torch(gen, (c.E, N, K), pow2=fmt == "pow2")
     buf = ep.Buffer(g)
     slots = slot_sc = None
     if use_slots:
@@ -327,22 +335,24 @@ def test_grouped_gemm_fp8_training_shapes_sampled(use_slots):
     assert h.status() == 0
 
 
-def test_grouped_gemm_fp8_prefill_shapes_sampled():
+@pytest.mark.parametrize("fmt", ["amax", "pow2"])
+def test_grouped_gemm_fp8_prefill_shapes_sampled(fmt):
     # prefill shapes in FP8: HT, 4096 tokens x top-8 over 256 experts, K = 7168,
     # N = 2048, quantised Gaussian rows and weights; sampled rows of sampled
     # groups, the largest one included
+    print(f"[gemm_fp8] prefill shapes, scales={fmt}", flush=True)
     inp = workloads.make_inputs("prefill")
     c = inp.cfg
     K, N = c.H, 2048
-    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht")
+    g = make_group(c.E, c.R, c.H, c.k, c.T, "ht", fp8_scales=fmt)
     h = ep.Handle(g, c.T)
     h.plan(dev_i32(inp.topk_idx))
     L = oracle.layout(inp.topk_idx, c.E, "ht")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(780)
 
-    x, sx = quantised_torch(gen, (L.rows, K))
-    w, sw = quantised_torch(gen, (c.E, N, K))
+    x, sx = quantised_torch(gen, (L.rows, K), pow2=fmt == "pow2")
+    w, sw = quantised_torch(gen, (c.E, N, K), pow2=fmt == "pow2")
     y = ep.Buffer(g).expert_gemm_fp8(x.view(torch.float8_e4m3fn), sx, w.view(torch.float8_e4m3fn), sw, h)
     torch.cuda.synchronize()
     groups = oracle.expert_groups(L, "ht", c.E)
