@@ -955,16 +955,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
 // 32 K-values the lane holds (A: the lane's row, B: its column), and both
 // 64-deep steps of a 128-deep slab lie in one scale block, so
 // SX[row][b] * SW[col][b] is applied exactly inside the MFMA and the
-// accumulators run over the whole of K with no vector-ALU fold.  What is left
-// is the bf16 wide kernel's loop: the same tiles, waves, LDS geometry (a
-// 128-deep slab of codes is 128 bytes per row, as a 64-deep bf16 slab) and
-// pipelining, with two 64-deep steps per slab instead of four 16-deep ones,
-// so half as many slabs for the same K.  The slab's exponents (one byte per
-// tile row and per tile column) go through LDS beside the codes, packed so a
-// lane reads the exponents of its four row blocks, and of its four column
-// blocks, as one word each; the MFMA's byte select (op_sel) picks them.
+// accumulators run over the whole of K with no vector-ALU fold.  Tiles, waves,
+// XCD order and LDS geometry are the bf16 wide kernel's (a 128-deep slab of
+// codes is 128 bytes per row, as a 64-deep bf16 slab), with two 64-deep steps
+// per slab.  The slabs travel differently: each goes from global memory
+// straight into LDS (buffer loads issued from asm, two buffers), the one
+// after next issued as soon as its buffer is free, with explicit waits before
+// the barrier that publishes a slab.  Each slab's 256 row and 256 column
+// scales go into LDS the same way, as fp32; a lane turns the eight it needs
+// (its four row blocks' and its four column blocks') into exponent bytes
+// packed in two words, and the MFMA's byte select (op_sel) picks them.
 // A scale that is not a positive normal power of two raises
-// EP_FLAG_SCALE_FORMAT (its block is then computed at the scale's exponent).
+// EP_FLAG_SCALE_FORMAT (its block is then computed at 2 to the scale's
+// exponent).
 
 constexpr int kF8KV = kF8Block / 16;   // 16-byte chunks per row of a slab (= kChunks)
 static_assert(kF8KV == kChunks, "an FP8 slab row is 128 bytes, as a bf16 one");
