@@ -252,3 +252,44 @@ def test_expert_ffn_all_fp8_pow2():
     ref2 = bf16_bits_to_f32(oracle.grouped_gemm_fp8(oq, os_, w2, sw2, groups)[rows]).astype(np.float64)
     assert rel_err(got, ref2) <= 2e-3
     assert float(got.ravel() @ ref2.ravel() / (np.linalg.norm(got) * np.linalg.norm(ref2))) > 0.999
+
+
+def test_wide_fp8_gemm_graph_replays_match_eager():
+    """The 256 x 256 FP8 kernel (tile table + GEMM) captured once as a HIP
+    graph; new codes and scales are copied into the captured buffers before
+    each replay, with eager work in between, and every replay must equal the
+    same call made eagerly, bit for bit (the kernel's slab loads and waits are
+    its own, so a replay must see the same pipeline as an eager launch)."""
+    T, E, k, K, N = 2000, 8, 4, 384, 320
+    print(f"[gemm_fp8_pow2] graph replay T={T} E={E} K={K} N={N}", flush=True)
+    idx, _, _ = workloads.random_case(6200, T, 8, E, k, skew=1.0)
+    g = make_group(E, 1, 8, k, T, "ht", fp8_scales="pow2")
+    h = ep.Handle(g, T)
+    h.plan(dev_i32(idx))
+    L = oracle.layout(idx, E, "ht")
+    rng = np.random.default_rng(62)
+    NB = K // 128
+    x = dev_u8(finite_codes(rng, (L.rows, K)))
+    sx = dev_f32(pow2_scales(rng, (L.rows, NB), -8, 2))
+    w = dev_u8(finite_codes(rng, (E, N, K)))
+    sw = dev_f32(pow2_scales(rng, (E, N, NB), -12, -6))
+    y = torch.zeros((L.rows, N), dtype=torch.bfloat16, device="cuda")
+    y_ref = torch.zeros_like(y)
+    call = lambda out, st: ep.ep_expert_gemm_fp8(h.ptr, x, sx, w, sw, None, None, out, st)
+    call(y, None)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(y, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for seed in range(3):
+        x.copy_(dev_u8(finite_codes(rng, (L.rows, K))))
+        sx.copy_(dev_f32(pow2_scales(rng, (L.rows, NB), -8, 2)))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_bits(y).copy()
+        _ = torch.ones(1 << 20, device="cuda").sum()          # eager work between replays
+        call(y_ref, None)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, host_bits(y_ref)), f"replay {seed}"
+        assert h.status() == 0
