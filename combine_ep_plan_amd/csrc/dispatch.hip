@@ -115,18 +115,20 @@ __device__ void fused_place(const FusedLayout &fl, int64_t t, int32_t *s_dst,
     const bool valid = id[c] >= 0 && id[c] < g.E;
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
-      if (K == 0 && j >= k) break;
-      const int64_t fj = t * k + j;
-      pos[j] += __popcll(__ballot(valid && id[c] == ej[j] && f < fj));
-      if (ht) less[j] += __popcll(__ballot(valid && id[c] < ej[j]));
+      if (K > 0 || j < k) {   // a guard, not a break: the loop unrolls fully
+        const int64_t fj = t * k + j;
+        pos[j] += __popcll(__ballot(valid && id[c] == ej[j] && f < fj));
+        if (ht) less[j] += __popcll(__ballot(valid && id[c] < ej[j]));
+      }
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
-      if (K == 0 && j >= k) break;
-      s_cnt[w][0][j] = pos[j];
-      s_cnt[w][1][j] = less[j];
+      if (K > 0 || j < k) {
+        s_cnt[w][0][j] = pos[j];
+        s_cnt[w][1][j] = less[j];
+      }
     }
   }
   __syncthreads();
