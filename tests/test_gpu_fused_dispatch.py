@@ -85,12 +85,14 @@ def _run(g, T, H, idx, w, x, fused, fp8):
     return h, out
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+# every case in bf16; in FP8 those whose hidden size is a multiple of 128
+# (the FP8 format's block), the only sizes the FP8 dispatch accepts
+_PAIRS = [(c, f) for f in (False, True) for c in CASES if not (f and c[2] % 128)]
+
+
+@pytest.mark.parametrize("c,fp8", _PAIRS, ids=[f"{c[0]}-{'fp8' if f else 'bf16'}" for c, f in _PAIRS])
 def test_plan_dispatch_matches_oracle_and_two_calls(c, fp8):
     T, H, E, k, kind, cap, R, S, idx, w, x = _inputs(c)
-    if fp8 and H % 128:
-        pytest.skip("FP8 needs H % 128 == 0")
     print(f"[plan_dispatch] {c[0]} fp8={fp8} T={T} E={E} k={k}", flush=True)
     g = make_group(E, R, H, k, T, kind, cap, S)
     h, got = _run(g, T, H, idx, w, x, True, fp8)
