@@ -63,6 +63,10 @@ def parse():
     p.add_argument("--dispatch-stores", choices=("auto", "cached", "streaming"), default="auto",
                    help="how dispatch writes the receive rows (default: cached for 64 MiB to "
                         "512 MiB of rows, non-temporal otherwise)")
+    p.add_argument("--combine-stores", choices=("auto", "cached", "streaming"), default=None,
+                   help="how combine writes its token rows (default: streaming for the training "
+                        "step, whose backward pass streams far more than the Infinity Cache "
+                        "holds; the library's default, cached, otherwise)")
     p.add_argument("--slot-mode", choices=("training", "inference"), default="training",
                    help="STATIC workloads: what the plan does past a rank's S-th replica slot")
     p.add_argument("--slots", type=int, default=None,
@@ -101,7 +105,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                    help="only run a plain device copy of MB megabytes K times (counter scaling)")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.combine_stores is None:
+        a.combine_stores = "streaming" if a.workload == "training" else "auto"
+    return a
 
 
 PREFETCH_P = 4096 * 1536   # elements of one expert projection (training shapes)
@@ -273,7 +280,8 @@ def run_microbatches(a):
     # overlapped micro-batches are passes in flight together: the library's
     # default store rule counts their receive rows together
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=c.S,
-                 dispatch_stores=a.dispatch_stores, passes_in_flight=M if a.overlap else 1)
+                 dispatch_stores=a.dispatch_stores, passes_in_flight=M if a.overlap else 1,
+                 combine_stores=a.combine_stores)
     streams = [torch.cuda.Stream() for _ in range(M)] if a.overlap else [main_stream] * M
     fused = c.layout in ("ll", "ht") and c.T * c.k <= 2048 and not a.two_call_dispatch
     mbs = []
@@ -409,6 +417,7 @@ def run_microbatches(a):
                                f"{'overlapped on ' + str(M) + ' streams' if a.overlap else 'in turn on one stream'}",
                    "T": c.T, "H": c.H, "E": c.E, "top_k": c.k, "layout": c.layout,
                    "microbatches": M, "overlap": a.overlap, "dispatch_stores": a.dispatch_stores,
+                   "combine_stores": a.combine_stores,
                    "step": " -> ".join(nm for nm, _ in mbs[0][1]) + f" (x{M})",
                    "prepared_calls": not a.no_prepare},
         "hbm_gbps": round(chain_bytes / step_s / 1e9, 1),
@@ -473,7 +482,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     g = ep.Group(c.E, c.R, c.H, c.k, c.T, c.layout, capacity=c.cap, slots_per_rank=S,
-                 slot_mode=a.slot_mode, dispatch_stores=a.dispatch_stores, fp8_scales=a.fp8_scales)
+                 slot_mode=a.slot_mode, dispatch_stores=a.dispatch_stores, fp8_scales=a.fp8_scales,
+                 combine_stores=a.combine_stores)
     h = ep.Handle(g, c.T)
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(inp.topk_idx).to(dev)
@@ -721,7 +731,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "T": c.T, "H": c.H, "E": c.E, "top_k": c.k,
                    "layout": c.layout, "ranks": c.R, "cold_cache": a.cold,
-                   "dispatch_stores": a.dispatch_stores,
+                   "dispatch_stores": a.dispatch_stores, "combine_stores": a.combine_stores,
                    "step": " -> ".join(nm for nm, _ in ops), "from_logits": a.route or a.fused_route,
                    "hip_graph": a.graph, "prepared_calls": not a.graph and not a.no_prepare,
                    "fp8_scales": a.fp8_scales if a.fp8 else None},

@@ -74,7 +74,7 @@ class ep_group_config_t(ctypes.Structure):
                 ("top_k", c_int32), ("max_tokens", c_int32), ("layout", c_int32),
                 ("capacity", c_int32), ("slots_per_rank", c_int32), ("slot_mode", c_int32),
                 ("dispatch_stores", c_int32), ("passes_in_flight", c_int32),
-                ("fp8_scales", c_int32)]
+                ("fp8_scales", c_int32), ("combine_stores", c_int32)]
 
 
 class ep_call_t(ctypes.Structure):
@@ -465,14 +465,15 @@ class Group:
                  max_tokens: int, layout: str | int = "ht", capacity: int = 0,
                  slots_per_rank: int = 0, slot_mode: str | int = "training",
                  dispatch_stores: str | int = "auto", passes_in_flight: int = 1,
-                 fp8_scales: str | int = "amax"):
+                 fp8_scales: str | int = "amax", combine_stores: str | int = "auto"):
         self.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
         mode = _SLOT_MODES[slot_mode] if isinstance(slot_mode, str) else int(slot_mode)
         stores = _STORES[dispatch_stores] if isinstance(dispatch_stores, str) else int(dispatch_stores)
         f8 = _FP8_SCALES[fp8_scales] if isinstance(fp8_scales, str) else int(fp8_scales)
+        cstores = _STORES[combine_stores] if isinstance(combine_stores, str) else int(combine_stores)
         self.cfg = ep_group_config_t(num_experts, num_ranks, hidden, top_k, max_tokens,
                                      self.layout, capacity, slots_per_rank, mode, stores,
-                                     passes_in_flight, f8)
+                                     passes_in_flight, f8, cstores)
         self.ptr = ep_group_create(self.cfg)
 
     @property

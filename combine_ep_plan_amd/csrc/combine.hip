@@ -8,7 +8,11 @@
 // Each lane owns 8 channels (one 16-byte vector)
 // and keeps all k gathers of its vector in flight before reducing them in
 // fp32 in ascending j, so the k rows of a token cost one HBM read each and
-// the output one HBM write.
+// the output one HBM write.  The output rows are written cached (the next
+// layer finds them in the Infinity Cache) or, as the group asks,
+// non-temporally.  Combine backward reads each token's gradient row once, so
+// it reads it non-temporally, like the expert rows (a training step
+// measured faster so).
 #include "device.h"
 #include "ep_internal.h"
 
@@ -16,7 +20,7 @@ namespace epk {
 
 constexpr int kRowThreads = 512;
 
-template <int K, bool WEIGHTED, bool OUT_F32>
+template <int K, bool WEIGHTED, bool OUT_F32, bool NT>
 __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict__ rows,
                                                          const int32_t *__restrict__ dst,
                                                          const float *__restrict__ w,
@@ -54,10 +58,18 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
     }
     if constexpr (OUT_F32) {
       f32x4 *o = reinterpret_cast<f32x4 *>(out) + (t * V + v) * 2;
-      o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      const f32x4 lo4{acc[0], acc[1], acc[2], acc[3]}, hi4{acc[4], acc[5], acc[6], acc[7]};
+      if constexpr (NT) {
+        store_stream(o, lo4);
+        store_stream(o + 1, hi4);
+      } else {
+        o[0] = lo4;
+        o[1] = hi4;
+      }
     } else {
-      reinterpret_cast<u32x4 *>(out)[t * V + v] = pack8(acc);
+      u32x4 *o = reinterpret_cast<u32x4 *>(out) + t * V + v;
+      if constexpr (NT) store_stream(o, pack8(acc));
+      else *o = pack8(acc);
     }
   }
 }
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_bwd(const u32x4 *__rest
   }
   for (int32_t v = threadIdx.x; v < V; v += kRowThreads) {
     float g[8];
-    unpack8(gy[t * V + v], g);
+    unpack8(load_stream(gy + t * V + v), g);
     u32x4 r[KN];
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
@@ -136,9 +148,15 @@ hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t
   const u32x4 *r = reinterpret_cast<const u32x4 *>(rows);
   int32_t chunk = V;
   const int32_t pieces = row_pieces(g.T, V, &chunk);
-#define L4(KK, WT, OF)                                                                        \
-  hipLaunchKernelGGL((k_combine<KK, WT, OF>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, r, \
+  const bool nt = g.cstores == 2;
+#define L5(KK, WT, OF, NT)                                                                        \
+  hipLaunchKernelGGL((k_combine<KK, WT, OF, NT>), dim3(g.T, pieces), dim3(kRowThreads), 0, s, r, \
                      ws.dst, topk_w, out, g.rows, V, g.k, chunk)
+#define L4(KK, WT, OF)         \
+  do {                         \
+    if (nt) L5(KK, WT, OF, true); \
+    else L5(KK, WT, OF, false);   \
+  } while (0)
 #define L(KK)                           \
   do {                                  \
     if (topk_w) {                       \
@@ -152,6 +170,7 @@ hipError_t launch_combine(const Geometry &g, const Workspace &ws, const uint16_t
   EP_K_SWITCH(g.k, L)
 #undef L
 #undef L4
+#undef L5
   return hipGetLastError();
 }
 

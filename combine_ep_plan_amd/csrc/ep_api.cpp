@@ -52,6 +52,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.slot_mode = c.slot_mode;
   geo.stores = c.dispatch_stores;
   geo.in_flight = c.passes_in_flight > 1 ? c.passes_in_flight : 1;
+  geo.cstores = c.combine_stores;
   geo.fp8_pow2 = c.fp8_scales == EP_FP8_SCALES_POW2 ? 1 : 0;
   geo.layout = c.layout;
   geo.cap = c.capacity;
@@ -205,6 +206,8 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
   if (c.dispatch_stores < EP_STORES_AUTO || c.dispatch_stores > EP_STORES_STREAMING)
     return EP_ERR_INVALID_ARG;
   if (c.passes_in_flight < 0 || c.passes_in_flight > 64) return EP_ERR_INVALID_ARG;
+  if (c.combine_stores < EP_STORES_AUTO || c.combine_stores > EP_STORES_STREAMING)
+    return EP_ERR_INVALID_ARG;
   if (c.fp8_scales != EP_FP8_SCALES_AMAX && c.fp8_scales != EP_FP8_SCALES_POW2) return EP_ERR_INVALID_ARG;
   if (c.slot_mode != EP_SLOTS_TRAINING &&
       !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))

@@ -64,6 +64,7 @@ struct Geometry {
   int32_t slot_mode;  // 0 training (overflow flags SLOT_BUDGET), 1 inference
   int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
   int32_t in_flight;  // passes of the group at once (>= 1): the size rule counts all their rows
+  int32_t cstores;    // combine's token rows: 0 or 1 cached, 2 non-temporal
   int32_t fp8_pow2;   // FP8 scales are powers of two (EP_FP8_SCALES_POW2)
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)

@@ -131,6 +131,14 @@ typedef enum ep_dispatch_stores {
   EP_STORES_STREAMING = 2  /* non-temporal */
 } ep_dispatch_stores_t;
 
+/* How ep_combine writes the token rows it outputs (weighted, and with NULL
+ * weights as the backward of dispatch), with the same three values.  AUTO
+ * and CACHED leave the rows in the Infinity Cache, where the next layer,
+ * which reads them, finds them.  STREAMING writes them non-temporally: a
+ * caller whose next kernels stream much more than the cache holds (a
+ * training step's backward pass) takes it, since the rows would otherwise be
+ * written back while those kernels run. */
+
 /* Format of the fp32 scales of FP8 rows (one per row and 128 channels).
  * The pages fix only that FP8 rows travel with scales (NCCL EP listing,
  * Table IV); both formats are readings.  AMAX: scale = amax / 448, the
@@ -174,6 +182,7 @@ typedef struct ep_group_config {
                                on several streams); 0 or 1 = one.  EP_STORES_AUTO weighs the
                                receive rows of all of them against the Infinity Cache. */
   int32_t fp8_scales;      /* ep_fp8_scales_t: FP8 dispatch scales and the FP8 GEMM's path */
+  int32_t combine_stores;  /* ep_dispatch_stores_t: how ep_combine writes its token rows */
 } ep_group_config_t;
 
 typedef struct ep_group *ep_group_t;

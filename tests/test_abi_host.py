@@ -56,7 +56,7 @@ def test_status_strings(lib):
 def cfg(**kw):
     base = dict(num_experts=8, num_ranks=4, hidden=256, top_k=2, max_tokens=64,
                 layout=ep.LAYOUT_HT, capacity=0, slots_per_rank=0, slot_mode=0, dispatch_stores=0,
-                passes_in_flight=0, fp8_scales=0)
+                passes_in_flight=0, fp8_scales=0, combine_stores=0)
     base.update(kw)
     return ep.ep_group_config_t(*[base[f] for f, _ in ep.ep_group_config_t._fields_])
 
@@ -74,6 +74,7 @@ def create(lib, **kw):
     dict(layout=ep.LAYOUT_STATIC, slot_mode=2), dict(layout=ep.LAYOUT_STATIC, slot_mode=-1),
     dict(dispatch_stores=3), dict(dispatch_stores=-1), dict(passes_in_flight=-1),
     dict(passes_in_flight=65), dict(fp8_scales=2), dict(fp8_scales=-1),
+    dict(combine_stores=3), dict(combine_stores=-1),
     dict(slot_mode=ep.SLOTS_INFERENCE),               # the inference slot mode is STATIC only
     dict(layout=ep.LAYOUT_STATIC, num_experts=1024, num_ranks=1024, slots_per_rank=1 << 22),
 ])
@@ -82,9 +83,10 @@ def test_group_config_validation(lib, bad):
     assert rc == 1  # EP_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("field", ["dispatch_stores", "combine_stores"])
 @pytest.mark.parametrize("stores", [ep.STORES_AUTO, ep.STORES_CACHED, ep.STORES_STREAMING])
-def test_group_accepts_each_dispatch_store_kind(lib, stores):
-    rc, g = create(lib, dispatch_stores=stores)
+def test_group_accepts_each_store_kind(lib, field, stores):
+    rc, g = create(lib, **{field: stores})
     assert rc == 0
     lib.ep_group_destroy(g)
 

@@ -365,3 +365,33 @@ def test_dispatch_store_kinds_give_identical_rows(fp8):
     for o in outs:
         for a, b in zip(o, want):
             assert np.array_equal(a, b)
+
+
+def test_combine_store_kinds_give_identical_rows():
+    # the group's combine_stores choice changes only how the token rows are
+    # written: weighted (bf16 and fp32 out) and unit-weight combines give the
+    # same bytes with cached, non-temporal and default stores
+    T, H, E, k = 700, 512, 32, 4
+    idx, w, _ = workloads.random_case(4343, T, H, E, k, skew=1.0)
+    L = oracle.layout(idx, E, "ht")
+    rng = np.random.default_rng(4343)
+    eo_bits = workloads.f32_to_bf16_bits(rng.standard_normal((L.rows, H)).astype(np.float32))
+    outs = []
+    for stores in ("auto", "cached", "streaming"):
+        g = ep.Group(E, 4, H, k, T, "ht", combine_stores=stores)
+        h = ep.Handle(g, T)
+        h.plan(dev_i32(idx))
+        buf = ep.Buffer(g)
+        eo = dev_bf16(eo_bits)
+        y16 = buf.combine(eo, h, dev_f32(w))
+        y32 = buf.combine(eo, h, dev_f32(w), out_dtype=torch.float32)
+        gx = buf.dispatch_bwd(eo, h)
+        torch.cuda.synchronize()
+        outs.append((host_bits(y16), host(y32).view(np.uint32), host_bits(gx)))
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert np.array_equal(a, b)
+    ref = oracle.combine(eo_bits, L.dst, w, out_fp32=True)
+    assert rel_err(outs[0][1].view(np.float32), ref) <= COMBINE_TOL
+    ref = oracle.combine(eo_bits, L.dst, None)
+    assert rel_err(bf16_bits_to_f32(outs[0][2]), bf16_bits_to_f32(ref)) <= COMBINE_TOL
