@@ -139,7 +139,6 @@ size_t carve_workspace(const Geometry &g, char *base, Workspace *ws) {
   w.status = reinterpret_cast<uint32_t *>(hdr);
   w.ticket = reinterpret_cast<uint32_t *>(hdr ? hdr + 4 : nullptr);
   w.stall = reinterpret_cast<uint32_t *>(hdr ? hdr + 8 : nullptr);
-  w.done = reinterpret_cast<uint32_t *>(hdr ? hdr + 12 : nullptr);
   w.arrive = reinterpret_cast<uint64_t *>(hdr ? hdr + 16 : nullptr);
   w.counts = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * g.E));
   w.offsets = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (g.E + 1)));

@@ -35,7 +35,6 @@ struct Workspace {
   // resident-tiles layout handshake (see plan.hip): words only grow or carry
   // the epoch mark of the call that wrote them, so no call resets them
   uint64_t *arrive;      // [1]  tiles that published their histogram, over all calls
-  uint32_t *done;        // [1]  epoch mark: tile 0's static-plan tables are out
   uint32_t *stall;       // [1]  epoch mark of the last call in which a tile's wait ran out
   uint64_t *tagged;      // [ntiles][E] histograms, then [ntiles] flags: (mark << 32) | value
   int32_t *counts;       // [E]

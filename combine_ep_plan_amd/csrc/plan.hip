@@ -16,12 +16,12 @@
 //   Several tiles, all resident at once (no more tiles than compute units):
 //   every tile publishes its histogram, waits until all tiles have, and
 //   then computes its own per-expert base and the totals from all the
-//   histograms, so it writes its destinations in the same launch.  Counts,
-//   offsets, flags and (static layout) the planner's tables come from
-//   tile 0; for the static layout the other tiles wait for them before
-//   placing their entries.  The wait is bounded: a tile that runs out of it
-//   raises EP_FLAG_PLAN_STALL (the layout is then incomplete) instead of
-//   hanging.
+//   histograms, so it writes its destinations in the same launch.  For the
+//   static layout every tile also runs the planner on those totals and
+//   places its entries from its own copy of the tables in LDS; counts,
+//   offsets, flags and the planner's tables are written out by tile 0.  The
+//   wait for the histograms is bounded: a tile that runs out of it raises
+//   EP_FLAG_PLAN_STALL (the layout is then incomplete) instead of hanging.
 //   More tiles than that: the last workgroup to finish (ticket counter)
 //   scans the tile histograms into per-tile bases, counts and offsets,
 //   raises the flags and runs the planner; then k_plan_dst, one thread per
@@ -86,20 +86,8 @@ __device__ __forceinline__ int32_t last_le(const int32_t *a, int32_t n, int32_t 
 // the barrier that precedes a release by one wave of the workgroup.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Bounded wait until the 32-bit epoch mark at p reaches mark (compared modulo
-// 2^32): agent-scope loads (they see other XCDs' stores), a short sleep
-// between them, at most about half a second.  Returns false if it ran out.
-constexpr uint32_t kSpinLimit = 1u << 21;
-__device__ bool wait_mark(uint32_t *p, uint32_t mark) {
-  for (uint32_t i = 0; i < kSpinLimit; ++i) {
-    const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int32_t)(v - mark) >= 0) return true;
-    __builtin_amdgcn_s_sleep(4);
-  }
-  return false;
-}
-
-// Receive row of an entry of expert e at position pos among e's entries.
+// Receive row of an entry of expert e at position pos among e's entries,
+// from the plan tables in global memory (the two-launch layout).
 __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace &ws,
                                              const int32_t *offs, int32_t e, int32_t pos) {
   if (g.layout == kHT) return offs[e] + pos;
@@ -130,23 +118,50 @@ __device__ __forceinline__ int32_t entry_dst(const Geometry &g, const Workspace 
 //  overflow in inference (MoonEP article, par. 5).
 // Every phase is parallel over ranks, experts, pieces or segments; the five
 // prefix sums are single-wave scans (four of them on four waves at once).
+// The planner's tables in LDS (region A of the layout kernel).
+struct StaticLds {
+  int32_t *tgt, *home, *D;
+  int32_t *recv_rank;    // [R] rank of the i-th receiver
+  int32_t *rbase;        // [R+1] receiver interval starts
+  int32_t *rord;         // [R+1] receivers before r
+  int32_t *rshed;        // [R+1] spill base of rank r
+  int32_t *rnp;          // [R+1] first piece of rank r
+  int32_t *ord;          // [E] hotness order inside the rank; at the end: native row
+  int32_t *shed;         // [E]
+  int32_t *piece_e;      // [E]
+  int32_t *piece_start;  // [E+1]
+  int32_t *nseg;         // [E+1] segments of piece p, then first segment; at the end:
+                         // start of expert e's piece in the shed sequence
+};
+__device__ __forceinline__ StaticLds static_lds(int32_t *pl, int32_t E, int32_t R) {
+  StaticLds t;
+  t.tgt = pl;
+  t.home = t.tgt + R;
+  t.D = t.home + R;
+  t.recv_rank = t.D + R;
+  t.rbase = t.recv_rank + R;
+  t.rord = t.rbase + R + 1;
+  t.rshed = t.rord + R + 1;
+  t.rnp = t.rshed + R + 1;
+  t.ord = t.rnp + R + 1;
+  t.shed = t.ord + E;
+  t.piece_e = t.shed + E;
+  t.piece_start = t.piece_e + E;
+  t.nseg = t.piece_start + E + 1;
+  return t;
+}
+
+// publish: write the tables to the workspace (one workgroup of a launch);
+// every caller ends with the tables entry_dst_static reads in LDS.
 __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_t *cnt,
-                            int32_t N, int32_t *pl, int32_t *s_small, uint32_t *s_flags) {
+                            int32_t N, int32_t *pl, int32_t *s_small, uint32_t *s_flags,
+                            bool publish) {
   const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6;
   const int32_t E = g.E, R = g.R, S = g.S, m = E / R;
-  int32_t *tgt = pl;
-  int32_t *home = tgt + R;
-  int32_t *D = home + R;
-  int32_t *recv_rank = D + R;          // [R] rank of the i-th receiver
-  int32_t *rbase = recv_rank + R;      // [R+1] receiver interval starts
-  int32_t *rord = rbase + R + 1;       // [R+1] receivers before r
-  int32_t *rshed = rord + R + 1;       // [R+1] spill base of rank r
-  int32_t *rnp = rshed + R + 1;        // [R+1] first piece of rank r
-  int32_t *ord = rnp + R + 1;          // [E]
-  int32_t *shed = ord + E;             // [E]
-  int32_t *piece_e = shed + E;         // [E]
-  int32_t *piece_start = piece_e + E;  // [E+1]
-  int32_t *nseg = piece_start + E + 1; // [E+1] segments of piece p, then first segment
+  const StaticLds L = static_lds(pl, E, R);
+  int32_t *tgt = L.tgt, *home = L.home, *D = L.D, *recv_rank = L.recv_rank, *rbase = L.rbase;
+  int32_t *rord = L.rord, *rshed = L.rshed, *rnp = L.rnp, *ord = L.ord, *shed = L.shed;
+  int32_t *piece_e = L.piece_e, *piece_start = L.piece_start, *nseg = L.nseg;
 
   for (int r = tid; r < R; r += nt) {
     const int32_t t = N / R + (r < N % R ? 1 : 0);
@@ -157,9 +172,10 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     D[r] = h < t ? t - h : 0;
     rbase[r] = D[r];
     rord[r] = D[r] > 0 ? 1 : 0;
-    ws.load[r] = t;
+    if (publish) ws.load[r] = t;
   }
-  for (int i = tid; i < R * S; i += nt) ws.replica[i] = -1;
+  if (publish)
+    for (int i = tid; i < R * S; i += nt) ws.replica[i] = -1;
   __syncthreads();
 
   for (int e = tid; e < E; e += nt) {
@@ -179,18 +195,20 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     }
     ord[e] = o;
     shed[e] = s;
-    ws.keep[e] = c - s;
+    if (publish) ws.keep[e] = c - s;
   }
   __syncthreads();
 
-  for (int e = tid; e < E; e += nt) {
-    const int32_t r = e / m;
-    int32_t row = 0;
-    for (int32_t e2 = r * m; e2 < e; ++e2) row += cnt[e2] - shed[e2];
-    ws.native_row[e] = row;
-    if (shed[e] == 0) {
-      ws.seg_first[e] = 0;
-      ws.seg_count[e] = 0;
+  if (publish) {
+    for (int e = tid; e < E; e += nt) {
+      const int32_t r = e / m;
+      int32_t row = 0;
+      for (int32_t e2 = r * m; e2 < e; ++e2) row += cnt[e2] - shed[e2];
+      ws.native_row[e] = row;
+      if (shed[e] == 0) {
+        ws.seg_first[e] = 0;
+        ws.seg_count[e] = 0;
+      }
     }
   }
   for (int r = tid; r < R; r += nt) {
@@ -243,16 +261,18 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     const int32_t ns = wave_exclusive_scan(nseg, npieces);
     if ((tid & 63) == 0) {
       s_small[1] = ns;
-      *ws.n_segments = ns;
+      if (publish) *ws.n_segments = ns;
     }
   }
   __syncthreads();
   const int32_t nsegs = s_small[1];
 
-  for (int p = tid; p < npieces; p += nt) {
-    const int32_t e = piece_e[p];
-    ws.seg_first[e] = nseg[p];
-    ws.seg_count[e] = (p + 1 < npieces ? nseg[p + 1] : nsegs) - nseg[p];
+  if (publish) {
+    for (int p = tid; p < npieces; p += nt) {
+      const int32_t e = piece_e[p];
+      ws.seg_first[e] = nseg[p];
+      ws.seg_count[e] = (p + 1 < npieces ? nseg[p + 1] : nsegs) - nseg[p];
+    }
   }
   // one thread per segment: its piece, its receiver, its rows and its slot
   for (int sid = tid; sid < nsegs; sid += nt) {
@@ -261,17 +281,46 @@ __device__ void plan_static(const Geometry &g, const Workspace &ws, const int32_
     const int32_t r = recv_rank[rord[last_le(rbase, R, a0)] + (sid - nseg[p])];
     const int32_t lo = a0 > rbase[r] ? a0 : rbase[r];
     const int32_t hi = b0 < rbase[r] + D[r] ? b0 : rbase[r] + D[r];
-    int32_t *sg = ws.segments + (int64_t)sid * 5;
-    sg[0] = e;
-    sg[1] = r;
-    sg[2] = (cnt[e] - shed[e]) + (lo - a0);
-    sg[3] = hi - lo;
-    sg[4] = home[r] + (lo - rbase[r]);
     const int32_t slot = p - last_le(piece_start, npieces, rbase[r]);
-    ws.seg_slot[sid] = slot < S ? slot : -1;
-    if (slot < S) ws.replica[r * S + slot] = e;
-    else if (g.slot_mode == 0) atomicOr(s_flags, kFlagSlotBudget);  // inference: direct read
+    if (publish) {
+      int32_t *sg = ws.segments + (int64_t)sid * 5;
+      sg[0] = e;
+      sg[1] = r;
+      sg[2] = (cnt[e] - shed[e]) + (lo - a0);
+      sg[3] = hi - lo;
+      sg[4] = home[r] + (lo - rbase[r]);
+      ws.seg_slot[sid] = slot < S ? slot : -1;
+      if (slot < S) ws.replica[r * S + slot] = e;
+    }
+    if (slot >= S && g.slot_mode == 0) atomicOr(s_flags, kFlagSlotBudget);  // inference: direct read
   }
+  // The tables the destinations need, in arrays no phase reads any more:
+  // ord[e] = expert e's first row among its rank's own rows, nseg[e] = where
+  // e's shed rows start in the sequence of all shed rows.
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    const int32_t r = e / m;
+    int32_t row = 0;
+    for (int32_t e2 = r * m; e2 < e; ++e2) row += cnt[e2] - shed[e2];
+    ord[e] = row;
+  }
+  for (int p = tid; p < npieces; p += nt) nseg[piece_e[p]] = piece_start[p];
+}
+
+// Receive row of an entry of expert e at position pos among e's entries,
+// static layout, from the planner's tables in LDS (after plan_static and a
+// barrier).  The first keep = cnt - shed entries stay on e's rank, after
+// the rows the rank keeps for its lower-numbered experts; entry keep + i is
+// entry i of e's piece of the shed sequence, which lands on the receiver
+// whose deficit interval holds it, after that receiver's own rows.
+__device__ __forceinline__ int32_t entry_dst_static(const Geometry &g, const StaticLds &L,
+                                                    const int32_t *cnt, int32_t e, int32_t pos) {
+  const int32_t m = g.E / g.R;
+  const int32_t kp = cnt[e] - L.shed[e];
+  if (pos < kp) return (e / m) * g.C + L.ord[e] + pos;
+  const int32_t a = L.nseg[e] + (pos - kp);
+  const int32_t r = last_le(L.rbase, g.R, a);
+  return r * g.C + L.home[r] + (a - L.rbase[r]);
 }
 
 // LDS of the layout kernel, in int32 words: region A holds the per-wave
@@ -328,6 +377,10 @@ __device__ __forceinline__ uint64_t tagged(uint32_t mark, uint32_t v) {
   return ((uint64_t)mark << 32) | v;
 }
 
+// Polling rounds a handshake wait may take before it gives up: each round
+// is a memory round trip and a short sleep, so one to two seconds.
+constexpr uint32_t kSpinLimit = 1u << 21;
+
 // Loads the words p[i * stride], i < n <= 16, into v, polling until every one
 // carries `mark`; each round re-issues all stale loads together, so a round
 // costs one memory latency however many are stale.  Bounded: returns false
@@ -359,7 +412,8 @@ __device__ __forceinline__ bool load_tagged(const uint64_t *p, int64_t stride, i
 // launch.  RG = 0: the ids come from a.idx.
 // RES: several tiles, all resident at once; every tile finishes its own
 // entries after reading every tile's histogram (no second launch).
-template <int RG, int RPER, bool RES>
+// ST: the static layout (the planner runs in the kernel).
+template <int RG, int RPER, bool RES, bool ST>
 __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   extern __shared__ int32_t lds[];
   __shared__ uint32_t s_flags;
@@ -373,7 +427,7 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   const bool single = gridDim.x == 1;
   uint16_t *wcnt = reinterpret_cast<uint16_t *>(lds);   // [waves][E], <= 256 each
   int32_t *pl = lds;                                     // planner tables (after ranking)
-  int32_t *cnt = lds + plan_region_a(E, g.layout == kStatic ? g.R : 0);   // [E]
+  int32_t *cnt = lds + plan_region_a(E, ST ? g.R : 0);   // [E]
   int32_t *offs = cnt + E;                               // [E+1]
   int32_t *s_idx = offs + E + 1;                         // RG > 0: the tile's routed ids
 
@@ -585,52 +639,40 @@ __global__ __launch_bounds__(kTileThreads) void k_plan_tiles(PlanArgs a) {
   block_exclusive_scan(cnt, offs, E, s_tmp);
   const int32_t total = offs[E];
   const bool writer = !RES || blockIdx.x == 0;   // the tile that writes the shared tables
-  if (writer) {
-    if (g.layout == kLL) {
-      for (int e = tid; e < E; e += kTileThreads)
-        if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
-    } else if (g.layout == kStatic) {
-      plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags);
-    }
+  if (g.layout == kLL && writer) {
+    for (int e = tid; e < E; e += kTileThreads)
+      if (cnt[e] > g.cap) atomicOr(&s_flags, kFlagCapacity);
     __syncthreads();
+  } else if constexpr (ST) {
+    // Every resident tile has every count, so each runs the planner on its
+    // own (the same tables, in its LDS) and places its entries from there;
+    // tile 0 also writes the tables out.  No tile waits for another's.
+    plan_static(g, ws, cnt, total, pl, s_tmp, &s_flags, writer);
+    __syncthreads();
+  }
+  if (writer) {
     for (int e = tid; e <= E; e += kTileThreads) {
       ws.offsets[e] = offs[e];
       if (e < E) ws.counts[e] = cnt[e];
     }
     if (tid == 0) *ws.status = s_flags;
   }
-
-  if constexpr (RES) {
-    // The static layout places entries through the planner's tables: tile 0
-    // releases them (epoch mark), the other tiles wait for the mark.  A tile
-    // whose wait ran out leaves this call's mark in the stall word, which
-    // ep_handle_status reports as EP_FLAG_PLAN_STALL.
-    if (g.layout == kStatic) {
-      if (blockIdx.x == 0) {
-        wait_stores();
-        __syncthreads();
-        if (tid == 0) {
-          __threadfence();
-          __hip_atomic_store(ws.done, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else {
-        if (tid == 0) {
-          if (!wait_mark(ws.done, mark)) s_last = 1;
-          __threadfence();
-        }
-        __syncthreads();
-      }
-    }
+  // A tile whose wait for the histograms ran out leaves this call's mark in
+  // the stall word, which ep_handle_status reports as EP_FLAG_PLAN_STALL.
+  if constexpr (RES)
     if (tid == 0 && s_last)
       __hip_atomic_store(ws.stall, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 
   if (single || RES) {
 #pragma unroll
     for (int c = 0; c < kTileChunks; ++c) {
       const int64_t f = wbase + c * 64 + lane;
       if (f < g.n) {
-        int32_t d = ev[c] >= 0 ? entry_dst(g, ws, offs, ev[c], rr[c]) : -1;
+        int32_t d = -1;
+        if (ev[c] >= 0) {
+          if constexpr (ST) d = entry_dst_static(g, static_lds(pl, E, g.R), cnt, ev[c], rr[c]);
+          else d = entry_dst(g, ws, offs, ev[c], rr[c]);
+        }
         if (d >= g.rows) d = -1;
         ws.eidx[f] = ev[c];
         ws.dst[f] = d;
@@ -691,13 +733,18 @@ hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float
   PlanArgs a{g, ws, idx, logits, idx, w};
   const size_t lds =
       plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0) + (size_t)kTileEntries * sizeof(int32_t);
-#define L2(P, RES)                                                                              \
-  hipLaunchKernelGGL((k_plan_tiles<kFusedRouteLanes, P, RES>), dim3(g.ntiles),                \
+#define L3(P, RES, ST)                                                                          \
+  hipLaunchKernelGGL((k_plan_tiles<kFusedRouteLanes, P, RES, ST>), dim3(g.ntiles),            \
                      dim3(kTileThreads), lds, s, a)
-#define L(P)                          \
-  do {                                \
+#define L2(P, RES)                                   \
+  do {                                               \
+    if (g.layout == kStatic) L3(P, RES, true);       \
+    else L3(P, RES, false);                          \
+  } while (0)
+#define L(P)                            \
+  do {                                  \
     if (resident_tiles(g)) L2(P, true); \
-    else L2(P, false);                \
+    else L2(P, false);                  \
   } while (0)
   if (per <= 1) L(1);
   else if (per <= 2) L(2);
@@ -707,6 +754,7 @@ hipError_t launch_route_plan(const Geometry &g, const Workspace &ws, const float
   else L(32);
 #undef L
 #undef L2
+#undef L3
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_plan_dst(g, a, s);
@@ -716,10 +764,17 @@ hipError_t launch_plan(const Geometry &g, const Workspace &ws, const int32_t *to
                        hipStream_t s) {
   PlanArgs a{g, ws, topk_idx, nullptr, nullptr, nullptr};
   const size_t lds = plan_lds_bytes(g.E, g.layout == kStatic ? g.R : 0);
-  if (resident_tiles(g))
-    hipLaunchKernelGGL((k_plan_tiles<0, 0, true>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_plan_tiles<0, 0, false>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a);
+#define L(RES, ST) \
+  hipLaunchKernelGGL((k_plan_tiles<0, 0, RES, ST>), dim3(g.ntiles), dim3(kTileThreads), lds, s, a)
+  const bool st = g.layout == kStatic;
+  if (resident_tiles(g)) {
+    if (st) L(true, true);
+    else L(true, false);
+  } else {
+    if (st) L(false, true);
+    else L(false, false);
+  }
+#undef L
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_plan_dst(g, a, s);

@@ -289,6 +289,78 @@ def test_planner_inference_slot_mode_random(R, m, S, data):
     assert bool(pt.flags & oracle.FLAG_SLOT_BUDGET) == bool(np.any(pt.seg_slot < 0))
 
 
+def static_dst_closed_form(idx, E, R):
+    """Destination rows of the static layout written straight from the
+    planner's definition (MoonEP article, paragraphs 3-5), with no segment
+    table: rank r keeps min(own rows, target) rows; a donor sheds the tail
+    rows of its hottest experts (count descending, id ascending); the shed
+    rows of all donors, in rank order and then in that walk order, fill the
+    receivers' deficits in rank order, each after the receiver's own rows."""
+    T, k = idx.shape
+    m = E // R
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E).astype(np.int64)
+    N = int(counts.sum())
+    C = -(-(T * k) // R)
+    tgt = np.array([N // R + (1 if r < N % R else 0) for r in range(R)], np.int64)
+    home = counts.reshape(R, m).sum(axis=1)
+    shed = np.zeros(E, np.int64)
+    order = {}
+    for r in range(R):
+        walk = sorted(range(r * m, (r + 1) * m), key=lambda e: (-counts[e], e))
+        order[r] = walk
+        left = max(int(home[r] - tgt[r]), 0)
+        for e in walk:
+            shed[e] = min(left, counts[e])
+            left -= shed[e]
+    keep = counts - shed
+    start, a = {}, 0                     # start of each expert's piece in the shed sequence
+    for r in range(R):
+        for e in order[r]:
+            if shed[e] > 0:
+                start[e] = a
+                a += int(shed[e])
+    deficit = np.maximum(tgt - home, 0)
+    rbase = np.concatenate([[0], np.cumsum(deficit)])
+    seen = np.zeros(E, np.int64)
+    dst = np.full(T * k, -1, np.int64)
+    for f, e in enumerate(flat):
+        if e < 0 or e >= E:
+            continue
+        pos = seen[e]
+        seen[e] += 1
+        r = e // m
+        if pos < keep[e]:
+            dst[f] = r * C + keep[r * m:e].sum() + pos
+        else:
+            a = start[e] + pos - keep[e]
+            q = int(np.searchsorted(rbase, a, side="right") - 1)
+            dst[f] = q * C + home[q] + (a - rbase[q])
+    return dst.reshape(T, k)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 8), st.integers(1, 6), st.integers(1, 60), st.integers(1, 4), st.data())
+def test_static_dst_matches_the_planner_in_closed_form(R, m, T, k, data):
+    E = R * m
+    k = min(k, E)
+    hot = data.draw(st.integers(0, E - 1))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    p = np.full(E, 1.0)
+    p[hot] += data.draw(st.floats(0.0, 20.0))
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    L = oracle.layout(idx, E, "static", R=R, S=2)
+    assert np.array_equal(L.dst, static_dst_closed_form(idx, E, R))
+
+
+@pytest.mark.parametrize("name,rho", [("training", 8.0), ("sweep", 8.0), ("sweep", 1.0)])
+def test_static_dst_closed_form_on_workloads(name, rho):
+    inp = workloads.make_inputs(name, rho=rho)
+    c = inp.cfg
+    L = oracle.layout(inp.topk_idx, c.E, "static", R=c.R, S=c.S)
+    assert np.array_equal(L.dst, static_dst_closed_form(inp.topk_idx, c.E, c.R))
+
+
 def test_planner_uniform_reduces_to_ht():
     # every rank's own load equals its target: no replicas, rows = HT layout
     R, m = 4, 2
