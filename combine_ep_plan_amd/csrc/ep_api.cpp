@@ -331,7 +331,7 @@ ep_status_t ep_handle_query(ep_handle_t h, ep_handle_view_t *v) {
 
 ep_status_t ep_handle_status(ep_handle_t h, void *stream, uint32_t *flags) {
   if (!h || !flags) return EP_ERR_INVALID_ARG;
-  // header: status word, ticket, stall mark, done mark, arrival count
+  // header: status word, ticket, stall mark, an unused word, arrival count
   uint32_t hdr[6] = {0, 0, 0, 0, 0, 0};
   hipError_t e = hipMemcpyAsync(hdr, h->ws.status, sizeof hdr, hipMemcpyDeviceToHost,
                                 as_stream(stream));
