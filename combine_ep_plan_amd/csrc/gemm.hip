@@ -53,7 +53,10 @@
 //    short ones (bound by streaming their weight slice), merged, column tile
 //    fastest, so no XCD holds only one kind: with skewed routing the hot
 //    experts' full tiles would otherwise sit on the first XCDs and the cold
-//    experts' short tiles on the last ones, which then idle.
+//    experts' short tiles on the last ones, which then idle.  Each XCD takes
+//    every eighth tile of a kind, so the XCDs walk the groups together and
+//    a hot expert's row tiles, spread over all of them at once, share its
+//    weight slices through the Infinity Cache.
 #include "device.h"
 #include "ep_internal.h"
 
@@ -119,8 +122,8 @@ __device__ __forceinline__ void group_of(const TileArgs &a, int32_t q, int32_t &
 // in group order from the front and the short ones in group order from the
 // back (entry max_tiles - 1 - j is short tile j), so the GEMM kernel can give
 // every XCD the same share of each kind (balanced_tile).  Without PART every
-// tile counts as full: the table is in group order, and each XCD takes a
-// contiguous eighth of it.
+// tile counts as full: the table is in group order, and XCD x takes tiles
+// x, x + 8, x + 16, ... of it.
 // ntiles[0] = all tiles, ntiles[1] = full tiles.
 template <int TM, bool PART>
 __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_tiles) {
@@ -188,27 +191,31 @@ __global__ __launch_bounds__(1024) void k_gemm_tiles(TileArgs a, int32_t max_til
 }
 
 // Work of workgroup blockIdx.x: its row tile (an index into the table) and
-// column tile.  Workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of
-// the full tiles and the x-th eighth of the short tiles, each in group
-// order, merged in proportion (Bresenham), every row tile with its column
-// tiles one after another.  So every XCD gets the same MFMA-bound and
-// streaming-bound work and runs both kinds side by side, and the column
-// tiles of a row tile stay on one XCD (they share X rows in its L2).  The
-// grid holds at least (max_tiles / 8 + 2) * n_col_tiles workgroups per XCD
-// (gemm_grid).
+// column tile.  Workgroup b runs on XCD b % 8; XCD x takes full tiles x,
+// x + 8, x + 16, ... and short tiles x, x + 8, ..., each in group order,
+// merged in proportion (Bresenham), every row tile with its column tiles one
+// after another.  So every XCD gets the same MFMA-bound and streaming-bound
+// work and runs both kinds side by side; the column tiles of a row tile stay
+// on one XCD (they share X rows in its L2); and the eight XCDs walk the
+// groups together, so the row tiles of one expert run on all of them at about
+// the same time and its weight slices, after the first read, come from the
+// Infinity Cache that the XCDs share (with each XCD taking a contiguous
+// eighth, the row tiles of a hot expert ran one after another on one XCD and
+// read its weights from HBM again each time).  The grid holds at least
+// (max_tiles / 8 + 2) * n_col_tiles workgroups per XCD (gemm_grid).
 __device__ __forceinline__ bool balanced_tile(const int32_t *__restrict__ ntiles,
                                               int32_t max_tiles, int32_t n_col_tiles,
                                               int32_t &tile, int32_t &col) {
   const int32_t nf = ntiles[1], ns = ntiles[0] - nf;
   const int32_t x = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int32_t f0 = (int32_t)((int64_t)x * nf / kXcds), f1 = (int32_t)((int64_t)(x + 1) * nf / kXcds);
-  const int32_t s0 = (int32_t)((int64_t)x * ns / kXcds), s1 = (int32_t)((int64_t)(x + 1) * ns / kXcds);
-  const int32_t b = f1 - f0, n = b + (s1 - s0);
+  // this XCD's full and short tiles: those whose index is x modulo 8
+  const int32_t b = x < nf ? (nf - x + kXcds - 1) / kXcds : 0;
+  const int32_t n = b + (x < ns ? (ns - x + kXcds - 1) / kXcds : 0);
   const int32_t p = slot / n_col_tiles;
   if (p >= n) return false;
   col = slot - p * n_col_tiles;
   const int32_t before = (int32_t)((int64_t)p * b / n), upto = (int32_t)((int64_t)(p + 1) * b / n);
-  tile = upto > before ? f0 + before : max_tiles - 1 - (s0 + p - before);
+  tile = upto > before ? x + kXcds * before : max_tiles - 1 - (x + kXcds * (p - before));
   return true;
 }
 
