@@ -193,7 +193,7 @@ def test_combine_bwd(c):
     assert np.all(host(gw)[L.dst < 0] == 0)
 
 
-@pytest.mark.parametrize("P", [4096, 1000, 8, 13])
+@pytest.mark.parametrize("P", [4096, 1000, 8, 13, 8200, 4100])
 def test_dup_reduce(P):
     rng = np.random.default_rng(P)
     E = 6
