@@ -157,6 +157,31 @@ def test_grouped_gemm_integer_inputs_are_exact():
     assert np.array_equal(host_bits(y), ref)
 
 
+@pytest.mark.parametrize("T,E,k,skew,seed", [(600, 2, 1, 0.0, 1), (1500, 4, 2, 2.0, 2), (3000, 8, 2, 1.5, 3),
+                                             (5000, 16, 4, 2.5, 4), (9000, 24, 4, 1.0, 5)])
+def test_wide_grouped_gemm_integer_inputs_cover_every_tile(T, E, k, skew, seed):
+    """The 256 x 256 kernel on small-integer inputs (exact in fp32, so bit for
+    bit), with groups whose row tiles are full and short in every count from
+    a few to dozens: every XCD's share of the tile table (tiles x, x + 8, ...
+    of each kind) is computed once and lands on its own rows."""
+    K, N = 192, 520   # three column tiles, the last one ragged
+    idx, w, _ = workloads.random_case(3200 + seed, T, 8, E, k, skew=skew)
+    g = make_group(E, 1, 8, k, T, "ht")
+    h = ep.Handle(g, T)
+    h.plan(dev_i32(idx))
+    L = oracle.layout(idx, E, "ht")
+    assert L.rows >= 128 * E, "the case must reach the 256 x 256 kernel"
+    rng = np.random.default_rng(40 + seed)
+    xb = _bits(rng.integers(-4, 5, (L.rows, K)))
+    wb = _bits(rng.integers(-4, 5, (E, N, K)) * 0.25)
+    y = torch.full((L.rows, N), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ep.Buffer(g).expert_gemm(dev_bf16(xb), dev_bf16(wb.reshape(E, -1)).view(E, N, K), h, out=y)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm(xb, wb, oracle.expert_groups(L, "ht", E),
+                              np.full((L.rows, N), SENTINEL, np.uint16))
+    assert np.array_equal(host_bits(y), ref)
+
+
 def test_grouped_gemm_repeat_is_deterministic():
     yb1, ref, _, _, _, _ = _run(CASES[4])
     yb2, _, _, _, _, _ = _run(CASES[4])
