@@ -45,10 +45,12 @@ def parse():
                    help="FP8 e4m3 dispatch (one fp32 scale per 128 channels); with --gemm the "
                         "grouped GEMM takes the FP8 rows and FP8 weights (roofline against the "
                         "fp8 MFMA peak)")
-    p.add_argument("--fp8-scales", choices=("amax", "pow2"), default="amax",
+    p.add_argument("--fp8-scales", choices=("amax", "pow2", "amax_pow2w"), default="amax",
                    help="format of the FP8 scales (the group's fp8_scales): amax/448, or the power "
                         "of two at or above it (then the FP8 GEMM of large groups runs on the "
-                        "256 x 256 kernel with the scales applied by the matrix cores)")
+                        "256 x 256 kernel with the scales applied by the matrix cores), or amax "
+                        "rows against power-of-two weight scales (the matrix cores apply the "
+                        "weights' scales, the rows' are folded)")
     p.add_argument("--route", action="store_true",
                    help="start the step from router logits (ep_route before ep_plan)")
     p.add_argument("--two-call-dispatch", action="store_true",
@@ -536,7 +538,8 @@ def main():
     elif a.prefetch:
         wts = torch.empty((c.E, PREFETCH_P), dtype=torch.bfloat16, device=dev).fill_(0.5)
     gemm_fp8 = bool(a.gemm and a.fp8)
-    pow2 = a.fp8_scales == "pow2"
+    pow2 = a.fp8_scales in ("pow2", "amax_pow2w")   # the weights' scale format
+    row_pow2 = a.fp8_scales == "pow2"                # the rows' (the FFN's activation)
     if gemm_fp8:   # the weights quantised like the rows (the library's quantiser, the group's format)
         wts, wsc = ep.Buffer.quantize_fp8(wts, pow2=pow2)
         torch.cuda.synchronize()
@@ -588,7 +591,7 @@ def main():
             asc = torch.empty((h.recv_rows, I // 128), dtype=torch.float32, device=dev)
             torch.cuda.synchronize()
             del w2
-            ops.append(("quantize", lambda: ep.ep_quantize_fp8(gy_out, aq, asc, LS["s"], pow2=pow2)))
+            ops.append(("quantize", lambda: ep.ep_quantize_fp8(gy_out, aq, asc, LS["s"], pow2=row_pow2)))
             ops.append(("gemm2", lambda: ep.ep_expert_gemm_fp8(h.ptr, aq, asc, w2c, w2s, None, None,
                                                                ffn_out, LS["s"])))
         else:

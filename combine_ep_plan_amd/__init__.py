@@ -49,8 +49,9 @@ SLOTS_TRAINING, SLOTS_INFERENCE = 0, 1
 _SLOT_MODES = {"training": SLOTS_TRAINING, "inference": SLOTS_INFERENCE}
 STORES_AUTO, STORES_CACHED, STORES_STREAMING = 0, 1, 2
 _STORES = {"auto": STORES_AUTO, "cached": STORES_CACHED, "streaming": STORES_STREAMING}
-FP8_SCALES_AMAX, FP8_SCALES_POW2 = 0, 1
-_FP8_SCALES = {"amax": FP8_SCALES_AMAX, "pow2": FP8_SCALES_POW2}
+FP8_SCALES_AMAX, FP8_SCALES_POW2, FP8_SCALES_AMAX_POW2_WEIGHTS = 0, 1, 2
+_FP8_SCALES = {"amax": FP8_SCALES_AMAX, "pow2": FP8_SCALES_POW2,
+               "amax_pow2w": FP8_SCALES_AMAX_POW2_WEIGHTS}
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float8_e4m3fn: 2, torch.int32: 3}
 _STATUS = ["EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_BAD_TAG", "EP_ERR_BAD_DTYPE",
            "EP_ERR_BAD_SHAPE", "EP_ERR_NOT_PLANNED", "EP_ERR_WORKSPACE_TOO_SMALL",

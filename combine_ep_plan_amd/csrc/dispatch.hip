@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch_fp8(const u32x4 *__res
     const u32x4 cur = xv;
     if (v + kRowThreads < hi) xv = x[t * V + v + kRowThreads];
     float s;
-    const u32x2 packed = quantize_fp8_vec(cur, &s, fl.g.fp8_pow2 != 0);
+    const u32x2 packed = quantize_fp8_vec(cur, &s, fl.g.fp8_pow2 == 1);
 #pragma unroll
     for (int j = 0; j < KN; ++j) {
       if (K == 0 && j >= k) break;

@@ -53,7 +53,7 @@ epk::Geometry make_geometry(const ep_group *g, int32_t T) {
   geo.stores = c.dispatch_stores;
   geo.in_flight = c.passes_in_flight > 1 ? c.passes_in_flight : 1;
   geo.cstores = c.combine_stores;
-  geo.fp8_pow2 = c.fp8_scales == EP_FP8_SCALES_POW2 ? 1 : 0;
+  geo.fp8_pow2 = c.fp8_scales;   // 0 AMAX, 1 POW2, 2 AMAX rows with POW2 weights
   geo.layout = c.layout;
   geo.cap = c.capacity;
   geo.n = (int64_t)T * c.top_k;
@@ -207,7 +207,9 @@ ep_status_t ep_group_create(const ep_group_config_t *cfg, ep_group_t *out) {
   if (c.passes_in_flight < 0 || c.passes_in_flight > 64) return EP_ERR_INVALID_ARG;
   if (c.combine_stores < EP_STORES_AUTO || c.combine_stores > EP_STORES_STREAMING)
     return EP_ERR_INVALID_ARG;
-  if (c.fp8_scales != EP_FP8_SCALES_AMAX && c.fp8_scales != EP_FP8_SCALES_POW2) return EP_ERR_INVALID_ARG;
+  if (c.fp8_scales != EP_FP8_SCALES_AMAX && c.fp8_scales != EP_FP8_SCALES_POW2 &&
+      c.fp8_scales != EP_FP8_SCALES_AMAX_POW2_WEIGHTS)
+    return EP_ERR_INVALID_ARG;
   if (c.slot_mode != EP_SLOTS_TRAINING &&
       !(c.slot_mode == EP_SLOTS_INFERENCE && c.layout == EP_LAYOUT_STATIC))
     return EP_ERR_INVALID_ARG;

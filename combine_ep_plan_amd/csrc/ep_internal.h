@@ -64,7 +64,7 @@ struct Geometry {
   int32_t stores;     // dispatch stores: 0 by size, 1 cached, 2 non-temporal
   int32_t in_flight;  // passes of the group at once (>= 1): the size rule counts all their rows
   int32_t cstores;    // combine's token rows: 0 or 1 cached, 2 non-temporal
-  int32_t fp8_pow2;   // FP8 scales are powers of two (EP_FP8_SCALES_POW2)
+  int32_t fp8_pow2;   // ep_fp8_scales_t: 1 every FP8 scale a power of two, 2 the weights' only
   int32_t C;        // STATIC rows per rank
   int32_t ntiles;   // layout tiles (>= 1)
   int32_t cus;      // compute units of the device (0 if unknown): the most tiles one launch finishes

@@ -705,14 +705,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kScaleBufs = 4;
 constexpr int kF8Block = 128;  // K per scale; also the slab depth in bytes
 
-template <bool GLU>
+// E8M0 exponent of a power-of-two fp32 scale; *bad is set if it is not one.
+__device__ __forceinline__ uint32_t scale_exponent(float s, uint32_t *bad) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t e = b >> 23;  // a set sign bit makes it 256 or more
+  // no branch: a mantissa bit, a sign, a zero or an all-ones exponent
+  *bad |= (b & 0x007FFFFFu) | (uint32_t)(e - 1u > 0xFDu);
+  return e & 0xFFu;
+}
+
+// WP2 (a group with power-of-two weight scales and amax row scales): each
+// block's MFMAs take the weight columns' exponents as their B block scales,
+// so the fold multiplies by the row scale alone (one FMA per element); a
+// weight scale that is not a power of two raises kFlagScaleFormat.
+template <bool GLU, bool WP2>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
     const u32x4 *__restrict__ X, const float *__restrict__ SX, const u32x4 *__restrict__ W,
     const float *__restrict__ SW, const u32x4 *__restrict__ Wslot,
     const float *__restrict__ SWslot, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, int32_t max_tiles, int32_t K, int32_t N, int32_t E,
     int32_t n_col_tiles,
-    uint16_t *__restrict__ Y) {
+    uint16_t *__restrict__ Y, uint32_t *__restrict__ status) {
   __shared__ u32x4 sa[2][kTileM * kChunks];
   __shared__ u32x4 sb[2][kBN * kChunks];
   __shared__ __attribute__((aligned(16))) float ssc[kScaleBufs][kTileM + kBN];  // row, then column scales
@@ -811,15 +824,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   // partial sum P.  cbsz = blgp = 0: both operands e4m3; scale exponents
   // 127: 2^0.
 #define BLOCK(P, i, j)                                                                         \
-  P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], f32x16{}, 0, 0, 0, 127,  \
-                                                      0, 127);                                 \
-  P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], P, 0, 0, 0, 127, 0, 127);
+  if constexpr (WP2) {                                                                         \
+    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], f32x16{}, 0, 0, 0, 127, \
+                                                        j, eb);                                \
+    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], P, 0, 0, 0, 127, j, eb); \
+  } else {                                                                                     \
+    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], f32x16{}, 0, 0, 0, 127, \
+                                                        0, 127);                               \
+    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], P, 0, 0, 0, 127, 0, 127); \
+  }
   // acc += P * (row scale * column scale); accumulator r of a lane is tile
   // row wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4, column wn*64 + j*32 + lane%32
 #define FOLD(P, i, j)                                                                          \
   _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4)                                             \
   _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                \
-      acc[i][j][g4 * 4 + q] += P[g4 * 4 + q] * (srow[g4][q] * scol[j]);
+      acc[i][j][g4 * 4 + q] += WP2 ? P[g4 * 4 + q] * srow[g4][q]                               \
+                                   : P[g4 * 4 + q] * (srow[g4][q] * scol[j]);
 #define ROWSCALES(i)                                                                           \
   _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) srow[g4] =                                  \
       *reinterpret_cast<const f32x4 *>(sc + wm * kWTM + (i) * 32 + g4 * 8 + (lane >> 5) * 4);
@@ -837,6 +857,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   i32x8 fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
   f32x16 p0, p1;
   float scol[kFN];
+  int eb = 0;          // WP2: the exponent bytes of the lane's two weight columns
+  uint32_t bad = 0u;   // WP2: a weight scale that is not a power of two
   f32x4 srow[4];
   GLOAD(0);
   SWRITE(0);
@@ -854,6 +876,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
       if constexpr ((LB) > 0) {                                                                \
         _Pragma("unroll") for (int j = 0; j < kFN; ++j)                                        \
             scol[j] = sc[kTileM + wn * kWTN + j * 32 + (lane & 31)];                           \
+        if constexpr (WP2)                                                                     \
+          eb = (int)(scale_exponent(scol[0], &bad) | (scale_exponent(scol[1], &bad) << 8));    \
         ROWSCALES(0);                                                                          \
         BLOCK(p0, 0, 0);                                                                       \
         BLOCK(p1, 0, 1);                                                                       \
@@ -887,6 +911,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_fp8(
   if (live >= kFM) F8_LOOP(kFM)
   else if (live == 1) F8_LOOP(1)
   else F8_LOOP(0)
+  if constexpr (WP2) {
+    if (__ballot(bad != 0u) != 0u && lane == 0) atomicOr(status, kFlagScaleFormat);
+  }
 #undef F8_LOOP
 #undef BLOCK
 #undef FOLD
@@ -994,14 +1021,6 @@ __device__ __forceinline__ void mfma8_rows(f32x16 (&acc)[kFM2][kFN2], const i32x
 }
 static_assert(kFN2 == 4, "mfma8_rows writes four column blocks");
 
-// E8M0 exponent of a power-of-two fp32 scale; *bad is set if it is not one.
-__device__ __forceinline__ uint32_t scale_exponent(float s, uint32_t *bad) {
-  const uint32_t b = __float_as_uint(s);
-  const uint32_t e = b >> 23;  // a set sign bit makes it 256 or more
-  // no branch: a mantissa bit, a sign, a zero or an all-ones exponent
-  *bad |= (b & 0x007FFFFFu) | (uint32_t)(e - 1u > 0xFDu);
-  return e & 0xFFu;
-}
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -1264,7 +1283,7 @@ static bool gemm_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
 // and at least 128 rows per expert on average; its buffer offsets over a
 // tile's codes are 32-bit as well.
 static bool gemm_fp8_uses_wide_tiles(const Geometry &g, int32_t K, int32_t N) {
-  return g.fp8_pow2 && N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E &&
+  return g.fp8_pow2 == 1 && N >= kBN2 && g.n >= (int64_t)(kBM2 / 2) * g.E &&
          (int64_t)kBM2 * K <= INT32_MAX;
 }
 
@@ -1318,10 +1337,18 @@ hipError_t launch_grouped_gemm_fp8(const Geometry &g, const Workspace &ws, const
   }
   hipLaunchKernelGGL((k_gemm_tiles<kTileM, false>), dim3(1), dim3(1024), 0, s, ta, max_tiles);
   const int32_t ncol = (N + kBN - 1) / kBN;
-  GEMM_LAUNCH(k_grouped_gemm_fp8, dim3(gemm_grid(max_tiles, ncol)), dim3(kGemmThreads), 0, s,
-                     reinterpret_cast<const u32x4 *>(x), sx, reinterpret_cast<const u32x4 *>(w), sw,
-                     reinterpret_cast<const u32x4 *>(wslot), swslot, ws.gemm_tiles,
-                     ws.gemm_ntiles, max_tiles, K, N, g.E, ncol, y);
+#define F8_ARGS                                                                                \
+  dim3(gemm_grid(max_tiles, ncol)), dim3(kGemmThreads), 0, s, reinterpret_cast<const u32x4 *>(x), sx, \
+      reinterpret_cast<const u32x4 *>(w), sw, reinterpret_cast<const u32x4 *>(wslot), swslot,       \
+      ws.gemm_tiles, ws.gemm_ntiles, max_tiles, K, N, g.E, ncol, y, ws.status
+  if (g.fp8_pow2 == 2) {
+    if (glu) hipLaunchKernelGGL((k_grouped_gemm_fp8<true, true>), F8_ARGS);
+    else hipLaunchKernelGGL((k_grouped_gemm_fp8<false, true>), F8_ARGS);
+  } else {
+    if (glu) hipLaunchKernelGGL((k_grouped_gemm_fp8<true, false>), F8_ARGS);
+    else hipLaunchKernelGGL((k_grouped_gemm_fp8<false, false>), F8_ARGS);
+  }
+#undef F8_ARGS
   return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ typedef enum ep_status {
                                    all run at once within about half a second (the GPU was held
                                    by other work): the layout of that call is incomplete and must
                                    be planned again */
-#define EP_FLAG_SCALE_FORMAT 16u /* a group with EP_FP8_SCALES_POW2: an FP8 scale handed to the
+#define EP_FLAG_SCALE_FORMAT 16u /* a group with EP_FP8_SCALES_POW2 (or _AMAX_POW2_WEIGHTS, for the
+                                    weights' scales): an FP8 scale handed to the
                                     grouped GEMM was not a positive normal power of two (its
                                     block was taken at the scale's exponent) */
 
@@ -150,7 +151,13 @@ typedef enum ep_dispatch_stores {
  * must be powers of two too (ep_quantize_fp8 with POW2 makes such). */
 typedef enum ep_fp8_scales {
   EP_FP8_SCALES_AMAX = 0,
-  EP_FP8_SCALES_POW2 = 1
+  EP_FP8_SCALES_POW2 = 1,
+  /* AMAX rows (dispatch and row quantiser as AMAX) against weights whose
+   * scales are powers of two (ep_quantize_fp8 with POW2): the FP8 GEMM's
+   * matrix cores apply the weight scales and only the row scales are folded
+   * per 128-channel block, one fused multiply-add per output element.  A
+   * weight scale that is not a power of two raises EP_FLAG_SCALE_FORMAT. */
+  EP_FP8_SCALES_AMAX_POW2_WEIGHTS = 2
 } ep_fp8_scales_t;
 
 /* Non-owning view of a contiguous row-major device tensor.  data must be

@@ -73,7 +73,7 @@ def create(lib, **kw):
     dict(layout=7), dict(layout=ep.LAYOUT_LL, capacity=0), dict(layout=ep.LAYOUT_STATIC, slots_per_rank=-1),
     dict(layout=ep.LAYOUT_STATIC, slot_mode=2), dict(layout=ep.LAYOUT_STATIC, slot_mode=-1),
     dict(dispatch_stores=3), dict(dispatch_stores=-1), dict(passes_in_flight=-1),
-    dict(passes_in_flight=65), dict(fp8_scales=2), dict(fp8_scales=-1),
+    dict(passes_in_flight=65), dict(fp8_scales=3), dict(fp8_scales=-1),
     dict(combine_stores=3), dict(combine_stores=-1),
     dict(slot_mode=ep.SLOTS_INFERENCE),               # the inference slot mode is STATIC only
     dict(layout=ep.LAYOUT_STATIC, num_experts=1024, num_ranks=1024, slots_per_rank=1 << 22),
@@ -91,7 +91,7 @@ def test_group_accepts_each_store_kind(lib, field, stores):
     lib.ep_group_destroy(g)
 
 
-@pytest.mark.parametrize("f8", [ep.FP8_SCALES_AMAX, ep.FP8_SCALES_POW2])
+@pytest.mark.parametrize("f8", [ep.FP8_SCALES_AMAX, ep.FP8_SCALES_POW2, ep.FP8_SCALES_AMAX_POW2_WEIGHTS])
 def test_group_accepts_each_fp8_scale_format(lib, f8):
     rc, g = create(lib, fp8_scales=f8)
     assert rc == 0
